@@ -1,0 +1,94 @@
+"""Expected decode outputs of the synthetic workloads, from the full history.
+
+Nothing here uses a cache slot, a ring pointer or a block table: the resident
+set is written down from its definition and the rows are regenerated from
+the synthetic history, so the GPU cache layout is checked, not assumed.
+
+Ring workloads (sink + sliding window, [sink] cache formula, [ring] §2.2):
+  at decode position t the query attends R(t) = sinks united with the last W
+  positions, the new token included (each step appends, then attends, as the
+  [ring] demo does, §4.3).  Cached K rows carry RoPE at their absolute
+  position, rounded to the storage dtype ([pool] "bake RoPE into K"); V rows
+  are stored as given; the query is rotated at t and stored the same way.
+Paged workloads (block table with a shared prefix, [share] §3.1-§3.2):
+  plain causal attention over all len_b tokens of sequence b; K rows are used
+  as given (no RoPE on this workload).
+Pool workloads (fixed pool + validity mask, [pool] "paging" and "mask"):
+  attention over exactly the tokens of the resident blocks; absent blocks
+  are as if they did not exist.  Resident K rows carry RoPE at their
+  absolute position; the query is taken as given (already rotated).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from synth import TENSOR_K, TENSOR_Q, TENSOR_V
+
+from .attention import attend_heads
+from .ring import resident_positions, simulate_appends
+from .rope import rope
+from .rounding import round_store
+
+
+def ring_rows(w, b: int, positions, style: str = "interleaved"):
+    """Cached (K, V) rows of sequence b at absolute positions: K rotated + rounded."""
+    pos = np.asarray(positions, dtype=np.int64)
+    k_raw = w.rows(TENSOR_K, b, pos)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    k = round_store(rope(k_raw, pos[:, None], w.rope_base, style), w.dtype)
+    return k, v
+
+
+def ring_query(w, b: int, t: int, style: str = "interleaved") -> np.ndarray:
+    """Query of sequence b at decode position t, rotated at t and rounded [Hq, d]."""
+    q_raw = w.rows(TENSOR_Q, b, [t])[0]
+    return round_store(rope(q_raw, t, w.rope_base, style), w.dtype)
+
+
+def ring_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
+    """(out [Hq, d], lse [Hq]) of decode step `step` for sequence b."""
+    t = int(w.decode_positions(step)[b])
+    pos = resident_positions(t, w.sinks, w.window)
+    k, v = ring_rows(w, b, pos, style)
+    return attend_heads(ring_query(w, b, t, style), k, v, scale)
+
+
+def ring_appended_positions(w, b: int, through_step: int | None = None) -> list:
+    """Every position appended to sequence b, in call order: the history calls,
+    then one token per decode step up to and including `through_step`."""
+    out = []
+    for first, n in w.history_calls():
+        out.extend(range(int(first[b]), int(first[b]) + n))
+    if through_step is not None:
+        start = int(w.decode_start[b])
+        out.extend(range(start, start + through_step + 1))
+    return out
+
+
+def ring_slot_table(w, b: int, through_step: int | None = None) -> np.ndarray:
+    """Position held by each slot of sequence b (-1 = empty) after the appends."""
+    table = simulate_appends(ring_appended_positions(w, b, through_step), w.sinks, w.window)
+    return np.asarray(table, dtype=np.int32)
+
+
+def paged_expected(w, b: int, step: int, scale=None):
+    n = int(w.lengths[b])
+    pos = np.arange(n, dtype=np.int64)
+    k = w.rows(TENSOR_K, b, pos).astype(np.float64)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)
+
+
+def pool_rows(w, b: int, style: str = "interleaved"):
+    """(positions, K rotated + rounded, V) of sequence b's resident tokens."""
+    pos = w.resident_positions(b)
+    k_raw = w.rows(TENSOR_K, b, pos)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    k = round_store(rope(k_raw, pos[:, None], w.rope_base, style), w.dtype)
+    return pos, k, v
+
+
+def pool_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
+    _, k, v = pool_rows(w, b, style)
+    return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)
