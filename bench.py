@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X.
+
+A step is one pass of the whole decode path over one batch: for the ring
+workloads, the fused RoPE append of the new token (which also rotates the
+query) followed by the split-K decode and its merge; for the paged / pool
+workloads, the decode and its merge.  Inputs are synthetic (synth/), resident
+in HBM before the timed region; every step's new-token rows and query are
+staged on the device beforehand.
+
+Prints one JSON line:
+  value            KV-read GB/s of the whole job: algorithmic KV bytes per step
+                   (resident rows x Hkv x d x 2 x element bytes, summed over
+                   the batch) x steps / wall time of the timed steps.
+  roofline         for the dominant kernel (the decode kernel): algorithmic
+                   bytes per launch / its mean launch duration, from HIP events
+                   recorded on the launch stream around every decode call,
+                   against the 8 TB/s HBM peak; `traffic` is the measured HBM
+                   bytes per launch from rocprofv3 counters (profiles/) when
+                   they were taken on the current kernel source, else null.
+  cpu_baseline     the float64 NumPy oracle on a bounded sample of the same
+                   workload (inputs already in host memory), host cores.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+DECODE_SRC = os.path.join(ROOT, "decode_attention_fixed_amd", "csrc", "decode.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def describe(w) -> dict:
+    if w.kind == "ring":
+        text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
+                f"d={w.head_dim}, {w.dtype}, W={w.window} + {w.sinks} sinks, "
+                f"history {w.history}, append+decode per step")
+    elif w.kind == "paged":
+        text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
+                f"d={w.head_dim}, {w.dtype}, {w.block_size}-token blocks, lengths "
+                f"{w.len_range[0]}..{w.len_range[1]}, shared prefix {w.shared_prefix}")
+    else:
+        text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
+                f"d={w.head_dim}, {w.dtype}, {w.logical_blocks} x {w.block_size}-token "
+                f"logical blocks, pool of {w.pool_slots} slots per sequence")
+    return {"workload": text, "batch": w.batch, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim}
+
+
+def resident_tokens(w) -> int:
+    """Resident rows attended per step, summed over the batch (per kv head)."""
+    import numpy as np
+    if w.kind == "ring":
+        t = w.decode_positions(0)
+        return int(sum(min(int(x) + 1, w.slots) for x in t))
+    if w.kind == "paged":
+        return int(w.lengths.sum())
+    return int(np.asarray(w.block_valid, dtype=np.int64).sum()) * w.block_size
+
+
+def kv_bytes_per_step(w) -> int:
+    return resident_tokens(w) * w.kv_bytes_per_token()
+
+
+def traffic_record():
+    """Counter-measured HBM bytes per decode launch, if taken on this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+
+def run_gpu(w, steps: int, warmup: int) -> dict:
+    import numpy as np
+    import torch
+
+    from decode_attention_fixed_amd import binding as B
+    from decode_attention_fixed_amd.workloads import PagedState, RingState, to_device
+    from synth import TENSOR_K, TENSOR_Q, TENSOR_V
+    from synth.draws import draw_rows_parallel
+
+    torch.cuda.set_device(0)
+    total = warmup + steps
+    t0 = time.time()
+    if w.kind == "ring":
+        st = RingState(w)
+        st.prefill()
+        start = w.decode_start
+
+        def staged(tensor, heads):
+            arr = np.empty((w.batch, total, heads, w.head_dim), dtype=np.float32)
+            for b in range(w.batch):
+                draw_rows_parallel(w.seed, tensor, b, int(start[b]), total, heads, w.head_dim,
+                                   w.scale, w.dtype, out=arr[b])
+            t = to_device(arr, w.dtype)                       # [B, total, H, d]
+            return t.permute(1, 0, 2, 3).contiguous().unsqueeze(2)  # [total, B, 1, H, d]
+
+        k_all = staged(TENSOR_K, w.num_kv_heads)
+        v_all = staged(TENSOR_V, w.num_kv_heads)
+        q_all = staged(TENSOR_Q, w.num_q_heads)
+        pos_all = torch.from_numpy(
+            (start[None, :] + np.arange(total)[:, None]).astype(np.int32)).cuda()
+        handle = st.cache.handle
+
+        def pre(i):
+            B.kv_append_rope(handle, k_all[i], v_all[i], pos_all[i], q_all[i])
+
+        def decode(i):
+            B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse)
+    else:
+        st = PagedState(w, out_dtype=torch.float32)
+        st.fill()
+        qs = torch.stack([st.step_query(i % w.decode_steps) for i in range(min(total,
+                                                                                w.decode_steps))])
+        # Pools smaller than the ~256 MB last-level cache are cycled through
+        # enough copies (>= 600 MB) that a step cannot be served from cache.
+        pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
+        copies = max(1, math.ceil(600e6 / pool_bytes)) if pool_bytes < 300e6 else 1
+        pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
+                                            for _ in range(copies - 1)]
+
+        def pre(i):
+            pass
+
+        def decode(i):
+            k, v = pools[i % copies]
+            B.decode_attn_paged(st.desc, qs[i % qs.shape[0]], k, v, st.block_table, st.seq_lens,
+                                st.block_valid, st.out, st.workspace, st.lse)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f} s")
+
+    for i in range(warmup):
+        pre(i)
+        decode(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    begin = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    begin.record()
+    for s in range(steps):
+        i = warmup + s
+        pre(i)
+        ev[s][0].record()
+        decode(i)
+        ev[s][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = begin.elapsed_time(end)
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    return {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": sum(dec_ms) / len(dec_ms),
+            "decode_ms_min": min(dec_ms)}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, budget_s: float = 15.0) -> dict:
+    """Times the float64 oracle on whole sequences of decode step 0; inputs are
+    drawn beforehand (host memory), only the oracle's arithmetic is timed."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle.attention import attend_heads
+    from oracle.ring import resident_positions
+    from oracle.rope import rope
+    from oracle.rounding import round_store
+    from synth import TENSOR_K, TENSOR_Q, TENSOR_V
+
+    def inputs(b):
+        if w.kind == "ring":
+            t = int(w.decode_positions(0)[b])
+            pos = np.asarray(resident_positions(t, w.sinks, w.window))
+            return (pos, t, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos),
+                    w.rows(TENSOR_Q, b, [t])[0])
+        if w.kind == "paged":
+            pos = np.arange(int(w.lengths[b]))
+            return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, 0)
+        pos = w.resident_positions(b)
+        return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, 0)
+
+    def oracle_step(pos, t, k_raw, v, q_raw):
+        if w.kind == "ring":
+            k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
+            q = round_store(rope(q_raw, t, w.rope_base), w.dtype)
+        elif w.kind == "paged":
+            k, q = k_raw.astype(np.float64), q_raw.astype(np.float64)
+        else:
+            k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
+            q = q_raw.astype(np.float64)
+        return attend_heads(q, k, v.astype(np.float64))
+
+    timed, n, b = 0.0, 0, 0
+    while n < w.batch and (n == 0 or timed < budget_s):
+        args = inputs(b)
+        t0 = time.perf_counter()
+        oracle_step(*args)
+        timed += time.perf_counter() - t0
+        n += 1
+        b += 1
+    per_seq = timed / n
+    steps_per_s = 1.0 / (per_seq * w.batch)
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    return {"value": round(steps_per_s * kv_bytes_per_step(w) / 1e9, 4), "unit": "GB/s",
+            "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
+            "sample": (f"decode step 0 of {w.name}, {n} of {w.batch} sequences (all heads), "
+                       f"inputs pre-drawn in host memory; float64 NumPy, {timed:.1f} s timed; "
+                       f"BLAS threads {threads}, elementwise ops on one thread; "
+                       f"scaled to the full batch")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mha-ring")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the decode path on one GPU only; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported: run with --gpus 1", file=sys.stderr)
+        return 2
+
+    from synth import WORKLOADS
+    w = WORKLOADS[args.workload]
+    res = run_gpu(w, args.steps, args.warmup)
+    kv_bytes = kv_bytes_per_step(w)
+    ms_per_step = res["total_ms"] / args.steps
+    value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9
+    achieved = kv_bytes / (res["decode_ms_mean"] / 1e3) / 1e9
+    traffic = traffic_record()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": (int(float(traffic["fetch_bytes_per_launch"])
+                                + float(traffic["write_bytes_per_launch"]))
+                            if traffic and traffic.get("workload") == w.name else None),
+                "kernel": "decode_attn (split-K decode + merge), per call",
+                "algorithmic_bytes": kv_bytes}
+    out = {
+        "metric": "decode-attention KV-read GB/s", "value": round(value_gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic", "config": describe(w),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "hbm_frac_of_peak": round(value_gbs / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,279 @@
+"""Thin ctypes binding of libswa (include/swa.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream; every step of the decode path runs in libswa's
+kernels.  There is no fallback of any kind: if libswa.so has not been built
+the import of this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswa.so")
+
+SWA_OK = 0
+SWA_ERR_INVALID_ARG = -1
+SWA_ERR_UNSUPPORTED = -2
+SWA_ERR_WORKSPACE = -3
+SWA_ERR_HIP = -4
+
+SWA_F32 = 0
+SWA_BF16 = 1
+SWA_ROPE_INTERLEAVED = 0
+SWA_ROPE_HALF = 1
+
+_DTYPE_CODE = {torch.float32: SWA_F32, torch.bfloat16: SWA_BF16}
+_DTYPE_NAME = {"f32": SWA_F32, "bf16": SWA_BF16}
+_STYLE_CODE = {"interleaved": SWA_ROPE_INTERLEAVED, "half": SWA_ROPE_HALF}
+
+
+class SwaCacheConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_sinks", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32)]
+
+
+class SwaPagedDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_phys_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_PROTOS = {
+    "swa_cache_required_bytes": (ctypes.c_int, [ctypes.POINTER(SwaCacheConfig),
+                                                ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "swa_cache_create": (ctypes.c_int, [ctypes.POINTER(SwaCacheConfig), _vp, _vp, _vp,
+                                        ctypes.POINTER(_vp)]),
+    "swa_cache_reset": (ctypes.c_int, [_vp, _vp]),
+    "swa_cache_destroy": (None, [_vp]),
+    "kv_append_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp]),
+    "decode_attn_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "decode_attn_ring": (ctypes.c_int, [_vp, _vp, _i32, ctypes.c_float, _vp, _i32, _vp, _vp,
+                                        ctypes.c_size_t, _vp]),
+    "decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
+                                         _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
+                                         ctypes.c_size_t, _vp]),
+    "kv_write_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i32, ctypes.c_float, _i32, _vp]),
+    "swa_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_PROTOS)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_fixed_amd.build`"
+                          " (there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _PROTOS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+class SwaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed ({code}): {swa_last_error()}")
+
+
+def _check(fn: str, code: int) -> None:
+    if code != SWA_OK:
+        raise SwaError(fn, code)
+
+
+def swa_last_error() -> str:
+    return LIB.swa_last_error().decode()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# ring cache
+# ---------------------------------------------------------------------------
+
+def make_config(batch: int, num_kv_heads: int, head_dim: int, window: int, num_sinks: int,
+                dtype: str = "bf16", rope_base: float = 10000.0,
+                rope_style: str = "interleaved") -> SwaCacheConfig:
+    return SwaCacheConfig(batch, num_kv_heads, head_dim, window, num_sinks, _DTYPE_NAME[dtype],
+                          rope_base, _STYLE_CODE[rope_style])
+
+
+def swa_cache_required_bytes(cfg: SwaCacheConfig) -> tuple:
+    kv, sp = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("swa_cache_required_bytes",
+           LIB.swa_cache_required_bytes(ctypes.byref(cfg), ctypes.byref(kv), ctypes.byref(sp)))
+    return kv.value, sp.value
+
+
+def swa_cache_create(cfg: SwaCacheConfig, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     slot_pos: torch.Tensor) -> int:
+    handle = _vp()
+    dt = torch.bfloat16 if cfg.dtype == SWA_BF16 else torch.float32
+    _check("swa_cache_create",
+           LIB.swa_cache_create(ctypes.byref(cfg), _ptr(k_cache, "k_cache", dt),
+                                _ptr(v_cache, "v_cache", dt), _ptr(slot_pos, "slot_pos", torch.int32),
+                                ctypes.byref(handle)))
+    return handle.value
+
+
+def swa_cache_reset(handle: int, stream=None) -> None:
+    _check("swa_cache_reset", LIB.swa_cache_reset(handle, _stream(stream)))
+
+
+def swa_cache_destroy(handle: int | None) -> None:
+    LIB.swa_cache_destroy(handle)
+
+
+def kv_append_rope(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                   q_inout: torch.Tensor | None = None, stream=None) -> None:
+    """k_new, v_new [B, T, Hkv, d]; pos [B] int32 (position of token 0);
+    q_inout [B, T, Hq, d] or None, rotated in place."""
+    n_tokens = k_new.shape[1]
+    hq = q_inout.shape[2] if q_inout is not None else 0
+    _check("kv_append_rope",
+           LIB.kv_append_rope(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                              _ptr(pos, "pos", torch.int32), n_tokens, _ptr(q_inout, "q_inout"),
+                              hq, _stream(stream)))
+
+
+def decode_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                max_kv_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check("decode_attn_workspace_bytes",
+           LIB.decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                           max_kv_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def decode_attn_ring(handle: int, q: torch.Tensor, out: torch.Tensor,
+                     workspace: torch.Tensor, lse: torch.Tensor | None = None,
+                     scale: float = 0.0, stream=None) -> None:
+    """q [B, Hq, d] (rotated); out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
+    _check("decode_attn_ring",
+           LIB.decode_attn_ring(handle, _ptr(q, "q"), q.shape[1], scale, _ptr(out, "out"),
+                                _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
+                                _ptr(workspace, "workspace"), workspace.numel() *
+                                workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# paged pool
+# ---------------------------------------------------------------------------
+
+def make_paged_desc(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    block_size: int, max_blocks_per_seq: int, num_phys_blocks: int,
+                    dtype: str = "bf16") -> SwaPagedDesc:
+    return SwaPagedDesc(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_phys_blocks, _DTYPE_NAME[dtype])
+
+
+def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
+                      v_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      block_valid: torch.Tensor | None, out: torch.Tensor,
+                      workspace: torch.Tensor, lse: torch.Tensor | None = None,
+                      scale: float = 0.0, stream=None) -> None:
+    _check("decode_attn_paged",
+           LIB.decode_attn_paged(ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"),
+                                 _ptr(v_pool, "v_pool"),
+                                 _ptr(block_table, "block_table", torch.int32),
+                                 _ptr(seq_lens, "seq_lens", torch.int32),
+                                 _ptr(block_valid, "block_valid", torch.uint8), scale,
+                                 _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   k_src: torch.Tensor, v_src: torch.Tensor, dst_rows: torch.Tensor,
+                   pos: torch.Tensor | None = None, rope_base: float = 10000.0,
+                   rope_style: str = "interleaved", stream=None) -> None:
+    """k_src, v_src [N, Hkv, d]; dst_rows [N] int32 physical token rows; pos [N] int32 or None."""
+    _check("kv_write_paged",
+           LIB.kv_write_paged(ctypes.byref(desc), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+                              _ptr(k_src, "k_src"), _ptr(v_src, "v_src"),
+                              _ptr(dst_rows, "dst_rows", torch.int32), _ptr(pos, "pos", torch.int32),
+                              k_src.shape[0], rope_base, _STYLE_CODE[rope_style], _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# convenience owner of a ring cache's device buffers
+# ---------------------------------------------------------------------------
+
+@dataclass
+class RingCache:
+    """Device buffers of one ring cache (allocated with torch) plus its handle."""
+    cfg: SwaCacheConfig
+    k: torch.Tensor
+    v: torch.Tensor
+    slot_pos: torch.Tensor
+    handle: int
+
+    @classmethod
+    def allocate(cls, batch: int, num_kv_heads: int, head_dim: int, window: int, num_sinks: int,
+                 dtype: str = "bf16", rope_base: float = 10000.0,
+                 rope_style: str = "interleaved", device="cuda", stream=None) -> "RingCache":
+        cfg = make_config(batch, num_kv_heads, head_dim, window, num_sinks, dtype, rope_base,
+                          rope_style)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        slots = num_sinks + window
+        k = torch.empty((batch, num_kv_heads, slots, head_dim), dtype=tdt, device=device)
+        v = torch.empty_like(k)
+        slot_pos = torch.empty((batch, slots), dtype=torch.int32, device=device)
+        handle = swa_cache_create(cfg, k, v, slot_pos)
+        swa_cache_reset(handle, stream)
+        return cls(cfg, k, v, slot_pos, handle)
+
+    @property
+    def slots(self) -> int:
+        return self.cfg.num_sinks + self.cfg.window
+
+    def workspace(self, num_q_heads: int) -> torch.Tensor:
+        n = decode_attn_workspace_bytes(self.cfg.batch, num_q_heads, self.cfg.num_kv_heads,
+                                        self.cfg.head_dim, self.slots)
+        return torch.empty(n, dtype=torch.uint8, device=self.k.device)
+
+    def close(self) -> None:
+        if self.handle:
+            swa_cache_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass

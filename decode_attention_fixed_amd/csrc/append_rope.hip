@@ -1,0 +1,198 @@
+// Write half of the decode step: fused RoPE + scatter of the new tokens into
+// the cache.
+//
+// Ring cache ([ring] §3.3 and §5.1: overwrite the oldest entry in place, no
+// allocation; [sink]: S pinned sink slots): token at absolute position p goes
+// to slot p (p < S) or S + (p mod W); its K row is rotated at p and rounded to
+// the storage dtype before the store ([pool] "bake RoPE into K"), V is copied
+// bit for bit, and the slot's true position is recorded ([ring] §3.2, §7).
+//
+// One workgroup per (sequence, token).  The d/2 rotation angles of the token
+// are computed once per workgroup in float64 (pos * theta reduced by the f64
+// sincos), so positions up to 2^31 lose no accuracy; the rotation itself is
+// done in f64 and rounded once to the storage dtype.
+#include "device_common.h"
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kAppendThreads = 256;
+constexpr int kMaxHalfDim = 64;  // head_dim <= 128
+
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  using T = uint16_t;
+  __device__ static double load(const T* p, int i) { return static_cast<double>(bf16_to_f32(p[i])); }
+  __device__ static void store(T* p, int i, double x) { p[i] = f64_to_bf16_rne(x); }
+};
+template <>
+struct Elem<false> {
+  using T = float;
+  __device__ static double load(const T* p, int i) { return static_cast<double>(p[i]); }
+  __device__ static void store(T* p, int i, double x) { p[i] = static_cast<float>(x); }
+};
+
+// Angles of the token: cos/sin(pos * base^(-2i/d)), i < d/2.
+__device__ void rope_angles(double pos, double base, int head_dim, double* s_cos, double* s_sin) {
+  const int half = head_dim / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+    double s, c;
+    sincos(pos * theta, &s, &c);
+    s_cos[i] = c;
+    s_sin[i] = s;
+  }
+}
+
+// Rotates `rows` rows of head_dim elements from src into dst (may alias);
+// consecutive rows are src_stride / dst_stride elements apart.
+template <bool BF16>
+__device__ void rotate_rows(const typename Elem<BF16>::T* src, size_t src_stride,
+                            typename Elem<BF16>::T* dst, size_t dst_stride, int rows,
+                            int head_dim, int rope_half, const double* s_cos,
+                            const double* s_sin) {
+  using E = Elem<BF16>;
+  const int half = head_dim / 2;
+  for (int w = threadIdx.x; w < rows * half; w += blockDim.x) {
+    const int r = w / half;
+    const int i = w - r * half;
+    const int i0 = rope_half ? i : 2 * i;
+    const int i1 = rope_half ? i + half : 2 * i + 1;
+    const typename E::T* s = src + static_cast<size_t>(r) * src_stride;
+    typename E::T* d = dst + static_cast<size_t>(r) * dst_stride;
+    const double x0 = E::load(s, i0);
+    const double x1 = E::load(s, i1);
+    const double c = s_cos[i], sn = s_sin[i];
+    E::store(d, i0, x0 * c - x1 * sn);
+    E::store(d, i1, x0 * sn + x1 * c);
+  }
+}
+
+// Copies `rows` rows of row_bytes (a multiple of 16) with byte strides.
+__device__ void copy_rows16(const void* src, size_t src_stride, void* dst, size_t dst_stride,
+                            int rows, size_t row_bytes) {
+  const size_t per_row = row_bytes / 16;
+  for (size_t w = threadIdx.x; w < rows * per_row; w += blockDim.x) {
+    const size_t r = w / per_row;
+    const size_t c = w - r * per_row;
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const char*>(src) + r * src_stride);
+    uint4* d = reinterpret_cast<uint4*>(static_cast<char*>(dst) + r * dst_stride);
+    d[c] = s[c];
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParams p) {
+  using T = typename Elem<BF16>::T;
+  __shared__ double s_cos[kMaxHalfDim];
+  __shared__ double s_sin[kMaxHalfDim];
+
+  const int b = blockIdx.x / p.n_tokens;
+  const int j = blockIdx.x - b * p.n_tokens;
+  const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
+  if (pos < 0 || pos > INT32_MAX) return;  // uniform over the workgroup
+
+  rope_angles(static_cast<double>(pos), p.rope_base, p.head_dim, s_cos, s_sin);
+  __syncthreads();
+
+  const int slots = p.sinks + p.window;
+  const int d = p.head_dim;
+  const size_t row_elems = static_cast<size_t>(p.num_kv_heads) * d;
+  // A later token of this call lands in the same ring slot: leave it the slot.
+  const bool overwritten = pos >= p.sinks && j + p.window <= p.n_tokens - 1;
+  if (!overwritten) {
+    const int slot = pos < p.sinks ? static_cast<int>(pos)
+                                   : p.sinks + static_cast<int>(pos % p.window);
+    const size_t src_row = (static_cast<size_t>(b) * p.n_tokens + j) * row_elems;
+    const T* k_src = static_cast<const T*>(p.k_new) + src_row;
+    const T* v_src = static_cast<const T*>(p.v_new) + src_row;
+    // head h of the token goes to row (b, h, slot) of the head-major cache
+    const size_t dst = (static_cast<size_t>(b) * p.num_kv_heads * slots + slot) * d;
+    const size_t head_stride = static_cast<size_t>(slots) * d;
+    rotate_rows<BF16>(k_src, d, static_cast<T*>(p.k_cache) + dst, head_stride, p.num_kv_heads,
+                      d, p.rope_half, s_cos, s_sin);
+    copy_rows16(v_src, d * sizeof(T), static_cast<T*>(p.v_cache) + dst, head_stride * sizeof(T),
+                p.num_kv_heads, d * sizeof(T));
+    if (threadIdx.x == 0) p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
+  }
+  if (p.q_inout != nullptr) {
+    T* q = static_cast<T*>(p.q_inout) +
+           (static_cast<size_t>(b) * p.n_tokens + j) * static_cast<size_t>(p.num_q_heads) * d;
+    rotate_rows<BF16>(q, d, q, d, p.num_q_heads, d, p.rope_half, s_cos, s_sin);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kAppendThreads) void write_paged_kernel(PagedWriteParams p) {
+  using T = typename Elem<BF16>::T;
+  __shared__ double s_cos[kMaxHalfDim];
+  __shared__ double s_sin[kMaxHalfDim];
+
+  const int n = blockIdx.x;
+  const int64_t row = p.dst_rows[n];
+  const int64_t rows_total = static_cast<int64_t>(p.num_phys_blocks) * p.block_size;
+  if (row < 0 || row >= rows_total) return;
+  const bool rotate = p.pos != nullptr;
+  const int32_t pos = rotate ? p.pos[n] : 0;
+  if (pos < 0) return;
+  if (rotate) {
+    rope_angles(static_cast<double>(pos), p.rope_base, p.head_dim, s_cos, s_sin);
+    __syncthreads();
+  }
+  const int d = p.head_dim;
+  const int64_t blk = row / p.block_size;
+  const int r = static_cast<int>(row - blk * p.block_size);
+  const size_t src_row = static_cast<size_t>(n) * p.num_kv_heads * d;
+  const T* k_src = static_cast<const T*>(p.k_src) + src_row;
+  const T* v_src = static_cast<const T*>(p.v_src) + src_row;
+  // head h of the token goes to row (blk, h, r) of the pool
+  const size_t dst = (static_cast<size_t>(blk) * p.num_kv_heads * p.block_size + r) * d;
+  const size_t head_stride = static_cast<size_t>(p.block_size) * d;
+  T* k_dst = static_cast<T*>(p.k_pool) + dst;
+  if (rotate)
+    rotate_rows<BF16>(k_src, d, k_dst, head_stride, p.num_kv_heads, d, p.rope_half, s_cos, s_sin);
+  else
+    copy_rows16(k_src, d * sizeof(T), k_dst, head_stride * sizeof(T), p.num_kv_heads,
+                d * sizeof(T));
+  copy_rows16(v_src, d * sizeof(T), static_cast<T*>(p.v_pool) + dst, head_stride * sizeof(T),
+              p.num_kv_heads, d * sizeof(T));
+}
+
+__global__ void fill_i32_kernel(int32_t* dst, size_t n, int32_t value) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+  fill_i32_kernel<<<grid, 256, 0, stream>>>(dst, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.n_tokens);
+  if (p.bf16)
+    append_rope_kernel<true><<<grid, kAppendThreads, 0, stream>>>(p);
+  else
+    append_rope_kernel<false><<<grid, kAppendThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_paged(const PagedWriteParams& p, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(p.n_tokens);
+  if (p.bf16)
+    write_paged_kernel<true><<<grid, kAppendThreads, 0, stream>>>(p);
+  else
+    write_paged_kernel<false><<<grid, kAppendThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -1,0 +1,367 @@
+// Read half of the decode step: one query per head attends to the resident
+// rows of its sequence, split-K over the rows, then a log-sum-exp merge.
+//
+// Math ([sink] weight formula; [kvc] §2.2): s = scale * <q, k>,
+// out = sum_j exp(s_j) v_j / sum_j exp(s_j), over exactly the resident rows.
+// Softmax does not care about row order, so the ring is read in place
+// without restoring chronological order (the [ring] page, §5.2, warns that a
+// FlashAttention-style call would need it reordered first).
+//
+// Work decomposition.  A workgroup is one wave64 and owns one (sequence,
+// kv head, split) where a split is a contiguous range of split_tokens rows of
+// that head.  All g = Hq/Hkv query heads of the kv head are handled by the
+// same wave, so every K/V byte is read from HBM once per step (GQA: [share]
+// §2.2, §4.1).  Rows are streamed with 16-byte loads, LPR lanes per row, so
+// each wave load instruction covers RPI whole rows of contiguous memory
+// (head-major layout: one head's rows are adjacent).  Per tile of
+// TILE = RPI * NSTEP rows: partial dot products are reduced across the LPR
+// lanes of a row, the running max / sum of the online softmax are updated
+// (base-2 exponentials with the scale folded in), and P * V is accumulated
+// in float32 registers.  At the end the RPI row groups are reduced and the
+// wave writes its partial output (normalised) and base-2 log-sum-exp.
+//
+// Rows that are not resident (empty ring slot, absent or out-of-range
+// block, past seq_len, past the split) are never read into arithmetic: their
+// score is replaced by -inf and their V by 0 with selects, so NaN garbage in
+// an empty slot cannot leak ([pool] "absent blocks are as if they did not
+// exist").
+#include <type_traits>
+
+#include "device_common.h"
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr int kNumSteps = 8;  // load instructions per tensor per tile
+
+template <bool BF16, int D>
+struct Geo {
+  static constexpr int kElemBytes = BF16 ? 2 : 4;
+  static constexpr int kEPL = 16 / kElemBytes;  // elements per lane per row
+  static constexpr int kLPR = D / kEPL;         // lanes per row
+  static constexpr int kRPI = 64 / kLPR;        // rows per wave load instruction
+  static_assert(kLPR >= 1 && kLPR <= 64 && 64 % kLPR == 0, "row must split evenly over a wave");
+};
+
+template <bool BF16>
+struct Unpack;
+template <>
+struct Unpack<true> {
+  __device__ static void run(const Vec16& v, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(v.w[i]);
+      x[2 * i + 1] = bf16_hi(v.w[i]);
+    }
+  }
+};
+template <>
+struct Unpack<false> {
+  __device__ static void run(const Vec16& v, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v.w[i]);
+  }
+};
+
+// Ring cache: token index = slot; resident iff the slot holds a position.
+struct RingAddr {
+  __device__ static int tokens(const DecodeParams& p, int) { return p.slots; }
+  template <int D>
+  __device__ static bool row(const DecodeParams& p, int b, int h, int t, size_t& off) {
+    off = ((static_cast<size_t>(b) * p.num_kv_heads + h) * p.slots + t) * D;
+    return p.slot_pos[static_cast<size_t>(b) * p.slots + t] >= 0;
+  }
+};
+
+// Paged pool: token t of sequence b lives in block block_table[b][t / bs],
+// row t % bs; resident iff the entry is valid and names a pool block.
+struct PoolAddr {
+  __device__ static int tokens(const DecodeParams& p, int b) {
+    const int n = p.seq_lens[b];
+    const int cap = p.max_blocks << p.block_shift;
+    return n < 0 ? 0 : (n > cap ? cap : n);
+  }
+  template <int D>
+  __device__ static bool row(const DecodeParams& p, int b, int h, int t, size_t& off) {
+    const int j = t >> p.block_shift;
+    const int r = t & ((1 << p.block_shift) - 1);
+    const size_t e = static_cast<size_t>(b) * p.max_blocks + j;
+    const int blk = p.block_table[e];
+    const bool ok = blk >= 0 && blk < p.num_phys_blocks &&
+                    (p.block_valid == nullptr || p.block_valid[e] != 0);
+    off = ok ? (((static_cast<size_t>(blk) * p.num_kv_heads + h) << p.block_shift) + r) * D : 0;
+    return ok;
+  }
+};
+
+template <bool BF16, int D, int G, class Addr>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
+  using Gm = Geo<BF16, D>;
+  using T = std::conditional_t<BF16, uint16_t, float>;
+  constexpr int EPL = Gm::kEPL, LPR = Gm::kLPR, RPI = Gm::kRPI;
+  constexpr int TILE = RPI * kNumSteps;
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x % p.num_splits;
+  const int unit = blockIdx.x / p.num_splits;
+  const int b = unit / p.num_kv_heads;
+  const int kvh = unit - b * p.num_kv_heads;
+  const int ntok = Addr::tokens(p, b);
+  const int t0 = split * p.split_tokens;
+  const int t1 = min(t0 + p.split_tokens, ntok);
+  const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
+  float* lse_out = p.ws_lse + head0 * p.num_splits + split;  // + g * num_splits
+
+  if (t0 >= t1) {  // nothing of this sequence falls in the split
+    if (lane < G) lse_out[static_cast<size_t>(lane) * p.num_splits] = kNegInf;
+    return;
+  }
+
+  const int rl = lane / LPR;  // row within a load instruction
+  const int cl = lane % LPR;  // 16-byte column chunk within the row
+  const float c = p.score_scale_log2;
+
+  float q[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    Unpack<BF16>::run(load16(static_cast<const T*>(p.q) + (head0 + g) * D + cl * EPL), q[g]);
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const T* kbase = static_cast<const T*>(p.k) + cl * EPL;
+  const T* vbase = static_cast<const T*>(p.v) + cl * EPL;
+
+  for (int ts = t0; ts < t1; ts += TILE) {
+    Vec16 kr[kNumSteps], vr[kNumSteps];
+    bool ok[kNumSteps];
+#pragma unroll
+    for (int i = 0; i < kNumSteps; ++i) {
+      const int t = ts + i * RPI + rl;
+      const bool in = t < t1;
+      size_t off;
+      ok[i] = Addr::template row<D>(p, b, kvh, in ? t : t0, off) && in;
+      kr[i] = load16(kbase + off);
+      vr[i] = load16(vbase + off);
+    }
+
+    float s[G][kNumSteps];
+#pragma unroll
+    for (int i = 0; i < kNumSteps; ++i) {
+      float kx[EPL];
+      Unpack<BF16>::run(kr[i], kx);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(q[g][e], kx[e], a);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o);
+        s[g][i] = ok[i] ? a : kNegInf;
+      }
+    }
+
+    float pr[G][kNumSteps];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mt = s[g][0];
+#pragma unroll
+      for (int i = 1; i < kNumSteps; ++i) mt = fmaxf(mt, s[g][i]);
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+      const float mn = fmaxf(m[g], mt);
+      if (mn == kNegInf) {  // no resident row yet (uniform over the wave)
+#pragma unroll
+        for (int i = 0; i < kNumSteps; ++i) pr[g][i] = 0.f;
+        continue;
+      }
+      const float alpha = exp2f((m[g] - mn) * c);
+      m[g] = mn;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < kNumSteps; ++i) {
+        pr[g][i] = ok[i] ? exp2f((s[g][i] - mn) * c) : 0.f;
+        l[g] += pr[g][i];
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < kNumSteps; ++i) {
+      float vx[EPL];
+      Unpack<BF16>::run(vr[i], vx);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vx[e] = ok[i] ? vx[e] : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[g][i], vx[e], acc[g][e]);
+    }
+  }
+
+  // Sum the RPI row groups (m is already wave-uniform).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      l[g] += __shfl_xor(l[g], o);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], o);
+    }
+  }
+
+  if (rl == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+      float* dst = p.ws_o + ((head0 + g) * p.num_splits + split) * D + cl * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(acc[g][e] * inv, acc[g][e + 1] * inv, acc[g][e + 2] * inv,
+                        acc[g][e + 3] * inv);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (lane == g)
+      lse_out[static_cast<size_t>(g) * p.num_splits] =
+          l[g] > 0.f ? m[g] * c + __log2f(l[g]) : kNegInf;
+}
+
+// Combines the splits of one (sequence, query head):
+//   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum w_s o_s / sum w_s,
+//   lse = (M + log2 sum w_s) * ln 2.
+// Splits with lse = -inf hold no row and are skipped (their o is never read).
+template <int D>
+__global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
+  constexpr int PER = D / 64;
+  const size_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int ns = p.num_splits;
+  const float* lse2 = p.ws_lse + bh * ns;
+
+  float mx = kNegInf;
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse2[s]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const float ls = lse2[s];
+      if (ls == kNegInf) continue;
+      const float w = exp2f(ls - mx);
+      wsum += w;
+      const float* po = p.ws_o + (bh * ns + s) * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(w, po[lane + 64 * k], o[k]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const float val = o[k] * inv;
+    const size_t idx = bh * D + lane + 64 * k;
+    if (p.out_bf16)
+      static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16_rne(val);
+    else
+      static_cast<float*>(p.out)[idx] = val;
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[bh] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
+}
+
+template <bool BF16, int D, class Addr>
+hipError_t launch_split(const DecodeParams& p, int g, hipStream_t stream) {
+  const unsigned grid =
+      static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
+  switch (g) {
+#define SWA_CASE(G)                                                             \
+  case G:                                                                       \
+    decode_split_kernel<BF16, D, G, Addr><<<grid, 64, 0, stream>>>(p);          \
+    break;
+    SWA_CASE(1)
+    SWA_CASE(2)
+    SWA_CASE(3)
+    SWA_CASE(4)
+    SWA_CASE(6)
+    SWA_CASE(8)
+#undef SWA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class Addr>
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const int g = p.num_q_heads / p.num_kv_heads;
+  hipError_t err;
+  if (p.bf16)
+    err = p.head_dim == 64 ? launch_split<true, 64, Addr>(p, g, stream)
+                           : launch_split<true, 128, Addr>(p, g, stream);
+  else
+    err = p.head_dim == 64 ? launch_split<false, 64, Addr>(p, g, stream)
+                           : launch_split<false, 128, Addr>(p, g, stream);
+  if (err != hipSuccess) return err;
+  const unsigned grid = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
+  if (p.head_dim == 64)
+    merge_kernel<64><<<grid, 64, 0, stream>>>(p);
+  else
+    merge_kernel<128><<<grid, 64, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool group_supported(int g) {
+  return g == 1 || g == 2 || g == 3 || g == 4 || g == 6 || g == 8;
+}
+
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens) {
+  // Aim for about eight waves per CU over the 256 CUs, with splits a
+  // multiple of 64 rows and at least 128 rows long.
+  const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
+  const int64_t target_waves = 2048;
+  const int64_t tokens = max_kv_tokens > 0 ? max_kv_tokens : 1;
+  int64_t per = (tokens * units + target_waves - 1) / target_waves;
+  per = (per + 63) / 64 * 64;
+  if (per < 128) per = 128;
+  const int64_t cap = (tokens + 63) / 64 * 64;
+  if (per > cap) per = cap;
+  SplitPlan plan;
+  plan.split_tokens = static_cast<int32_t>(per);
+  plan.num_splits = static_cast<int32_t>((tokens + per - 1) / per);
+  return plan;
+}
+
+size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                       const SplitPlan& plan) {
+  const size_t heads = static_cast<size_t>(batch) * num_q_heads * plan.num_splits;
+  const size_t o_bytes = (heads * head_dim * sizeof(float) + 255) / 256 * 256;
+  const size_t lse_bytes = (heads * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + lse_bytes;
+}
+
+hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream) {
+  return launch_decode<RingAddr>(p, stream);
+}
+
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
+  return launch_decode<PoolAddr>(p, stream);
+}
+
+}  // namespace swa

@@ -1,0 +1,356 @@
+// C-ABI layer of libswa: argument validation (before any HIP call), the
+// opaque ring-cache descriptor, workspace sizing, launches on the caller's
+// stream and the thread-local error text.  See include/swa.h for the
+// contract of every entry point.
+#include "swa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "swa_internal.h"
+
+struct swa_cache {
+  swa_cache_config cfg;
+  void* k;
+  void* v;
+  int32_t* slot_pos;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+swa_status fail(swa_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+swa_status ok() {
+  g_last_error.clear();
+  return SWA_OK;
+}
+
+swa_status from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(SWA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(swa_dtype t) { return t == SWA_BF16 ? 2 : 4; }
+
+bool dtype_valid(swa_dtype t) { return t == SWA_F32 || t == SWA_BF16; }
+
+bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
+
+swa_status check_config(const swa_cache_config* cfg) {
+  if (cfg == nullptr) return fail(SWA_ERR_INVALID_ARG, "config is NULL");
+  if (cfg->batch < 1) return fail(SWA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", cfg->batch);
+  if (cfg->num_kv_heads < 1)
+    return fail(SWA_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", cfg->num_kv_heads);
+  if (cfg->window < 1) return fail(SWA_ERR_INVALID_ARG, "window must be >= 1 (got %d)", cfg->window);
+  if (cfg->num_sinks < 0)
+    return fail(SWA_ERR_INVALID_ARG, "num_sinks must be >= 0 (got %d)", cfg->num_sinks);
+  if (static_cast<int64_t>(cfg->window) + cfg->num_sinks > (int64_t{1} << 30))
+    return fail(SWA_ERR_INVALID_ARG, "num_sinks + window too large");
+  if (!dtype_valid(cfg->dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown dtype %d", cfg->dtype);
+  if (!head_dim_supported(cfg->head_dim))
+    return fail(SWA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", cfg->head_dim);
+  if (!(cfg->rope_base > 0.f) || !std::isfinite(cfg->rope_base))
+    return fail(SWA_ERR_INVALID_ARG, "rope_base must be positive and finite");
+  if (cfg->rope_style != SWA_ROPE_INTERLEAVED && cfg->rope_style != SWA_ROPE_HALF)
+    return fail(SWA_ERR_INVALID_ARG, "unknown rope_style %d", cfg->rope_style);
+  return SWA_OK;
+}
+
+swa_status check_group(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads < 1) return fail(SWA_ERR_INVALID_ARG, "num_q_heads must be >= 1");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(SWA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (!swa::group_supported(num_q_heads / num_kv_heads))
+    return fail(SWA_ERR_UNSUPPORTED, "query heads per kv head = %d not supported",
+                num_q_heads / num_kv_heads);
+  return SWA_OK;
+}
+
+swa_status check_decode_common(const void* q, void* out, swa_dtype out_dtype, float* lse,
+                               void* workspace, size_t workspace_bytes, size_t need) {
+  if (q == nullptr) return fail(SWA_ERR_INVALID_ARG, "q is NULL");
+  if (out == nullptr) return fail(SWA_ERR_INVALID_ARG, "out is NULL");
+  if (!dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(SWA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SWA_ERR_INVALID_ARG, "lse misaligned");
+  if (workspace == nullptr) return fail(SWA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(SWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(SWA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  return SWA_OK;
+}
+
+float resolve_scale(float scale, int32_t head_dim) {
+  const float s = scale > 0.f ? scale : 1.f / std::sqrt(static_cast<float>(head_dim));
+  return s * 1.44269504088896340736f;  // fold log2(e): softmax runs on exp2
+}
+
+void fill_workspace_ptrs(swa::DecodeParams& p, void* workspace) {
+  const size_t heads = static_cast<size_t>(p.batch) * p.num_q_heads * p.num_splits;
+  const size_t o_bytes = (heads * p.head_dim * sizeof(float) + 255) / 256 * 256;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+}
+
+int log2_exact(int32_t x) {
+  int s = 0;
+  while ((int64_t{1} << s) < x) ++s;
+  return (int64_t{1} << s) == x ? s : -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+swa_status swa_cache_required_bytes(const swa_cache_config* cfg, size_t* kv_bytes_each,
+                                    size_t* slot_pos_bytes) {
+  swa_status st = check_config(cfg);
+  if (st != SWA_OK) return st;
+  if (kv_bytes_each == nullptr || slot_pos_bytes == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "output pointer is NULL");
+  const size_t slots = static_cast<size_t>(cfg->num_sinks) + cfg->window;
+  *kv_bytes_each = static_cast<size_t>(cfg->batch) * cfg->num_kv_heads * slots * cfg->head_dim *
+                   elem_bytes(cfg->dtype);
+  *slot_pos_bytes = static_cast<size_t>(cfg->batch) * slots * sizeof(int32_t);
+  return ok();
+}
+
+swa_status swa_cache_create(const swa_cache_config* cfg, void* k_cache, void* v_cache,
+                            int32_t* slot_pos, swa_cache** out) {
+  swa_status st = check_config(cfg);
+  if (st != SWA_OK) return st;
+  if (out == nullptr) return fail(SWA_ERR_INVALID_ARG, "out is NULL");
+  if (k_cache == nullptr || v_cache == nullptr || slot_pos == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "cache buffer is NULL");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(slot_pos, 4))
+    return fail(SWA_ERR_INVALID_ARG, "cache buffers must be 16-byte aligned");
+  swa_cache* c = new (std::nothrow) swa_cache;
+  if (c == nullptr) return fail(SWA_ERR_INVALID_ARG, "out of host memory");
+  c->cfg = *cfg;
+  c->k = k_cache;
+  c->v = v_cache;
+  c->slot_pos = slot_pos;
+  *out = c;
+  return ok();
+}
+
+swa_status swa_cache_reset(swa_cache* cache, void* stream) {
+  if (cache == nullptr) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+  const size_t n =
+      static_cast<size_t>(cache->cfg.batch) * (cache->cfg.num_sinks + cache->cfg.window);
+  return from_hip(swa::launch_fill_i32(cache->slot_pos, n, -1, static_cast<hipStream_t>(stream)),
+                  "swa_cache_reset");
+}
+
+void swa_cache_destroy(swa_cache* cache) { delete cache; }
+
+swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new,
+                          const int32_t* pos, int32_t n_tokens, void* q_inout,
+                          int32_t num_q_heads, void* stream) {
+  if (cache == nullptr) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+  if (k_new == nullptr || v_new == nullptr || pos == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "k_new, v_new and pos must not be NULL");
+  if (n_tokens < 1) return fail(SWA_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", n_tokens);
+  if (static_cast<int64_t>(n_tokens) * cache->cfg.batch > INT32_MAX)
+    return fail(SWA_ERR_INVALID_ARG, "batch * n_tokens too large");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
+    return fail(SWA_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  if (q_inout != nullptr) {
+    swa_status st = check_group(num_q_heads, cache->cfg.num_kv_heads);
+    if (st != SWA_OK) return st;
+    if (!aligned(q_inout, 16)) return fail(SWA_ERR_INVALID_ARG, "q_inout must be 16-byte aligned");
+  }
+  swa::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.pos = pos;
+  p.q_inout = q_inout;
+  p.k_cache = cache->k;
+  p.v_cache = cache->v;
+  p.slot_pos = cache->slot_pos;
+  p.batch = cache->cfg.batch;
+  p.n_tokens = n_tokens;
+  p.num_kv_heads = cache->cfg.num_kv_heads;
+  p.num_q_heads = q_inout != nullptr ? num_q_heads : 0;
+  p.head_dim = cache->cfg.head_dim;
+  p.window = cache->cfg.window;
+  p.sinks = cache->cfg.num_sinks;
+  p.rope_base = cache->cfg.rope_base;
+  p.rope_half = cache->cfg.rope_style == SWA_ROPE_HALF;
+  p.bf16 = cache->cfg.dtype == SWA_BF16;
+  return from_hip(swa::launch_append_rope(p, static_cast<hipStream_t>(stream)), "kv_append_rope");
+}
+
+swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_kv_tokens, size_t* bytes) {
+  if (bytes == nullptr) return fail(SWA_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || num_kv_heads < 1 || max_kv_tokens < 0)
+    return fail(SWA_ERR_INVALID_ARG, "batch, num_kv_heads must be >= 1, max_kv_tokens >= 0");
+  swa_status st = check_group(num_q_heads, num_kv_heads);
+  if (st != SWA_OK) return st;
+  if (!head_dim_supported(head_dim))
+    return fail(SWA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  const swa::SplitPlan plan = swa::plan_splits(batch, num_kv_heads, max_kv_tokens);
+  *bytes = swa::workspace_bytes(batch, num_q_heads, head_dim, plan);
+  return ok();
+}
+
+swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
+                            float scale, void* out, swa_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache == nullptr) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+  const swa_cache_config& cfg = cache->cfg;
+  swa_status st = check_group(num_q_heads, cfg.num_kv_heads);
+  if (st != SWA_OK) return st;
+  const int32_t slots = cfg.num_sinks + cfg.window;
+  const swa::SplitPlan plan = swa::plan_splits(cfg.batch, cfg.num_kv_heads, slots);
+  const size_t need = swa::workspace_bytes(cfg.batch, num_q_heads, cfg.head_dim, plan);
+  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, need);
+  if (st != SWA_OK) return st;
+
+  swa::DecodeParams p{};
+  p.q = q;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.slot_pos = cache->slot_pos;
+  p.batch = cfg.batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cfg.num_kv_heads;
+  p.head_dim = cfg.head_dim;
+  p.slots = slots;
+  p.split_tokens = plan.split_tokens;
+  p.num_splits = plan.num_splits;
+  p.score_scale_log2 = resolve_scale(scale, cfg.head_dim);
+  p.out = out;
+  p.lse = lse;
+  p.out_bf16 = out_dtype == SWA_BF16;
+  p.bf16 = cfg.dtype == SWA_BF16;
+  fill_workspace_ptrs(p, workspace);
+  return from_hip(swa::launch_decode_ring(p, static_cast<hipStream_t>(stream)),
+                  "decode_attn_ring");
+}
+
+static swa_status check_paged_desc(const swa_paged_desc* d) {
+  if (d == nullptr) return fail(SWA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1 || d->num_kv_heads < 1 || d->max_blocks_per_seq < 1 || d->num_phys_blocks < 1)
+    return fail(SWA_ERR_INVALID_ARG,
+                "batch, num_kv_heads, max_blocks_per_seq, num_phys_blocks must be >= 1");
+  if (!dtype_valid(d->dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!head_dim_supported(d->head_dim))
+    return fail(SWA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  const int shift = log2_exact(d->block_size);
+  if (shift < 4 || shift > 10)
+    return fail(SWA_ERR_UNSUPPORTED, "block_size %d must be a power of two in [16, 1024]",
+                d->block_size);
+  if (static_cast<int64_t>(d->max_blocks_per_seq) * d->block_size > INT32_MAX ||
+      static_cast<int64_t>(d->num_phys_blocks) * d->block_size > INT32_MAX)
+    return fail(SWA_ERR_INVALID_ARG, "pool too large for 32-bit token indices");
+  return SWA_OK;
+}
+
+swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, const uint8_t* block_valid, float scale,
+                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  swa_status st = check_paged_desc(desc);
+  if (st != SWA_OK) return st;
+  st = check_group(desc->num_q_heads, desc->num_kv_heads);
+  if (st != SWA_OK) return st;
+  if (k_pool == nullptr || v_pool == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "k_pool, v_pool, block_table and seq_lens must not be NULL");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return fail(SWA_ERR_INVALID_ARG, "pool buffers misaligned");
+  const int32_t max_tokens = desc->max_blocks_per_seq * desc->block_size;
+  const swa::SplitPlan plan = swa::plan_splits(desc->batch, desc->num_kv_heads, max_tokens);
+  const size_t need = swa::workspace_bytes(desc->batch, desc->num_q_heads, desc->head_dim, plan);
+  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, need);
+  if (st != SWA_OK) return st;
+
+  swa::DecodeParams p{};
+  p.q = q;
+  p.k = k_pool;
+  p.v = v_pool;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.block_valid = block_valid;
+  p.batch = desc->batch;
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.block_shift = log2_exact(desc->block_size);
+  p.max_blocks = desc->max_blocks_per_seq;
+  p.num_phys_blocks = desc->num_phys_blocks;
+  p.split_tokens = plan.split_tokens;
+  p.num_splits = plan.num_splits;
+  p.score_scale_log2 = resolve_scale(scale, desc->head_dim);
+  p.out = out;
+  p.lse = lse;
+  p.out_bf16 = out_dtype == SWA_BF16;
+  p.bf16 = desc->dtype == SWA_BF16;
+  fill_workspace_ptrs(p, workspace);
+  return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream)),
+                  "decode_attn_paged");
+}
+
+swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool,
+                          const void* k_src, const void* v_src, const int32_t* dst_rows,
+                          const int32_t* pos, int32_t n_tokens, float rope_base,
+                          swa_rope_style rope_style, void* stream) {
+  swa_status st = check_paged_desc(desc);
+  if (st != SWA_OK) return st;
+  if (k_pool == nullptr || v_pool == nullptr || k_src == nullptr || v_src == nullptr ||
+      dst_rows == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "pool, source and dst_rows pointers must not be NULL");
+  if (n_tokens < 1) return fail(SWA_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", n_tokens);
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_src, 16) || !aligned(v_src, 16))
+    return fail(SWA_ERR_INVALID_ARG, "pool and source rows must be 16-byte aligned");
+  if (pos != nullptr) {
+    if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+      return fail(SWA_ERR_INVALID_ARG, "rope_base must be positive and finite");
+    if (rope_style != SWA_ROPE_INTERLEAVED && rope_style != SWA_ROPE_HALF)
+      return fail(SWA_ERR_INVALID_ARG, "unknown rope_style %d", rope_style);
+  }
+  swa::PagedWriteParams p{};
+  p.k_src = k_src;
+  p.v_src = v_src;
+  p.dst_rows = dst_rows;
+  p.pos = pos;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.n_tokens = n_tokens;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.block_size = desc->block_size;
+  p.num_phys_blocks = desc->num_phys_blocks;
+  p.rope_base = rope_base;
+  p.rope_half = rope_style == SWA_ROPE_HALF;
+  p.bf16 = desc->dtype == SWA_BF16;
+  return from_hip(swa::launch_write_paged(p, static_cast<hipStream_t>(stream)), "kv_write_paged");
+}
+
+const char* swa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal interface between the C-ABI layer (swa_api.cpp) and the HIP
+// kernels (append_rope.hip, decode.hip).  Launchers return hipError_t from
+// the launch; arguments reaching them have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+constexpr int kMaxGroup = 8;
+
+struct AppendParams {
+  const void* k_new;      // [B, T, Hkv, d]
+  const void* v_new;      // [B, T, Hkv, d]
+  const int32_t* pos;     // [B]
+  void* q_inout;          // [B, T, Hq, d] or null
+  void* k_cache;          // [B, Hkv, S+W, d]
+  void* v_cache;
+  int32_t* slot_pos;      // [B, S+W]
+  int32_t batch, n_tokens, num_kv_heads, num_q_heads, head_dim, window, sinks;
+  double rope_base;
+  int rope_half;          // 0: pairs (2i, 2i+1); 1: pairs (i, i + d/2)
+  int bf16;               // storage dtype
+};
+
+struct PagedWriteParams {
+  const void* k_src;      // [N, Hkv, d]
+  const void* v_src;
+  const int32_t* dst_rows;  // [N]
+  const int32_t* pos;       // [N] or null
+  void* k_pool;           // [Nphys, Hkv, bs, d]
+  void* v_pool;
+  int32_t n_tokens, num_kv_heads, head_dim, block_size, num_phys_blocks;
+  double rope_base;
+  int rope_half;
+  int bf16;
+};
+
+// One decode step, both addressing modes.  The split kernel writes one
+// partial (normalised output, base-2 log-sum-exp) per (sequence, query head,
+// split); the merge kernel combines the partials of each (sequence, head).
+struct DecodeParams {
+  const void* q;              // [B, Hq, d]
+  const void* k;              // ring [B, Hkv, slots, d] | pool [Nphys, Hkv, bs, d]
+  const void* v;
+  const int32_t* slot_pos;    // ring: [B, slots]
+  const int32_t* block_table; // pool: [B, max_blocks]
+  const int32_t* seq_lens;    // pool: [B]
+  const uint8_t* block_valid; // pool: [B, max_blocks] or null
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t slots;              // ring: S + W
+  int32_t block_shift;        // pool: log2(block_size)
+  int32_t max_blocks, num_phys_blocks;
+  int32_t split_tokens, num_splits;
+  float score_scale_log2;     // softmax scale * log2(e)
+  float* ws_o;                // [B, Hq, num_splits, d]
+  float* ws_lse;              // [B, Hq, num_splits]
+  void* out;                  // [B, Hq, d]
+  float* lse;                 // [B, Hq] or null
+  int out_bf16;
+  int bf16;
+};
+
+struct SplitPlan {
+  int32_t split_tokens;
+  int32_t num_splits;
+};
+
+// How a sequence's token range is cut into splits (shared by the workspace
+// query and the launch so both agree).
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens);
+size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                       const SplitPlan& plan);
+
+hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream);
+hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream);
+hipError_t launch_write_paged(const PagedWriteParams& p, hipStream_t stream);
+hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+
+bool group_supported(int g);
+
+}  // namespace swa

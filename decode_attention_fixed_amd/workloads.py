@@ -1,0 +1,185 @@
+"""Loads the synthetic workloads (synth/) into device memory through libswa.
+
+Device memory is allocated with torch; every cache write goes through the
+library's own entry points (kv_append_rope for ring caches, kv_write_paged
+for pools), so a loaded workload is exactly what the decode path sees in use.
+Used by the GPU tests, the smoke check and the benchmark.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from synth import TENSOR_K, TENSOR_Q, TENSOR_V, PagedWorkload, PoolWorkload, RingWorkload
+from synth.draws import SHARED_SEQUENCE, draw_rows_parallel
+
+from . import binding as B
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Upload float32 draws that are exact values of `dtype`."""
+    t = torch.from_numpy(np.ascontiguousarray(arr)).to(device, non_blocking=False)
+    return t.to(_TORCH_DTYPE[dtype])
+
+
+class RingState:
+    """A ring cache filled with a RingWorkload's history, plus decode buffers."""
+
+    MAX_CALL_TOKENS = 512  # history calls are issued in pieces of at most this many tokens
+
+    def __init__(self, w: RingWorkload, device="cuda", rope_style: str = "interleaved",
+                 out_dtype=torch.float32):
+        self.w = w
+        self.device = device
+        self.cache = B.RingCache.allocate(w.batch, w.num_kv_heads, w.head_dim, w.window, w.sinks,
+                                          w.dtype, w.rope_base, rope_style, device)
+        self.workspace = self.cache.workspace(w.num_q_heads)
+        self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=out_dtype,
+                               device=device)
+        self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=device)
+
+    # -- history -------------------------------------------------------------
+    def _rows(self, tensor: int, first: np.ndarray, n: int) -> np.ndarray:
+        w = self.w
+        heads = w.num_q_heads if tensor == TENSOR_Q else w.num_kv_heads
+        out = np.empty((w.batch, n, heads, w.head_dim), dtype=np.float32)
+        for b in range(w.batch):
+            draw_rows_parallel(w.seed, tensor, b, int(first[b]), n, heads, w.head_dim, w.scale,
+                               w.dtype, out=out[b])
+        return out
+
+    def append(self, first: np.ndarray, n: int, with_q: bool = False):
+        """Appends positions first[b] .. first[b]+n-1 for every sequence in one call;
+        returns the rotated query tensor when with_q."""
+        k = to_device(self._rows(TENSOR_K, first, n), self.w.dtype, self.device)
+        v = to_device(self._rows(TENSOR_V, first, n), self.w.dtype, self.device)
+        q = to_device(self._rows(TENSOR_Q, first, n), self.w.dtype, self.device) if with_q else None
+        pos = torch.from_numpy(np.asarray(first, dtype=np.int32)).to(self.device)
+        B.kv_append_rope(self.cache.handle, k, v, pos, q)
+        return q
+
+    def prefill(self, after_call=None) -> None:
+        """Issues the workload's history calls (split into pieces of at most
+        MAX_CALL_TOKENS tokens, which appends the same tokens in the same order)."""
+        for first, n in self.w.history_calls():
+            done = 0
+            while done < n:
+                m = min(self.MAX_CALL_TOKENS, n - done)
+                self.append(first + done, m)
+                done += m
+            if after_call is not None:
+                after_call(first, n)
+
+    # -- decode --------------------------------------------------------------
+    def step_inputs(self, step: int) -> dict:
+        t = self.w.decode_positions(step)
+        return dict(
+            k=to_device(self._rows(TENSOR_K, t, 1), self.w.dtype, self.device),
+            v=to_device(self._rows(TENSOR_V, t, 1), self.w.dtype, self.device),
+            q=to_device(self._rows(TENSOR_Q, t, 1), self.w.dtype, self.device),
+            pos=torch.from_numpy(t.astype(np.int32)).to(self.device),
+        )
+
+    def step(self, inputs: dict, scale: float = 0.0) -> None:
+        """One decode step: append the new token (rotating q in place), then attend."""
+        B.kv_append_rope(self.cache.handle, inputs["k"], inputs["v"], inputs["pos"], inputs["q"])
+        B.decode_attn_ring(self.cache.handle, inputs["q"][:, 0], self.out, self.workspace,
+                           self.lse, scale)
+
+    def close(self) -> None:
+        self.cache.close()
+
+
+class PagedState:
+    """A paged pool holding a PagedWorkload or a PoolWorkload."""
+
+    def __init__(self, w, device="cuda", out_dtype=torch.float32, rope_style="interleaved"):
+        self.w = w
+        self.device = device
+        dt = _TORCH_DTYPE[w.dtype]
+        if isinstance(w, PagedWorkload):
+            table = w.block_table
+            self.num_phys = w.num_unique_blocks
+            lens = w.lengths
+            valid = None
+        elif isinstance(w, PoolWorkload):
+            table = w.block_table
+            self.num_phys = w.batch * w.pool_slots
+            lens = np.full(w.batch, w.pool_slots * w.block_size, dtype=np.int64)
+            valid = w.block_valid
+        else:
+            raise TypeError(type(w))
+        self.desc = B.make_paged_desc(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                      w.block_size, table.shape[1], self.num_phys, w.dtype)
+        shape = (self.num_phys, w.num_kv_heads, w.block_size, w.head_dim)
+        self.k_pool = torch.empty(shape, dtype=dt, device=device)
+        self.v_pool = torch.empty(shape, dtype=dt, device=device)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
+        self.seq_lens = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.block_valid = (torch.from_numpy(np.ascontiguousarray(valid)).to(device)
+                            if valid is not None else None)
+        n = B.decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          table.shape[1] * w.block_size)
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=out_dtype,
+                               device=device)
+        self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=device)
+        self.rope_style = rope_style
+
+    def _write(self, k: np.ndarray, v: np.ndarray, rows: np.ndarray, pos=None) -> None:
+        w = self.w
+        kd = to_device(k, w.dtype, self.device)
+        vd = to_device(v, w.dtype, self.device)
+        rd = torch.from_numpy(rows.astype(np.int32)).to(self.device)
+        pd = torch.from_numpy(pos.astype(np.int32)).to(self.device) if pos is not None else None
+        base = getattr(w, "rope_base", 10000.0)
+        B.kv_write_paged(self.desc, self.k_pool, self.v_pool, kd, vd, rd, pd, base,
+                         self.rope_style)
+
+    def fill(self) -> None:
+        """Writes every resident token's K/V row into its pool row (the physical
+        row is block_table[b][i // bs] * bs + i % bs, computed here on the host
+        from the workload's table, independently of the kernels)."""
+        w = self.w
+        bs = w.block_size
+        if isinstance(w, PagedWorkload):
+            # the shared prefix once, from the shared stream
+            pre = w.shared_prefix
+            k = draw_rows_parallel(w.seed, TENSOR_K, SHARED_SEQUENCE, 0, pre, w.num_kv_heads,
+                                   w.head_dim, w.scale, w.dtype)
+            v = draw_rows_parallel(w.seed, TENSOR_V, SHARED_SEQUENCE, 0, pre, w.num_kv_heads,
+                                   w.head_dim, w.scale, w.dtype)
+            i = np.arange(pre)
+            self._write(k, v, w.block_table[0][i // bs].astype(np.int64) * bs + i % bs)
+            for b in range(w.batch):
+                n = int(w.lengths[b])
+                if n <= pre:
+                    continue
+                k = draw_rows_parallel(w.seed, TENSOR_K, b, pre, n - pre, w.num_kv_heads,
+                                       w.head_dim, w.scale, w.dtype)
+                v = draw_rows_parallel(w.seed, TENSOR_V, b, pre, n - pre, w.num_kv_heads,
+                                       w.head_dim, w.scale, w.dtype)
+                i = np.arange(pre, n)
+                self._write(k, v, w.block_table[b][i // bs].astype(np.int64) * bs + i % bs)
+        else:
+            for b in range(w.batch):
+                slots = np.nonzero(w.slot_blocks[b] >= 0)[0]
+                blocks = w.slot_blocks[b][slots]
+                pos = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+                rows = (w.block_table[b][slots].astype(np.int64)[:, None] * bs
+                        + np.arange(bs)[None, :]).reshape(-1)
+                k = w.rows(TENSOR_K, b, pos)
+                v = w.rows(TENSOR_V, b, pos)
+                self._write(k, v, rows, pos)
+
+    def step_query(self, step: int) -> torch.Tensor:
+        q = np.stack([self.w.query(b, step) for b in range(self.w.batch)])
+        return to_device(q, self.w.dtype, self.device)
+
+    def step(self, q: torch.Tensor, scale: float = 0.0) -> None:
+        B.decode_attn_paged(self.desc, q, self.k_pool, self.v_pool, self.block_table,
+                            self.seq_lens, self.block_valid, self.out, self.workspace, self.lse,
+                            scale)

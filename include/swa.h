@@ -1,0 +1,209 @@
+/*
+ * swa.h - decode attention over a bounded KV cache on MI355X (gfx950).
+ *
+ * Two halves of one decode step:
+ *   write: the new token's K (rotated by RoPE at its absolute position, the
+ *          rotation baked into the stored row) and V go into a cache slot;
+ *   read:  one query per head attends, with online softmax, to exactly the
+ *          resident rows, found through a slot-position array (ring cache) or
+ *          a block table plus a per-slot validity mask (paged pool).
+ *
+ * Pages cited (address, section):
+ *   [ring]  http://www.2kiu.com/news/4318096/          sliding window + ring KV buffer
+ *   [share] http://www.pwwt.cn/news/6215824/           KV sharing, block tables, GQA
+ *   [sink]  https://openeuler.csdn.net/6ad3842349ed150a32d85530.html  attention sinks
+ *   [kvc]   http://www.pwwt.cn/news/5010196/           KV cache fundamentals
+ *   [pool]  https://www.cloudlnk.cn/blog/kv-cache-paging  fixed KV pool, slot mask
+ *
+ * Conventions for every entry point:
+ *   - Plain C linkage; no exception crosses this boundary.
+ *   - Every buffer is owned by the caller.  Device buffers are device
+ *     pointers (hipMalloc'ed or equivalent); the library never allocates or
+ *     frees device memory.  The only host-side allocation is the opaque
+ *     swa_cache descriptor.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
+ *     are asynchronous on it; work on one stream runs in call order, so an
+ *     append followed by a decode on the same stream reads the new token.
+ *   - Arguments are validated on the host before any HIP call; a bad
+ *     argument returns SWA_ERR_INVALID_ARG / SWA_ERR_UNSUPPORTED /
+ *     SWA_ERR_WORKSPACE and launches nothing.  A failed launch returns
+ *     SWA_ERR_HIP.  swa_last_error() gives the text of the last failure on
+ *     the calling thread.
+ *   - Values that live in device memory (positions, block ids, lengths) are
+ *     not visible to the host: kernels skip out-of-range entries instead of
+ *     reading or writing out of bounds (documented per entry point).
+ *   - Device pointers to K/V/Q/output rows must be 16-byte aligned.
+ */
+#ifndef SWA_H_
+#define SWA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swa_status {
+  SWA_OK = 0,
+  SWA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment        */
+  SWA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group, dtype */
+  SWA_ERR_WORKSPACE = -3,   /* workspace missing or too small              */
+  SWA_ERR_HIP = -4          /* the HIP runtime reported an error           */
+} swa_status;
+
+typedef enum swa_dtype { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+/* RoPE pairing: coordinates (2i, 2i+1) or (i, i + d/2) rotate together by
+ * angle pos * base^(-2i/d).  The pages name RoPE without fixing a pairing. */
+typedef enum swa_rope_style { SWA_ROPE_INTERLEAVED = 0, SWA_ROPE_HALF = 1 } swa_rope_style;
+
+/* ------------------------------------------------------------------------- */
+/* Ring cache: S pinned sink slots followed by a W-slot ring.                 */
+/* ------------------------------------------------------------------------- */
+
+typedef struct swa_cache_config {
+  int32_t batch;          /* B sequences, each with its own cache ([ring] §5.3) */
+  int32_t num_kv_heads;   /* Hkv */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t window;         /* W >= 1: last W positions kept ([ring] §2.2) */
+  int32_t num_sinks;      /* S >= 0: first S positions kept forever ([sink], S = 4) */
+  swa_dtype dtype;        /* storage dtype of K, V and of queries */
+  float rope_base;        /* > 0, e.g. 10000 */
+  swa_rope_style rope_style;
+} swa_cache_config;
+
+/* Opaque host descriptor: the config plus the caller's device pointers. */
+typedef struct swa_cache swa_cache;
+
+/* Bytes the caller must allocate for the cache of `cfg`:
+ *   K and V, each  [B, Hkv, S+W, d]  elements of cfg->dtype (head-major, so
+ *                   one head's slots are contiguous rows of d elements);
+ *   slot_pos       [B, S+W] int32, the absolute position held by each slot,
+ *                   -1 when empty ([ring] §3.2: a cache slot must remember its
+ *                   true position, the slot index is not the position). */
+swa_status swa_cache_required_bytes(const swa_cache_config* cfg, size_t* kv_bytes_each,
+                                    size_t* slot_pos_bytes);
+
+/* Wraps caller-owned device buffers of the sizes above in a descriptor.
+ * Nothing is launched: call swa_cache_reset before the first append.
+ * The buffers must outlive the descriptor.  *out is set only on SWA_OK. */
+swa_status swa_cache_create(const swa_cache_config* cfg, void* k_cache, void* v_cache,
+                            int32_t* slot_pos, swa_cache** out);
+
+/* Marks every slot empty (slot_pos := -1) with a fill kernel on `stream`. */
+swa_status swa_cache_reset(swa_cache* cache, void* stream);
+
+/* Frees the host descriptor (not the device buffers).  NULL is a no-op. */
+void swa_cache_destroy(swa_cache* cache);
+
+/* Appends n_tokens consecutive tokens per sequence ([ring] §3.3 and §5.1:
+ * overwrite the oldest entry in O(1), never move or allocate).
+ *
+ *   k_new, v_new  [B, n_tokens, Hkv, d] in the cache dtype, device.
+ *   pos           [B] int32, device: absolute position of token 0 of
+ *                 sequence b; token j has position pos[b] + j.
+ *   q_inout       [B, n_tokens, Hq, d] in the cache dtype, or NULL.  When
+ *                 given, query row (b, j) is rotated in place at pos[b] + j.
+ *
+ * Token at position p goes to slot p if p < S, else to slot S + (p mod W).
+ * Its K row is rotated by RoPE at p and rounded (nearest-even) to the cache
+ * dtype before it is stored ([pool] "bake RoPE into K"; [kvc] §4.5); V is
+ * stored as given; slot_pos[b][slot] = p.  The result equals n_tokens
+ * single-token appends in order: a token whose slot is taken again by a later
+ * token of the same call is not written.  Tokens with a negative position are
+ * ignored (nothing written, query left as is). */
+swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new,
+                          const int32_t* pos, int32_t n_tokens, void* q_inout,
+                          int32_t num_q_heads, void* stream);
+
+/* Workspace (device bytes) that decode_attn_ring / decode_attn_paged need for
+ * these sizes; max_kv_tokens = S + W for a ring cache, max_blocks_per_seq *
+ * block_size for a paged pool.  0 bytes is never returned. */
+swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_kv_tokens, size_t* bytes);
+
+/* One decode step over a ring cache: every query head attends to the slots
+ * with slot_pos >= 0 of its sequence (sinks united with the last W positions
+ * after appends of 0..t: [sink] cache formula; [ring] §2.2, the current
+ * token included).  Softmax weights exp(s) / sum exp(s) with
+ * s = scale * <q, k> ([sink] weight formula; [kvc] §2.2); the order of the
+ * slots does not matter, so the ring is read in place.
+ *
+ *   q         [B, Hq, d] in the cache dtype, already rotated at its position.
+ *   Hq        multiple of Hkv; query head h reads kv head h / (Hq/Hkv)
+ *             ([share] §2.2, §4.1 GQA); Hq/Hkv in {1, 2, 3, 4, 6, 8}.
+ *   scale     <= 0 means 1/sqrt(d).
+ *   out       [B, Hq, d] of out_dtype (SWA_F32 or SWA_BF16).
+ *   lse       [B, Hq] float32 natural-log log-sum-exp of the scaled scores,
+ *             or NULL.  A head with no resident row gets out = 0, lse = -inf.
+ *   workspace decode_attn_workspace_bytes(B, Hq, Hkv, d, S + W) bytes,
+ *             device, 256-byte aligned; contents need no initialisation. */
+swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
+                            float scale, void* out, swa_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Paged pool: fixed-size blocks addressed through a block table.             */
+/* ------------------------------------------------------------------------- */
+
+typedef struct swa_paged_desc {
+  int32_t batch;              /* B */
+  int32_t num_q_heads;        /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads;       /* Hkv */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* tokens per block: a power of two, 16..1024 */
+  int32_t max_blocks_per_seq; /* columns of block_table / block_valid */
+  int32_t num_phys_blocks;    /* blocks in the pool */
+  swa_dtype dtype;            /* pool and query dtype */
+} swa_paged_desc;
+
+/* One decode step over a paged pool ([share] §3.1 block table; [pool]
+ * "paging" and "the kernel forgets absent blocks").
+ *
+ *   k_pool, v_pool  [num_phys_blocks, Hkv, block_size, d], device.
+ *   block_table     [B, max_blocks_per_seq] int32, device: entry j of
+ *                   sequence b is the physical block holding its tokens
+ *                   j*block_size .. (j+1)*block_size - 1.  Several sequences
+ *                   may name the same block (a shared prefix, [share] §3.2).
+ *   seq_lens        [B] int32, device: tokens of sequence b (clamped to
+ *                   [0, max_blocks_per_seq * block_size]).
+ *   block_valid     [B, max_blocks_per_seq] uint8, device, or NULL (all
+ *                   valid): 0 marks a slot whose block is absent.
+ *
+ * Resident rows of sequence b: tokens i < seq_lens[b] whose entry
+ * j = i / block_size is valid and names a block in [0, num_phys_blocks);
+ * every other row is never read into the arithmetic ("as if it did not
+ * exist").  K rows are used as stored (RoPE, if any, already baked in), so
+ * the call needs no positions.  q, scale, out, lse, workspace as for
+ * decode_attn_ring with max_kv_tokens = max_blocks_per_seq * block_size. */
+swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, const uint8_t* block_valid, float scale,
+                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Writes n_tokens rows into a paged pool, rotating K at a given position
+ * first ([pool] "bake RoPE into K": each block becomes self-contained).
+ *
+ *   k_src, v_src  [n_tokens, Hkv, d] in the pool dtype, device.
+ *   dst_rows      [n_tokens] int32, device: physical token row
+ *                 block * block_size + r of each token.
+ *   pos           [n_tokens] int32, device: RoPE position of each token, or
+ *                 NULL to store K as given.
+ * Tokens whose dst_rows entry is outside [0, num_phys_blocks * block_size) or
+ * whose position is negative are skipped.  Two tokens naming the same row
+ * race (one of them wins). */
+swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool,
+                          const void* k_src, const void* v_src, const int32_t* dst_rows,
+                          const int32_t* pos, int32_t n_tokens, float rope_base,
+                          swa_rope_style rope_style, void* stream);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H_ */

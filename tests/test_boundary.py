@@ -1,0 +1,225 @@
+"""The C-ABI boundary on the host: libswa loads, exports every function that
+include/swa.h declares, sizes buffers, and rejects bad arguments before any
+HIP call (no compute is launched by these tests; they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_fixed_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*([A-Za-z_]\w*)\s*\(", src, re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_functions_are_exported():
+    declared = _declared_functions()
+    assert len(declared) == 10, declared
+    assert sorted(B.EXPORTED) == declared
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    base = dict(batch=8, num_kv_heads=32, head_dim=128, window=4096, num_sinks=4, dtype="bf16")
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def test_required_bytes():
+    kv, sp = B.swa_cache_required_bytes(_cfg())
+    assert kv == 8 * 32 * 4100 * 128 * 2
+    assert sp == 8 * 4100 * 4
+    kv, sp = B.swa_cache_required_bytes(_cfg(batch=1, num_kv_heads=4, head_dim=64, window=16,
+                                             dtype="f32"))
+    assert kv == 1 * 4 * 20 * 64 * 4 and sp == 20 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), B.SWA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), B.SWA_ERR_INVALID_ARG),
+    (dict(window=0), B.SWA_ERR_INVALID_ARG),
+    (dict(num_sinks=-1), B.SWA_ERR_INVALID_ARG),
+    (dict(head_dim=96), B.SWA_ERR_UNSUPPORTED),
+    (dict(head_dim=256), B.SWA_ERR_UNSUPPORTED),
+])
+def test_bad_config(kw, code):
+    with pytest.raises(B.SwaError) as e:
+        B.swa_cache_required_bytes(_cfg(**kw))
+    assert e.value.code == code
+    assert B.swa_last_error() != ""
+
+
+def test_bad_rope_base_and_dtype():
+    cfg = _cfg()
+    cfg.rope_base = 0.0
+    with pytest.raises(B.SwaError):
+        B.swa_cache_required_bytes(cfg)
+    cfg = _cfg()
+    cfg.dtype = 7
+    with pytest.raises(B.SwaError):
+        B.swa_cache_required_bytes(cfg)
+
+
+def _create(**kw):
+    cfg = _cfg(**kw)
+    h = ctypes.c_void_p()
+    rc = B.LIB.swa_cache_create(ctypes.byref(cfg), FAKE, FAKE, FAKE, ctypes.byref(h))
+    assert rc == B.SWA_OK, B.swa_last_error()
+    assert B.swa_last_error() == ""
+    return h.value
+
+
+def test_create_and_destroy_touch_no_device_memory():
+    h = _create()
+    assert h
+    B.swa_cache_destroy(h)
+    B.swa_cache_destroy(None)
+
+
+def test_create_rejects_null_and_misaligned():
+    cfg = _cfg()
+    h = ctypes.c_void_p()
+    assert B.LIB.swa_cache_create(ctypes.byref(cfg), None, FAKE, FAKE, ctypes.byref(h)) == \
+        B.SWA_ERR_INVALID_ARG
+    assert B.LIB.swa_cache_create(ctypes.byref(cfg), FAKE + 2, FAKE, FAKE, ctypes.byref(h)) == \
+        B.SWA_ERR_INVALID_ARG
+    assert B.LIB.swa_cache_create(ctypes.byref(cfg), FAKE, FAKE, FAKE, None) == \
+        B.SWA_ERR_INVALID_ARG
+    assert h.value is None
+
+
+def test_append_validation():
+    h = _create(num_kv_heads=4)
+    L = B.LIB
+    try:
+        assert L.kv_append_rope(None, FAKE, FAKE, FAKE, 1, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, None, FAKE, FAKE, 1, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, FAKE, FAKE, None, 1, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, FAKE, FAKE, FAKE, 0, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, FAKE, FAKE, FAKE, -3, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, FAKE + 8, FAKE, FAKE, 1, None, 0, None) == B.SWA_ERR_INVALID_ARG
+        # query heads: not a multiple of Hkv / unsupported group
+        assert L.kv_append_rope(h, FAKE, FAKE, FAKE, 1, FAKE, 6, None) == B.SWA_ERR_INVALID_ARG
+        assert L.kv_append_rope(h, FAKE, FAKE, FAKE, 1, FAKE, 20, None) == B.SWA_ERR_UNSUPPORTED
+        assert L.kv_append_rope(h, FAKE, FAKE, FAKE, 1, FAKE, 0, None) == B.SWA_ERR_INVALID_ARG
+    finally:
+        B.swa_cache_destroy(h)
+
+
+def test_workspace_sizes():
+    n = B.decode_attn_workspace_bytes(8, 32, 32, 128, 4100)
+    assert n > 8 * 32 * 128 * 4 and n % 256 == 0
+    # more tokens never needs less workspace
+    sizes = [B.decode_attn_workspace_bytes(64, 32, 8, 128, t) for t in (1, 100, 4100, 40000)]
+    assert sizes == sorted(sizes)
+    with pytest.raises(B.SwaError):
+        B.decode_attn_workspace_bytes(8, 30, 32, 128, 4100)
+    with pytest.raises(B.SwaError):
+        B.decode_attn_workspace_bytes(8, 32, 32, 80, 4100)
+
+
+def test_decode_ring_validation():
+    h = _create()
+    L = B.LIB
+    need = B.decode_attn_workspace_bytes(8, 32, 32, 128, 4100)
+    try:
+        args = dict(q=FAKE, hq=32, scale=0.0, out=FAKE, odt=B.SWA_F32, lse=None, ws=FAKE,
+                    wsb=need)
+
+        def call(**kw):
+            a = dict(args)
+            a.update(kw)
+            return L.decode_attn_ring(h, a["q"], a["hq"], a["scale"], a["out"], a["odt"], a["lse"],
+                                      a["ws"], a["wsb"], None)
+
+        assert call(wsb=need - 1) == B.SWA_ERR_WORKSPACE
+        assert "too small" in B.swa_last_error()
+        assert call(ws=None) == B.SWA_ERR_WORKSPACE
+        assert call(ws=FAKE + 16) == B.SWA_ERR_WORKSPACE  # not 256-byte aligned
+        assert call(q=None) == B.SWA_ERR_INVALID_ARG
+        assert call(out=None) == B.SWA_ERR_INVALID_ARG
+        assert call(out=FAKE + 4) == B.SWA_ERR_INVALID_ARG
+        assert call(odt=5) == B.SWA_ERR_INVALID_ARG
+        assert call(hq=48) == B.SWA_ERR_INVALID_ARG
+        assert call(hq=32 * 5) == B.SWA_ERR_UNSUPPORTED
+        assert L.decode_attn_ring(None, FAKE, 32, 0.0, FAKE, 0, None, FAKE, need, None) == \
+            B.SWA_ERR_INVALID_ARG
+    finally:
+        B.swa_cache_destroy(h)
+
+
+def _desc(**kw):
+    base = dict(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                max_blocks_per_seq=2048, num_phys_blocks=30000, dtype="bf16")
+    base.update(kw)
+    return B.make_paged_desc(**base)
+
+
+def _paged(desc, **kw):
+    try:
+        need = B.decode_attn_workspace_bytes(desc.batch, desc.num_q_heads, desc.num_kv_heads,
+                                             desc.head_dim,
+                                             desc.max_blocks_per_seq * desc.block_size)
+    except B.SwaError:
+        need = 1 << 30  # the descriptor itself is what the call must reject
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, bv=None, out=FAKE, ws=FAKE, wsb=need)
+    a.update(kw)
+    return B.LIB.decode_attn_paged(ctypes.byref(desc), a["q"], a["k"], a["v"], a["bt"], a["sl"],
+                                   a["bv"], 0.0, a["out"], B.SWA_F32, None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=8), B.SWA_ERR_UNSUPPORTED),
+    (dict(block_size=48), B.SWA_ERR_UNSUPPORTED),
+    (dict(block_size=2048), B.SWA_ERR_UNSUPPORTED),
+    (dict(num_phys_blocks=0), B.SWA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), B.SWA_ERR_INVALID_ARG),
+    (dict(num_q_heads=12), B.SWA_ERR_INVALID_ARG),
+    (dict(head_dim=32), B.SWA_ERR_UNSUPPORTED),
+    (dict(num_phys_blocks=200_000_000), B.SWA_ERR_INVALID_ARG),
+])
+def test_decode_paged_desc_validation(kw, code):
+    assert _paged(_desc(**kw)) == code
+
+
+def test_decode_paged_pointer_validation():
+    d = _desc()
+    assert _paged(d, sl=None) == B.SWA_ERR_INVALID_ARG
+    assert _paged(d, bt=None) == B.SWA_ERR_INVALID_ARG
+    assert _paged(d, k=FAKE + 2) == B.SWA_ERR_INVALID_ARG
+    assert _paged(d, wsb=16) == B.SWA_ERR_WORKSPACE
+
+
+def test_write_paged_validation():
+    d = _desc()
+    L = B.LIB
+    assert L.kv_write_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1e4, 0,
+                            None) == B.SWA_ERR_INVALID_ARG
+    assert L.kv_write_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, 5, 1e4, 0,
+                            None) == B.SWA_ERR_INVALID_ARG
+    assert L.kv_write_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, -1.0, 0,
+                            None) == B.SWA_ERR_INVALID_ARG
+    assert L.kv_write_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 1e4, 9,
+                            None) == B.SWA_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_fallback():
+    """The binding imports nothing from the oracle and has no CPU path."""
+    src = open(os.path.join(ROOT, "decode_attention_fixed_amd", "binding.py")).read()
+    assert "oracle" not in src and "numpy" not in src
+    for f in os.listdir(os.path.join(ROOT, "decode_attention_fixed_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "decode_attention_fixed_amd", "csrc",
+                                                 f)).read()
