@@ -269,7 +269,7 @@ def main() -> int:
                 "traffic": (int(float(traffic["fetch_bytes_per_launch"])
                                 + float(traffic["write_bytes_per_launch"]))
                             if traffic and traffic.get("workload") == w.name else None),
-                "kernel": "decode_attn (split-K decode + merge), per call",
+                "kernel": "decode kernel (one launch per decode call)",
                 "algorithmic_bytes": kv_bytes}
     out = {
         "metric": "decode-attention KV-read GB/s", "value": round(value_gbs, 1), "unit": "GB/s",

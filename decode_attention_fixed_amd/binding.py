@@ -180,6 +180,13 @@ def decode_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int,
     return n.value
 
 
+def new_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  max_kv_tokens: int, device="cuda") -> torch.Tensor:
+    """A decode workspace for these sizes (no initialisation needed)."""
+    n = decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def decode_attn_ring(handle: int, q: torch.Tensor, out: torch.Tensor,
                      workspace: torch.Tensor, lse: torch.Tensor | None = None,
                      scale: float = 0.0, stream=None) -> None:
@@ -263,9 +270,8 @@ class RingCache:
         return self.cfg.num_sinks + self.cfg.window
 
     def workspace(self, num_q_heads: int) -> torch.Tensor:
-        n = decode_attn_workspace_bytes(self.cfg.batch, num_q_heads, self.cfg.num_kv_heads,
-                                        self.cfg.head_dim, self.slots)
-        return torch.empty(n, dtype=torch.uint8, device=self.k.device)
+        return new_workspace(self.cfg.batch, num_q_heads, self.cfg.num_kv_heads,
+                             self.cfg.head_dim, self.slots, self.k.device)
 
     def close(self) -> None:
         if self.handle:

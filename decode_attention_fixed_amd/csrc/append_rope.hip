@@ -84,45 +84,75 @@ __device__ void copy_rows16(const void* src, size_t src_stride, void* dst, size_
   }
 }
 
+// One thread per unit of work of one token: a rotated K pair, a rotated query
+// pair, or a 16-byte chunk of the V row.  Each thread computes the angle of its
+// own pair, so a single-token decode append spreads over many workgroups
+// instead of looping inside a few.
 template <bool BF16>
-__global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParams p) {
-  using T = typename Elem<BF16>::T;
-  __shared__ double s_cos[kMaxHalfDim];
-  __shared__ double s_sin[kMaxHalfDim];
-
-  const int b = blockIdx.x / p.n_tokens;
-  const int j = blockIdx.x - b * p.n_tokens;
+__global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParams p,
+                                                                     int items_per_token,
+                                                                     int wgs_per_token) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  const int token = blockIdx.x / wgs_per_token;  // b * n_tokens + j
+  const int item = (blockIdx.x - token * wgs_per_token) * kAppendThreads + threadIdx.x;
+  if (item >= items_per_token) return;
+  const int b = token / p.n_tokens;
+  const int j = token - b * p.n_tokens;
   const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
-  if (pos < 0 || pos > INT32_MAX) return;  // uniform over the workgroup
+  if (pos < 0 || pos > INT32_MAX) return;
 
-  rope_angles(static_cast<double>(pos), p.rope_base, p.head_dim, s_cos, s_sin);
-  __syncthreads();
-
-  const int slots = p.sinks + p.window;
   const int d = p.head_dim;
-  const size_t row_elems = static_cast<size_t>(p.num_kv_heads) * d;
+  const int half = d / 2;
+  const int slots = p.sinks + p.window;
+  const int k_items = p.num_kv_heads * half;
+  const int q_items = p.q_inout != nullptr ? p.num_q_heads * half : 0;
   // A later token of this call lands in the same ring slot: leave it the slot.
   const bool overwritten = pos >= p.sinks && j + p.window <= p.n_tokens - 1;
-  if (!overwritten) {
-    const int slot = pos < p.sinks ? static_cast<int>(pos)
-                                   : p.sinks + static_cast<int>(pos % p.window);
-    const size_t src_row = (static_cast<size_t>(b) * p.n_tokens + j) * row_elems;
-    const T* k_src = static_cast<const T*>(p.k_new) + src_row;
-    const T* v_src = static_cast<const T*>(p.v_new) + src_row;
-    // head h of the token goes to row (b, h, slot) of the head-major cache
-    const size_t dst = (static_cast<size_t>(b) * p.num_kv_heads * slots + slot) * d;
-    const size_t head_stride = static_cast<size_t>(slots) * d;
-    rotate_rows<BF16>(k_src, d, static_cast<T*>(p.k_cache) + dst, head_stride, p.num_kv_heads,
-                      d, p.rope_half, s_cos, s_sin);
-    copy_rows16(v_src, d * sizeof(T), static_cast<T*>(p.v_cache) + dst, head_stride * sizeof(T),
-                p.num_kv_heads, d * sizeof(T));
-    if (threadIdx.x == 0) p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
+  const int slot = pos < p.sinks ? static_cast<int>(pos) : p.sinks + static_cast<int>(pos % p.window);
+
+  if (item < k_items + q_items) {
+    const bool is_k = item < k_items;
+    if (is_k && overwritten) return;
+    const int w = is_k ? item : item - k_items;
+    const int h = w / half;
+    const int i = w - h * half;
+    const double theta = pow(p.rope_base, -2.0 * static_cast<double>(i) / static_cast<double>(d));
+    double sn, cs;
+    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+    const int i0 = p.rope_half ? i : 2 * i;
+    const int i1 = p.rope_half ? i + half : 2 * i + 1;
+    const T* src;
+    T* dst;
+    if (is_k) {
+      src = static_cast<const T*>(p.k_new) +
+            ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_kv_heads + h) * d;
+      dst = static_cast<T*>(p.k_cache) +
+            ((static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot) * d;
+    } else {
+      dst = static_cast<T*>(p.q_inout) +
+            ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
+      src = dst;
+    }
+    const double x0 = E::load(src, i0);
+    const double x1 = E::load(src, i1);
+    E::store(dst, i0, x0 * cs - x1 * sn);
+    E::store(dst, i1, x0 * sn + x1 * cs);
+    if (is_k && item == 0) p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
+    return;
   }
-  if (p.q_inout != nullptr) {
-    T* q = static_cast<T*>(p.q_inout) +
-           (static_cast<size_t>(b) * p.n_tokens + j) * static_cast<size_t>(p.num_q_heads) * d;
-    rotate_rows<BF16>(q, d, q, d, p.num_q_heads, d, p.rope_half, s_cos, s_sin);
-  }
+  if (overwritten) return;
+  // V: 16-byte chunks of the token's Hkv rows
+  const int per_row = d * static_cast<int>(sizeof(T)) / 16;
+  const int w = item - k_items - q_items;
+  const int h = w / per_row;
+  const int c = w - h * per_row;
+  const uint4* src = reinterpret_cast<const uint4*>(
+      static_cast<const T*>(p.v_new) +
+      ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_kv_heads + h) * d);
+  uint4* dst = reinterpret_cast<uint4*>(
+      static_cast<T*>(p.v_cache) + ((static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot) * d);
+  dst[c] = src[c];
 }
 
 template <bool BF16>
@@ -178,11 +208,17 @@ hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t st
 }
 
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.n_tokens);
+  const int half = p.head_dim / 2;
+  const int elem = p.bf16 ? 2 : 4;
+  const int items = p.num_kv_heads * half + (p.q_inout != nullptr ? p.num_q_heads * half : 0) +
+                    p.num_kv_heads * (p.head_dim * elem / 16);
+  const int wgs = (items + kAppendThreads - 1) / kAppendThreads;
+  const size_t grid = static_cast<size_t>(p.batch) * p.n_tokens * wgs;
+  if (grid > 0x7fffffffu) return hipErrorInvalidValue;
   if (p.bf16)
-    append_rope_kernel<true><<<grid, kAppendThreads, 0, stream>>>(p);
+    append_rope_kernel<true><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
   else
-    append_rope_kernel<false><<<grid, kAppendThreads, 0, stream>>>(p);
+    append_rope_kernel<false><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
   return hipGetLastError();
 }
 

@@ -331,9 +331,11 @@ bool group_supported(int g) {
   return g == 1 || g == 2 || g == 3 || g == 4 || g == 6 || g == 8;
 }
 
+bool use_mfma_path(int bf16, int32_t head_dim) { return bf16 && head_dim == 128; }
+
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens) {
-  // Aim for about eight waves per CU over the 256 CUs, with splits a
-  // multiple of 64 rows and at least 128 rows long.
+  // One wave per split: aim for about eight waves per CU over the 256 CUs,
+  // with splits a multiple of 64 rows and at least 128 rows long.
   const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
   const int64_t target_waves = 2048;
   const int64_t tokens = max_kv_tokens > 0 ? max_kv_tokens : 1;
@@ -348,19 +350,51 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens
   return plan;
 }
 
-size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                       const SplitPlan& plan) {
-  const size_t heads = static_cast<size_t>(batch) * num_q_heads * plan.num_splits;
-  const size_t o_bytes = (heads * head_dim * sizeof(float) + 255) / 256 * 256;
-  const size_t lse_bytes = (heads * sizeof(float) + 255) / 256 * 256;
-  return o_bytes + lse_bytes;
+SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens,
+                           bool ragged) {
+  // One multi-wave workgroup per split.  Enough splits per (sequence, kv head)
+  // that the grid covers the 256 CUs; splits are whole 64-row tiles and at
+  // most 8192 rows long, or 2048 when sequence lengths differ (a paged pool),
+  // so that short and long sequences balance over the CUs.
+  const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
+  const int64_t tokens = max_kv_tokens > 0 ? max_kv_tokens : 1;
+  const int64_t cap = ragged ? 2048 : 8192;
+  const int64_t fill = (256 + units - 1) / units;
+  const int64_t by_len = (tokens + cap - 1) / cap;
+  int64_t per_unit = fill > by_len ? fill : by_len;
+  if (per_unit > kMaxMfmaSplits) per_unit = kMaxMfmaSplits;  // longer splits instead
+  int64_t per = (tokens + per_unit - 1) / per_unit;
+  per = (per + 63) / 64 * 64;
+  SplitPlan plan;
+  plan.split_tokens = static_cast<int32_t>(per);
+  plan.num_splits = static_cast<int32_t>((tokens + per - 1) / per);
+  return plan;
+}
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_kv_tokens) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  int32_t most = 0;
+  for (const SplitPlan& pl : {plan_splits(batch, num_kv_heads, max_kv_tokens),
+                              plan_splits_mfma(batch, num_kv_heads, max_kv_tokens, false),
+                              plan_splits_mfma(batch, num_kv_heads, max_kv_tokens, true)})
+    most = pl.num_splits > most ? pl.num_splits : most;
+  const size_t splits = static_cast<size_t>(most);
+  const size_t heads = static_cast<size_t>(batch) * num_q_heads * splits;
+  WorkspaceLayout w;
+  w.o_offset = 0;
+  w.lse_offset = w.o_offset + up(heads * head_dim * sizeof(float));
+  w.total = w.lse_offset + up(heads * sizeof(float));
+  return w;
 }
 
 hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream) {
+  if (use_mfma_path(p.bf16, p.head_dim)) return launch_decode_mfma_ring(p, stream);
   return launch_decode<RingAddr>(p, stream);
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
+  if (use_mfma_path(p.bf16, p.head_dim)) return launch_decode_mfma_pool(p, stream);
   return launch_decode<PoolAddr>(p, stream);
 }
 

@@ -106,11 +106,18 @@ float resolve_scale(float scale, int32_t head_dim) {
   return s * 1.44269504088896340736f;  // fold log2(e): softmax runs on exp2
 }
 
-void fill_workspace_ptrs(swa::DecodeParams& p, void* workspace) {
-  const size_t heads = static_cast<size_t>(p.batch) * p.num_q_heads * p.num_splits;
-  const size_t o_bytes = (heads * p.head_dim * sizeof(float) + 255) / 256 * 256;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+void fill_workspace_ptrs(swa::DecodeParams& p, void* workspace,
+                         const swa::WorkspaceLayout& lay) {
+  char* base = static_cast<char*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(base + lay.o_offset);
+  p.ws_lse = reinterpret_cast<float*>(base + lay.lse_offset);
+}
+
+swa::SplitPlan plan_for(int bf16, int32_t head_dim, int32_t batch, int32_t num_kv_heads,
+                        int32_t max_tokens, bool ragged) {
+  return swa::use_mfma_path(bf16, head_dim)
+             ? swa::plan_splits_mfma(batch, num_kv_heads, max_tokens, ragged)
+             : swa::plan_splits(batch, num_kv_heads, max_tokens);
 }
 
 int log2_exact(int32_t x) {
@@ -211,8 +218,7 @@ swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
   if (st != SWA_OK) return st;
   if (!head_dim_supported(head_dim))
     return fail(SWA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
-  const swa::SplitPlan plan = swa::plan_splits(batch, num_kv_heads, max_kv_tokens);
-  *bytes = swa::workspace_bytes(batch, num_q_heads, head_dim, plan);
+  *bytes = swa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_kv_tokens).total;
   return ok();
 }
 
@@ -224,9 +230,14 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
   swa_status st = check_group(num_q_heads, cfg.num_kv_heads);
   if (st != SWA_OK) return st;
   const int32_t slots = cfg.num_sinks + cfg.window;
-  const swa::SplitPlan plan = swa::plan_splits(cfg.batch, cfg.num_kv_heads, slots);
-  const size_t need = swa::workspace_bytes(cfg.batch, num_q_heads, cfg.head_dim, plan);
-  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, need);
+  if (swa::use_mfma_path(cfg.dtype == SWA_BF16, cfg.head_dim) && slots > swa::kMaxMfmaTokens)
+    return fail(SWA_ERR_UNSUPPORTED, "num_sinks + window above %lld rows per sequence",
+                static_cast<long long>(swa::kMaxMfmaTokens));
+  const swa::SplitPlan plan =
+      plan_for(cfg.dtype == SWA_BF16, cfg.head_dim, cfg.batch, cfg.num_kv_heads, slots, false);
+  const swa::WorkspaceLayout lay =
+      swa::workspace_layout(cfg.batch, num_q_heads, cfg.num_kv_heads, cfg.head_dim, slots);
+  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, lay.total);
   if (st != SWA_OK) return st;
 
   swa::DecodeParams p{};
@@ -246,7 +257,7 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
   p.lse = lse;
   p.out_bf16 = out_dtype == SWA_BF16;
   p.bf16 = cfg.dtype == SWA_BF16;
-  fill_workspace_ptrs(p, workspace);
+  fill_workspace_ptrs(p, workspace, lay);
   return from_hip(swa::launch_decode_ring(p, static_cast<hipStream_t>(stream)),
                   "decode_attn_ring");
 }
@@ -284,9 +295,15 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
       !aligned(seq_lens, 4))
     return fail(SWA_ERR_INVALID_ARG, "pool buffers misaligned");
   const int32_t max_tokens = desc->max_blocks_per_seq * desc->block_size;
-  const swa::SplitPlan plan = swa::plan_splits(desc->batch, desc->num_kv_heads, max_tokens);
-  const size_t need = swa::workspace_bytes(desc->batch, desc->num_q_heads, desc->head_dim, plan);
-  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, need);
+  if (swa::use_mfma_path(desc->dtype == SWA_BF16, desc->head_dim) &&
+      max_tokens > swa::kMaxMfmaTokens)
+    return fail(SWA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size above %lld rows per sequence",
+                static_cast<long long>(swa::kMaxMfmaTokens));
+  const swa::SplitPlan plan = plan_for(desc->dtype == SWA_BF16, desc->head_dim, desc->batch,
+                                       desc->num_kv_heads, max_tokens, true);
+  const swa::WorkspaceLayout lay = swa::workspace_layout(
+      desc->batch, desc->num_q_heads, desc->num_kv_heads, desc->head_dim, max_tokens);
+  st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, lay.total);
   if (st != SWA_OK) return st;
 
   swa::DecodeParams p{};
@@ -310,7 +327,7 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
   p.lse = lse;
   p.out_bf16 = out_dtype == SWA_BF16;
   p.bf16 = desc->dtype == SWA_BF16;
-  fill_workspace_ptrs(p, workspace);
+  fill_workspace_ptrs(p, workspace, lay);
   return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream)),
                   "decode_attn_paged");
 }

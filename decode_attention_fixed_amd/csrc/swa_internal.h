@@ -10,6 +10,9 @@
 namespace swa {
 
 constexpr int kMaxGroup = 8;
+constexpr int kMfmaWaves = 8;  // waves per workgroup of the bf16 / head_dim 128 decode kernel
+constexpr int kMaxMfmaSplits = 512;         // splits per sequence on that path
+constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path
 
 struct AppendParams {
   const void* k_new;      // [B, T, Hkv, d]
@@ -69,16 +72,31 @@ struct SplitPlan {
 };
 
 // How a sequence's token range is cut into splits (shared by the workspace
-// query and the launch so both agree).
+// query and the launch so both agree).  The bf16 / head_dim-128 path runs
+// multi-wave workgroups and merges across workgroups inside the kernel; the
+// generic path runs one wave per split and a separate merge kernel.
+bool use_mfma_path(int bf16, int32_t head_dim);
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens);
-size_t workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                       const SplitPlan& plan);
+SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens,
+                           bool ragged);
+
+// Workspace layout: [partial outputs | partial lse], each region 256-byte
+// aligned.  Sized for whichever path needs more.
+struct WorkspaceLayout {
+  size_t o_offset;
+  size_t lse_offset;
+  size_t total;
+};
+WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_kv_tokens);
 
 hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream);
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream);
 hipError_t launch_write_paged(const PagedWriteParams& p, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream);
 
 bool group_supported(int g);
 

@@ -121,9 +121,8 @@ class PagedState:
         self.seq_lens = torch.from_numpy(lens.astype(np.int32)).to(device)
         self.block_valid = (torch.from_numpy(np.ascontiguousarray(valid)).to(device)
                             if valid is not None else None)
-        n = B.decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                          table.shape[1] * w.block_size)
-        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        self.workspace = B.new_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         table.shape[1] * w.block_size, device)
         self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=out_dtype,
                                device=device)
         self.lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=device)

@@ -119,7 +119,11 @@ swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new
 
 /* Workspace (device bytes) that decode_attn_ring / decode_attn_paged need for
  * these sizes; max_kv_tokens = S + W for a ring cache, max_blocks_per_seq *
- * block_size for a paged pool.  0 bytes is never returned. */
+ * block_size for a paged pool.  0 bytes is never returned.
+ *
+ * The workspace holds the per-split partial results of one call; it needs no
+ * initialisation.  Calls that share a workspace must not overlap (use one
+ * stream, or one workspace per stream). */
 swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_kv_tokens, size_t* bytes);
 
@@ -138,7 +142,8 @@ swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *   lse       [B, Hq] float32 natural-log log-sum-exp of the scaled scores,
  *             or NULL.  A head with no resident row gets out = 0, lse = -inf.
  *   workspace decode_attn_workspace_bytes(B, Hq, Hkv, d, S + W) bytes,
- *             device, 256-byte aligned; contents need no initialisation. */
+ *             device, 256-byte aligned; contents need no initialisation.
+ *   A bf16 cache with d = 128 takes up to 4,194,304 rows per sequence. */
 swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
                             float scale, void* out, swa_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);

@@ -70,10 +70,22 @@ def draw_rows(seed: int, tensor: int, seq: int, positions, heads: int, dim: int,
     if pos.min() < 0:
         raise ValueError("positions must be non-negative")
     chunks = pos // CHUNK
-    for c in np.unique(chunks):
-        sel = np.nonzero(chunks == c)[0]
-        block = _draw_chunk(seed, tensor, seq, int(c), heads, dim, scale)
+    order = np.argsort(chunks, kind="stable")
+    uniq, starts = np.unique(chunks[order], return_index=True)
+    bounds = list(starts[1:]) + [pos.size]
+
+    def work(k: int) -> None:
+        c = int(uniq[k])
+        sel = order[starts[k]:bounds[k]]
+        block = _draw_chunk(seed, tensor, seq, c, heads, dim, scale)
         out[sel] = block[pos[sel] - c * CHUNK]
+
+    if uniq.size > 16:
+        with _cf.ThreadPoolExecutor(max_workers=_default_workers()) as pool:
+            list(pool.map(work, range(uniq.size)))
+    else:
+        for k in range(uniq.size):
+            work(k)
     return encode_storage(out, dtype)
 
 

@@ -150,8 +150,7 @@ def _probe_pool(batch, hkv, d, bs, tables, resident_tokens, nphys, maxb):
 def _run_paged(batch, hq, hkv, d, bs, maxb, nphys, k, v, bt, lens, valid=None, q=None):
     from decode_attention_fixed_amd import binding as B
     desc = B.make_paged_desc(batch, hq, hkv, d, bs, maxb, nphys, "bf16")
-    ws = torch.empty(B.decode_attn_workspace_bytes(batch, hq, hkv, d, maxb * bs),
-                     dtype=torch.uint8, device="cuda")
+    ws = B.new_workspace(batch, hq, hkv, d, maxb * bs)
     if q is None:
         q = torch.randn(batch, hq, d, device="cuda").to(torch.bfloat16)
     out = torch.empty(batch, hq, d, device="cuda")
