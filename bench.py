@@ -11,17 +11,20 @@ staged on the device beforehand.
 Prints one JSON line:
   value            KV-read GB/s of the whole job: algorithmic KV bytes per step
                    (resident rows x Hkv x d x 2 x element bytes, summed over
-                   the batch) x steps / wall time of the timed steps.
+                   the batch) x steps / time of the timed steps (HIP events
+                   at the two ends of the region only).
   roofline         for the dominant kernel (the decode kernel): algorithmic
                    bytes per launch / its mean launch duration, from HIP events
-                   recorded on the launch stream around every decode call,
-                   against the 8 TB/s HBM peak; `traffic` is the measured HBM
-                   bytes per launch from rocprofv3 counters (profiles/) when
-                   they were taken on the current kernel source, else null.
+                   recorded on the launch stream around every decode call in a
+                   second timed region of the same steps, against the 8 TB/s
+                   HBM peak; `traffic` is the measured HBM bytes per launch
+                   from rocprofv3 counters (profiles/) when they were taken on
+                   the current kernel sources, else null.
   cpu_baseline     the float64 NumPy oracle on a bounded sample of the same
                    workload (inputs already in host memory), host cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
 
 from __future__ import annotations
@@ -39,7 +42,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
-DECODE_SRC = os.path.join(ROOT, "decode_attention_fixed_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "decode_attention_fixed_amd", "csrc", f)
+               for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
 
 
 def log(msg: str) -> None:
@@ -87,10 +91,16 @@ def traffic_record():
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != decode_source_sha():
         return None
     return rec
+
+
+def decode_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------
@@ -107,7 +117,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     from synth.draws import draw_rows_parallel
 
     torch.cuda.set_device(0)
-    total = warmup + steps
+    total = warmup + 2 * steps  # warmup, then two timed regions of `steps` steps
     t0 = time.time()
     if w.kind == "ring":
         st = RingState(w)
@@ -137,8 +147,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     else:
         st = PagedState(w, out_dtype=torch.float32)
         st.fill()
-        qs = torch.stack([st.step_query(i % w.decode_steps) for i in range(min(total,
-                                                                                w.decode_steps))])
+        qs = torch.stack([st.step_query(i) for i in range(min(total, w.decode_steps))])
         # Pools smaller than the ~256 MB last-level cache are cycled through
         # enough copies (>= 600 MB) that a step cannot be served from cache.
         pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
@@ -161,23 +170,33 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
         decode(i)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # Region 1: whole steps, events only at the two ends.
     begin = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     begin.record()
     for s in range(steps):
         i = warmup + s
         pre(i)
-        ev[s][0].record()
         decode(i)
-        ev[s][1].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = begin.elapsed_time(end)
+
+    # Region 2: the same steps again, events around every decode call.  The
+    # ring cache keeps advancing (positions continue), so every step still
+    # appends a new token and attends over a full window.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        i = warmup + steps + s
+        pre(i)
+        ev[s][0].record()
+        decode(i)
+        ev[s][1].record()
+    torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     return {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": sum(dec_ms) / len(dec_ms),
             "decode_ms_min": min(dec_ms)}
@@ -241,6 +260,27 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
                        f"scaled to the full batch")}
 
 
+def copy_calibration(nbytes: int = 1 << 30) -> None:
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings scale the decode kernel's readings to bytes."""
+    import torch
+    torch.cuda.set_device(0)
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    print(json.dumps({"copy_bytes": nbytes, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +288,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mha-ring")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -255,6 +296,10 @@ def main() -> int:
         print(f"bench.py measures the decode path on one GPU only; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported: run with --gpus 1", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
 
     from synth import WORKLOADS
     w = WORKLOADS[args.workload]
