@@ -354,11 +354,11 @@ SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_t
                            bool ragged) {
   // One multi-wave workgroup per split.  Enough splits per (sequence, kv head)
   // that the grid covers the 256 CUs; splits are whole 64-row tiles and at
-  // most 8192 rows long, or 2048 when sequence lengths differ (a paged pool),
+  // most 8192 rows long, or kRaggedSplit when lengths differ (a paged pool),
   // so that short and long sequences balance over the CUs.
   const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
   const int64_t tokens = max_kv_tokens > 0 ? max_kv_tokens : 1;
-  const int64_t cap = ragged ? 2048 : 8192;
+  const int64_t cap = ragged ? kRaggedSplit : 8192;
   const int64_t fill = (256 + units - 1) / units;
   const int64_t by_len = (tokens + cap - 1) / cap;
   int64_t per_unit = fill > by_len ? fill : by_len;

@@ -15,9 +15,13 @@
 //
 // Per tile of NS 16-row subtiles and wave (lane l, row group lq = l / 16,
 // column lc = l % 16):
-//   K  4NS x 16-byte loads: lane l holds K[16u + lc][32s + 8lq .. +7] for row
-//      subtile u < NS and k-step s < 4, which is the A operand of
-//      v_mfma_f32_16x16x32_bf16 (16 rows x 32 dims).  The B operand holds the
+//   K  4NS x 16-byte loads, each covering four whole 256-byte rows (a load
+//      in the operand layout would read 64-byte pieces of 16 rows per
+//      instruction, which streams ~15% slower); the wave passes its K tile
+//      through a swizzled LDS area so that lane l then holds
+//      K[16u + lc][32s + 8lq .. +7] for row subtile u < NS and k-step s < 4,
+//      the A operand of v_mfma_f32_16x16x32_bf16 (16 rows x 32 dims).  The B
+//      operand holds the
 //      g query heads of the kv head (padded to 16 with zeros): lane l holds
 //      q[head lc][32s + 8lq .. +7].  The result D[row 4lq + r][head lc] lands
 //      in lane l, register r: scores of rows 16u + 4lq + r for head lc.
@@ -142,20 +146,26 @@ struct PoolRows {
 };
 
 // Row subtiles (16 rows each) per wave tile: 4 when few query heads share the
-// kv head, 2 when the P*V accumulators take more registers (8-wave
+// kv head, fewer when the P*V accumulators take more registers (8-wave
 // workgroups cap a wave at 256 VGPRs).
 template <int G>
-constexpr int subtiles() { return G <= 2 ? 4 : 2; }
+constexpr int subtiles() { return G <= 2 ? 4 : (G < 8 ? 2 : 1); }
 
 template <int G, class Rows, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   static_assert(G >= 1 && G <= 16, "q heads per kv head");
   constexpr int NS = subtiles<G>();
   constexpr int TILE = 16 * NS;
+  // LDS: each wave's K tile while streaming; the same bytes hold the waves'
+  // P*V accumulators for the final merge.
+  constexpr int KBUF = TILE * 16;  // 16-byte chunks per wave: TILE rows x 256 B
+  constexpr size_t KBYTES = static_cast<size_t>(NW) * KBUF * 16;
+  constexpr size_t ABYTES = static_cast<size_t>(NW) * G * kD * sizeof(float);
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[KBYTES > ABYTES ? KBYTES : ABYTES];
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
-  __shared__ float s_acc[NW][G][kD];
   __shared__ int32_t s_blk[kMaxSplitBlocks];
+  float(*s_acc)[G][kD] = reinterpret_cast<float(*)[G][kD]>(s_raw);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -199,35 +209,81 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
+  // This wave's K staging area: row rho of subtile u, 16-byte chunk c lives at
+  // chunk (u * 16 + rho) * 16 + (c ^ rho), so both the row-wise writes and the
+  // operand-wise reads below touch 16 distinct bank groups per 16 lanes.
+  uint4* s_k = reinterpret_cast<uint4*>(s_raw) + wave * KBUF;
+
   for (int ts = t0 + wave * TILE; ts < t1; ts += NW * TILE) {
-    Vec16 kr[NS][kKSteps];
-    Vec16 vr[NS][4];
+    Vec16 kr[NS][4];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
+    Vec16 vr[NS][4];  // V: row 4lq + r of subtile u, chunk lc
     uint32_t vm[NS];  // bit i: row ts + 16u + i is resident
+    size_t base[NS];
+    bool live[NS];
+    // Every load instruction reads four whole 256-byte rows; K first, so the
+    // score phase waits on K while the V loads are still in flight.
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const int tu = ts + 16 * u;
       vm[u] = 0;
-      size_t base = 0;
-      if (tu < t1 && rows.subtile(p, s_blk, t0, tu, base)) {
+      base[u] = 0;
+      live[u] = tu < t1 && rows.subtile(p, s_blk, t0, tu, base[u]);
+      if (live[u]) {
         const int tk = tu + lc;
         const bool okk = tk < t1 && rows.row_ok(tk);
         vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
-        const size_t koff = base + static_cast<size_t>(tk < t1 ? lc : 0) * kD;
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) kr[u][s] = load16_stream(kb + koff + 32 * s + 8 * lq);
+        for (int i = 0; i < 4; ++i) {
+          const int rho = 4 * i + lq;
+          const size_t koff = base[u] + static_cast<size_t>(tu + rho < t1 ? rho : 0) * kD;
+          kr[u][i] = load16_stream(kb + koff + 8 * lc);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kr[u][i] = Vec16{};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int tu = ts + 16 * u;
+      if (live[u]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * lq + r;
-          const size_t voff = base + static_cast<size_t>(tu + i < t1 ? i : 0) * kD;
+          const size_t voff = base[u] + static_cast<size_t>(tu + i < t1 ? i : 0) * kD;
           vr[u][r] = load16_stream(vb + voff + 8 * lc);
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) kr[u][s] = Vec16{};
-#pragma unroll
         for (int r = 0; r < 4; ++r) vr[u][r] = Vec16{};
       }
     }
+
+    // K chunks into the MFMA A-operand layout through LDS (DS instructions of
+    // one wave execute in order; the wave barriers only stop the compiler from
+    // moving LDS accesses across each other).
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = 4 * i + lq;
+        s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
+            make_uint4(kr[u][i].w[0], kr[u][i].w[1], kr[u][i].w[2], kr[u][i].w[3]);
+      }
+    __builtin_amdgcn_wave_barrier();
+    Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
+        ka[u][s].w[0] = t.x;
+        ka[u][s].w[1] = t.y;
+        ka[u][s].w[2] = t.z;
+        ka[u][s].w[3] = t.w;
+      }
+    __builtin_amdgcn_wave_barrier();
     uint32_t all = 0xffffu;
 #pragma unroll
     for (int u = 0; u < NS; ++u) all &= vm[u];
@@ -241,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[u][s]), qop[s], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
@@ -319,6 +375,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
       acc[h][e] += __shfl_xor(acc[h][e], 16);
       acc[h][e] += __shfl_xor(acc[h][e], 32);
     }
+  __syncthreads();  // every wave is done with its K staging area (aliases s_acc)
   if (lane < G) {
     s_m[wave][lane] = m;
     s_l[wave][lane] = lsum;
@@ -438,9 +495,8 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p, int r
   }
 }
 
-template <class Rows>
+template <class Rows, int NW>
 hipError_t launch_rows(const DecodeParams& p, int ragged, hipStream_t stream) {
-  constexpr int NW = kMfmaWaves;
   const unsigned grid =
       static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
   switch (p.num_q_heads / p.num_kv_heads) {
@@ -468,11 +524,16 @@ hipError_t launch_rows(const DecodeParams& p, int ragged, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
-  return launch_rows<RingRows>(p, 0, stream);
+  return launch_rows<RingRows, kRingWaves>(p, 0, stream);
 }
 
 hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream) {
-  return launch_rows<PoolRows>(p, 1, stream);
+  // Many workgroups (ragged or long pools): 4-wave workgroups, two per CU, so
+  // one workgroup's start and end overlap the other's streaming.  Few
+  // workgroups: 8 waves each, to keep enough waves per CU.
+  const int64_t wgs = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
+  if (wgs >= kPoolManyWorkgroups) return launch_rows<PoolRows, 4>(p, 1, stream);
+  return launch_rows<PoolRows, 8>(p, 1, stream);
 }
 
 }  // namespace swa

@@ -10,7 +10,21 @@
 namespace swa {
 
 constexpr int kMaxGroup = 8;
-constexpr int kMfmaWaves = 8;  // waves per workgroup of the bf16 / head_dim 128 decode kernel
+// Tuning of the bf16 / head_dim 128 decode kernel: waves per workgroup for
+// ring caches, the workgroup count from which paged pools use 4-wave
+// workgroups, and the longest split of a ragged (paged) sequence.
+#ifndef SWA_RING_WAVES
+#define SWA_RING_WAVES 8
+#endif
+#ifndef SWA_POOL_MANY_WGS
+#define SWA_POOL_MANY_WGS 1024
+#endif
+#ifndef SWA_RAGGED_SPLIT
+#define SWA_RAGGED_SPLIT 2048
+#endif
+constexpr int kRingWaves = SWA_RING_WAVES;
+constexpr int64_t kPoolManyWorkgroups = SWA_POOL_MANY_WGS;
+constexpr int kRaggedSplit = SWA_RAGGED_SPLIT;
 constexpr int kMaxMfmaSplits = 512;         // splits per sequence on that path
 constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path
 
