@@ -350,19 +350,16 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens
   return plan;
 }
 
-SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens,
-                           bool ragged) {
-  // One multi-wave workgroup per split.  Enough splits per (sequence, kv head)
-  // that the grid covers the 256 CUs; splits are whole 64-row tiles and at
-  // most 8192 rows long, or kRaggedSplit when lengths differ (a paged pool),
-  // so that short and long sequences balance over the CUs.
+SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens) {
+  // Ring caches on the bf16 / head_dim 128 path: one multi-wave workgroup per
+  // split, enough splits per (sequence, kv head) that the grid covers the 256
+  // CUs, splits of whole 64-row tiles and at most 8192 rows.
   const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
   const int64_t tokens = max_kv_tokens > 0 ? max_kv_tokens : 1;
-  const int64_t cap = ragged ? kRaggedSplit : 8192;
   const int64_t fill = (256 + units - 1) / units;
-  const int64_t by_len = (tokens + cap - 1) / cap;
+  const int64_t by_len = (tokens + 8191) / 8192;
   int64_t per_unit = fill > by_len ? fill : by_len;
-  if (per_unit > kMaxMfmaSplits) per_unit = kMaxMfmaSplits;  // longer splits instead
+  if (per_unit > kMaxMfmaSplits) per_unit = kMaxMfmaSplits;
   int64_t per = (tokens + per_unit - 1) / per_unit;
   per = (per + 63) / 64 * 64;
   SplitPlan plan;
@@ -374,17 +371,18 @@ SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_t
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_kv_tokens) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  int32_t most = 0;
+  const size_t units = static_cast<size_t>(batch) * num_kv_heads;
+  const size_t g = static_cast<size_t>(num_q_heads / num_kv_heads);
+  size_t slots = units + kPoolGrid;
   for (const SplitPlan& pl : {plan_splits(batch, num_kv_heads, max_kv_tokens),
-                              plan_splits_mfma(batch, num_kv_heads, max_kv_tokens, false),
-                              plan_splits_mfma(batch, num_kv_heads, max_kv_tokens, true)})
-    most = pl.num_splits > most ? pl.num_splits : most;
-  const size_t splits = static_cast<size_t>(most);
-  const size_t heads = static_cast<size_t>(batch) * num_q_heads * splits;
+                              plan_splits_mfma(batch, num_kv_heads, max_kv_tokens)}) {
+    const size_t n = units * static_cast<size_t>(pl.num_splits);
+    slots = n > slots ? n : slots;
+  }
   WorkspaceLayout w;
   w.o_offset = 0;
-  w.lse_offset = w.o_offset + up(heads * head_dim * sizeof(float));
-  w.total = w.lse_offset + up(heads * sizeof(float));
+  w.lse_offset = up(slots * g * head_dim * sizeof(float));
+  w.total = w.lse_offset + up(slots * g * sizeof(float));
   return w;
 }
 

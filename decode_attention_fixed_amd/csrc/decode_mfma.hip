@@ -1,17 +1,27 @@
 // Read half of the decode step for bf16 caches with head_dim 128: split-K
 // over the resident rows, q-group x K-tile scores on the matrix cores, online
 // softmax and P*V in fp32 registers, in-workgroup merge of the waves.  A
-// sequence that fits one split gets its output written directly (one launch
-// per decode call); longer ones are combined by a small merge launch.
+// (sequence, kv head) processed by one workgroup gets its output written
+// directly (one launch per decode call); one spread over several workgroups
+// is combined by a small merge launch.
 //
 // Math as in decode.hip ([sink] weight formula; [kvc] §2.2).  Only the
 // resident rows take part: empty ring slots, absent or out-of-range blocks and
 // rows past the sequence length are removed with selects, never multiplied by
 // zero ([pool] "absent blocks are as if they did not exist").
 //
-// Workgroup = NW waves = one (sequence b, kv head, split).  A split is a
-// contiguous range of split_tokens rows; its tiles are dealt to the waves
-// round-robin, so the workgroup streams contiguous memory.
+// Work units.  A piece is a contiguous range of rows of one (sequence b, kv
+// head); a workgroup of NW waves attends a piece with all g query heads of the
+// kv head, its tiles dealt to the waves round-robin so that the workgroup
+// streams contiguous memory.
+//   ring cache  all sequences have S + W slots: a grid of (b, kv head, split)
+//               with equal splits, one piece per workgroup.
+//   paged pool  lengths differ: a fixed grid of workgroups, each taking an
+//               equal share of all resident rows (every sequence's rows padded
+//               to a 64-row multiple, kv heads laid end to end); its share
+//               may span several pieces.  Equal shares keep the last round of
+//               workgroups from running half empty when long and short
+//               sequences mix.
 //
 // Per tile of NS 16-row subtiles and wave (lane l, row group lq = l / 16,
 // column lc = l % 16):
@@ -78,14 +88,38 @@ __device__ __forceinline__ float row_bcast(float x) {
                                          false));
 }
 
+// Broadcast of lane h of each 16-lane row; h is a compile-time constant after
+// unrolling, so the switch folds to one DPP move.
+__device__ __forceinline__ float row_bcast_dyn(float x, int h) {
+  switch (h) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);
+    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);
+    case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);
+    case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);
+    default: return row_bcast<15>(x);
+  }
+}
+
 __device__ __forceinline__ float xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask));
 }
 
 // Largest block-table span one split can touch: splits are at most 8192 rows
 // and blocks at least 16 rows, plus one for a split that starts mid-block.
-constexpr int kMaxSplitBlocks = 8192 / 16 + 1;
-constexpr int kMaxSplits = 512;  // splits per sequence (the plan never exceeds it)
+constexpr int kChunk = 8192;  // rows whose block ids are staged in LDS at a time
+constexpr int kMaxSplitBlocks = kChunk / 16 + 1;
+constexpr int kMaxSplits = 512;  // ring splits per sequence (the plan never exceeds it)
 
 // Ring: rows of head (b, h) are contiguous, slot t at row t; a row is
 // resident iff its slot holds a position.
@@ -151,40 +185,38 @@ struct PoolRows {
 template <int G>
 constexpr int subtiles() { return G <= 2 ? 4 : (G < 8 ? 2 : 1); }
 
-template <int G, class Rows, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
-  static_assert(G >= 1 && G <= 16, "q heads per kv head");
-  constexpr int NS = subtiles<G>();
-  constexpr int TILE = 16 * NS;
-  // LDS: each wave's K tile while streaming; the same bytes hold the waves'
-  // P*V accumulators for the final merge.
-  constexpr int KBUF = TILE * 16;  // 16-byte chunks per wave: TILE rows x 256 B
-  constexpr size_t KBYTES = static_cast<size_t>(NW) * KBUF * 16;
-  constexpr size_t ABYTES = static_cast<size_t>(NW) * G * kD * sizeof(float);
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[KBYTES > ABYTES ? KBYTES : ABYTES];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
-  __shared__ int32_t s_blk[kMaxSplitBlocks];
-  float(*s_acc)[G][kD] = reinterpret_cast<float(*)[G][kD]>(s_raw);
+template <int G, int NW>
+struct Smem {
+  static constexpr int NS = subtiles<G>();
+  static constexpr int TILE = 16 * NS;
+  static constexpr int KBUF = TILE * 16;  // 16-byte chunks per wave: TILE rows x 256 B
+  static constexpr size_t KBYTES = static_cast<size_t>(NW) * KBUF * 16;
+  static constexpr size_t ABYTES = static_cast<size_t>(NW) * G * kD * sizeof(float);
+  // each wave's K tile while streaming; the same bytes then hold the waves'
+  // P*V accumulators for the workgroup merge
+  __attribute__((aligned(16))) unsigned char raw[KBYTES > ABYTES ? KBYTES : ABYTES];
+  float m[NW][G];
+  float l[NW][G];
+  int32_t blk[kMaxSplitBlocks];
+};
 
+// Attention of the G query heads of (b, kvh) over rows [t0, t1) by the whole
+// workgroup.  Writes the output and lse (direct) or, for a piece of a longer
+// sequence, the normalised partial output and base-2 lse at partial slot
+// `slot` (layout [slot][head][d]).  Every thread of the workgroup must call it
+// with the same arguments; it returns with LDS free for reuse.
+template <int G, class Rows, int NW>
+__device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int kvh, int t0,
+                             int t1, bool direct, size_t slot) {
+  constexpr int NS = Smem<G, NW>::NS;
+  constexpr int TILE = Smem<G, NW>::TILE;
+  constexpr int KBUF = Smem<G, NW>::KBUF;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane >> 4;
   const int lc = lane & 15;
-  const int ns = p.num_splits;
-  const int split = blockIdx.x % ns;
-  const int unit = blockIdx.x / ns;
-  const int b = unit / p.num_kv_heads;
-  const int kvh = unit - b * p.num_kv_heads;
-  const int ntok = Rows::tokens(p, b);
-  const int nsb = ntok > 0 ? (ntok + p.split_tokens - 1) / p.split_tokens : 1;
-  if (split >= nsb) return;  // past the sequence: this workgroup takes no part
-  const int t0 = split * p.split_tokens;
-  const int t1 = min(t0 + p.split_tokens, ntok);
   const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
   const Rows rows(p, b, kvh);
-  if (t1 > t0) rows.stage(p, t0, t1, s_blk);
-  __syncthreads();
   const uint16_t* kb = static_cast<const uint16_t*>(p.k);
   const uint16_t* vb = static_cast<const uint16_t*>(p.v);
 
@@ -212,157 +244,151 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   // This wave's K staging area: row rho of subtile u, 16-byte chunk c lives at
   // chunk (u * 16 + rho) * 16 + (c ^ rho), so both the row-wise writes and the
   // operand-wise reads below touch 16 distinct bank groups per 16 lanes.
-  uint4* s_k = reinterpret_cast<uint4*>(s_raw) + wave * KBUF;
+  uint4* s_k = reinterpret_cast<uint4*>(sm.raw) + wave * KBUF;
 
-  for (int ts = t0 + wave * TILE; ts < t1; ts += NW * TILE) {
-    Vec16 kr[NS][4];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
-    Vec16 vr[NS][4];  // V: row 4lq + r of subtile u, chunk lc
-    uint32_t vm[NS];  // bit i: row ts + 16u + i is resident
-    size_t base[NS];
-    bool live[NS];
-    // Every load instruction reads four whole 256-byte rows; K first, so the
-    // score phase waits on K while the V loads are still in flight.
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const int c1 = min(c0 + kChunk, t1);
+    rows.stage(p, c0, c1, sm.blk);
+    __syncthreads();
+    for (int ts = c0 + wave * TILE; ts < c1; ts += NW * TILE) {
+      Vec16 kr[NS][4];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
+      Vec16 vr[NS][4];  // V: row 4lq + r of subtile u, chunk lc
+      uint32_t vm[NS];  // bit i: row ts + 16u + i is resident
+      size_t base[NS];
+      bool live[NS];
+      // Every load instruction reads four whole 256-byte rows; K first, so
+      // the score phase waits on K while the V loads are still in flight.
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int tu = ts + 16 * u;
-      vm[u] = 0;
-      base[u] = 0;
-      live[u] = tu < t1 && rows.subtile(p, s_blk, t0, tu, base[u]);
-      if (live[u]) {
-        const int tk = tu + lc;
-        const bool okk = tk < t1 && rows.row_ok(tk);
-        vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
+      for (int u = 0; u < NS; ++u) {
+        const int tu = ts + 16 * u;
+        vm[u] = 0;
+        base[u] = 0;
+        live[u] = tu < c1 && rows.subtile(p, sm.blk, c0, tu, base[u]);
+        if (live[u]) {
+          const int tk = tu + lc;
+          const bool okk = tk < c1 && rows.row_ok(tk);
+          vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rho = 4 * i + lq;
+            const size_t koff = base[u] + static_cast<size_t>(tu + rho < c1 ? rho : 0) * kD;
+            kr[u][i] = load16_stream(kb + koff + 8 * lc);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kr[u][i] = Vec16{};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int tu = ts + 16 * u;
+        if (live[u]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * lq + r;
+            const size_t voff = base[u] + static_cast<size_t>(tu + i < c1 ? i : 0) * kD;
+            vr[u][r] = load16_stream(vb + voff + 8 * lc);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[u][r] = Vec16{};
+        }
+      }
+
+      // K chunks into the MFMA A-operand layout through LDS (DS instructions
+      // of one wave execute in order; the wave barriers only stop the compiler
+      // from moving LDS accesses across each other).
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rho = 4 * i + lq;
-          const size_t koff = base[u] + static_cast<size_t>(tu + rho < t1 ? rho : 0) * kD;
-          kr[u][i] = load16_stream(kb + koff + 8 * lc);
+          s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
+              make_uint4(kr[u][i].w[0], kr[u][i].w[1], kr[u][i].w[2], kr[u][i].w[3]);
         }
-      } else {
+      __builtin_amdgcn_wave_barrier();
+      Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kr[u][i] = Vec16{};
-      }
-    }
+      for (int u = 0; u < NS; ++u)
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int tu = ts + 16 * u;
-      if (live[u]) {
+        for (int s = 0; s < kKSteps; ++s) {
+          const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
+          ka[u][s].w[0] = t.x;
+          ka[u][s].w[1] = t.y;
+          ka[u][s].w[2] = t.z;
+          ka[u][s].w[3] = t.w;
+        }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t all = 0xffffu;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) all &= vm[u];
+      const bool all_ok = all == 0xffffu;
+
+      // scores (log2 units) of rows 16u + 4lq + r for head lc
+      float x[NS][4];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 4 * lq + r;
-          const size_t voff = base[u] + static_cast<size_t>(tu + i < t1 ? i : 0) * kD;
-          vr[u][r] = load16_stream(vb + voff + 8 * lc);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vr[u][r] = Vec16{};
-      }
-    }
-
-    // K chunks into the MFMA A-operand layout through LDS (DS instructions of
-    // one wave execute in order; the wave barriers only stop the compiler from
-    // moving LDS accesses across each other).
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rho = 4 * i + lq;
-        s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
-            make_uint4(kr[u][i].w[0], kr[u][i].w[1], kr[u][i].w[2], kr[u][i].w[3]);
-      }
-    __builtin_amdgcn_wave_barrier();
-    Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
-        ka[u][s].w[0] = t.x;
-        ka[u][s].w[1] = t.y;
-        ka[u][s].w[2] = t.z;
-        ka[u][s].w[3] = t.w;
-      }
-    __builtin_amdgcn_wave_barrier();
-    uint32_t all = 0xffffu;
-#pragma unroll
-    for (int u = 0; u < NS; ++u) all &= vm[u];
-    const bool all_ok = all == 0xffffu;
-
-    // scores (log2 units) of rows 16u + 4lq + r for head lc
-    float x[NS][4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
-        x[u][r] = ok ? d[r] * c : kNegInf;
-        tmax = fmaxf(tmax, x[u][r]);
-      }
-    }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
-    const float mn = fmaxf(m, tmax);
-    // mn == -inf: nothing resident so far for this head; keep everything at 0
-    const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
-    m = mn;
-    float pr[NS][4];
-    float tsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[u][r] = x[u][r] == kNegInf ? 0.f : exp2f(x[u][r] - mn);
-        tsum += pr[u][r];
-      }
-    lsum = lsum * alpha + tsum;
-
-    // P * V
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = 1.f;
-      switch (h) {  // compile-time dispatch of the DPP source lane
-#define SWA_B(H) case H: a = row_bcast<H>(alpha); break;
-        SWA_B(0) SWA_B(1) SWA_B(2) SWA_B(3) SWA_B(4) SWA_B(5) SWA_B(6) SWA_B(7)
-        SWA_B(8) SWA_B(9) SWA_B(10) SWA_B(11) SWA_B(12) SWA_B(13) SWA_B(14) SWA_B(15)
-#undef SWA_B
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_lo(vr[u][r].w[i]);
-          v[2 * i + 1] = bf16_hi(vr[u][r].w[i]);
-        }
-        if (!all_ok) {
           const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
+          x[u][r] = ok ? d[r] * c : kNegInf;
+          tmax = fmaxf(tmax, x[u][r]);
         }
+      }
+      tmax = xor_max(tmax, 16);
+      tmax = xor_max(tmax, 32);
+      const float mn = fmaxf(m, tmax);
+      // mn == -inf: nothing resident so far for this head; keep everything at 0
+      const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
+      m = mn;
+      float pr[NS][4];
+      float tsum = 0.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float ph = 0.f;
-          switch (h) {
-#define SWA_B(H) case H: ph = row_bcast<H>(pr[u][r]); break;
-            SWA_B(0) SWA_B(1) SWA_B(2) SWA_B(3) SWA_B(4) SWA_B(5) SWA_B(6) SWA_B(7)
-            SWA_B(8) SWA_B(9) SWA_B(10) SWA_B(11) SWA_B(12) SWA_B(13) SWA_B(14) SWA_B(15)
-#undef SWA_B
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[u][r] = x[u][r] == kNegInf ? 0.f : exp2f(x[u][r] - mn);
+          tsum += pr[u][r];
+        }
+      lsum = lsum * alpha + tsum;
+
+      // P * V
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float a = row_bcast_dyn(alpha, h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+      }
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(vr[u][r].w[i]);
+            v[2 * i + 1] = bf16_hi(vr[u][r].w[i]);
+          }
+          if (!all_ok) {
+            const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+          for (int h = 0; h < G; ++h) {
+            const float ph = row_bcast_dyn(pr[u][r], h);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+          }
         }
-      }
+    }
+    __syncthreads();  // the next chunk restages the block ids
   }
 
   // Wave totals: sum the four row groups.
@@ -375,10 +401,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
       acc[h][e] += __shfl_xor(acc[h][e], 16);
       acc[h][e] += __shfl_xor(acc[h][e], 32);
     }
+  float(*s_acc)[G][kD] = reinterpret_cast<float(*)[G][kD]>(sm.raw);
   __syncthreads();  // every wave is done with its K staging area (aliases s_acc)
   if (lane < G) {
-    s_m[wave][lane] = m;
-    s_l[wave][lane] = lsum;
+    sm.m[wave][lane] = m;
+    sm.l[wave][lane] = lsum;
   }
   if (lq == 0) {
 #pragma unroll
@@ -389,21 +416,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
   __syncthreads();
 
   // Workgroup merge: thread -> (head, dim) pairs.
-  const bool direct = nsb == 1;  // the whole sequence in this workgroup: write the output
-  float* ws_o = p.ws_o + (head0 * ns + static_cast<size_t>(split)) * kD;  // head h: + h * ns * kD
-  float* ws_lse = p.ws_lse + head0 * ns + split;                          // head h: + h * ns
   for (int i = threadIdx.x; i < G * kD; i += NW * 64) {
     const int h = i / kD;
     const int d = i - h * kD;
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm.m[w][h]);
     float lt = 0.f, o = 0.f;
     if (mx != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float sc = s_m[w][h] == kNegInf ? 0.f : exp2f(s_m[w][h] - mx);
-        lt = fmaf(s_l[w][h], sc, lt);
+        const float sc = sm.m[w][h] == kNegInf ? 0.f : exp2f(sm.m[w][h] - mx);
+        lt = fmaf(sm.l[w][h], sc, lt);
         o = fmaf(s_acc[w][h][d], sc, o);
       }
     }
@@ -417,69 +441,226 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams p) {
         static_cast<float*>(p.out)[idx] = val;
       if (p.lse != nullptr && d == 0) p.lse[head0 + h] = lse2 * kLn2;
     } else {
-      ws_o[static_cast<size_t>(h) * ns * kD + d] = val;
-      if (d == 0) ws_lse[static_cast<size_t>(h) * ns] = lse2;
+      p.ws_o[(slot * G + h) * kD + d] = val;
+      if (d == 0) p.ws_lse[slot * G + h] = lse2;
     }
   }
+  __syncthreads();  // LDS free for the caller
 }
 
-// Combines the splits of one (sequence, query head) when its sequence was cut
-// into several workgroups (a separate launch, so the partials written by the
-// split kernel are visible without any cross-workgroup fence):
+// Ring caches: grid of (b, kv head, split), one piece per workgroup; partial
+// slot (b * Hkv + kv head) * num_splits + split.
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
+  __shared__ Smem<G, NW> sm;
+  const int ns = p.num_splits;
+  const int split = blockIdx.x % ns;
+  const int unit = blockIdx.x / ns;
+  const int b = unit / p.num_kv_heads;
+  const int kvh = unit - b * p.num_kv_heads;
+  const int ntok = p.slots;
+  const int t0 = split * p.split_tokens;
+  const int t1 = min(t0 + p.split_tokens, ntok);
+  attend_piece<G, RingRows, NW>(p, sm, b, kvh, t0, t1, ns == 1,
+                                static_cast<size_t>(unit) * ns + split);
+}
+
+// Balanced schedule of a paged pool.  Row space: sequence b contributes Hkv
+// ranges of L_b = round_up(len_b, 64) rows (one per kv head, heads laid end
+// to end), sequences in order; total T = Hkv * sum_b L_b.  Workgroup w of W
+// owns rows [g(w), g(w+1)) with g(w) = floor(w T / W) rounded down to a
+// multiple of 64.  The piece of unit u = b * Hkv + h inside workgroup w uses
+// partial slot u + w (pieces in row order move u or w forward by one each, so
+// the slots are distinct and fewer than units + W).
+__device__ __forceinline__ int64_t padded_rows(const DecodeParams& p, int b) {
+  return (static_cast<int64_t>(PoolRows::tokens(p, b)) + 63) / 64 * 64;
+}
+
+__device__ __forceinline__ int64_t pool_total(const DecodeParams& p) {
+  int64_t t = 0;
+  for (int b = 0; b < p.batch; ++b) t += padded_rows(p, b);
+  return t * p.num_kv_heads;
+}
+
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg) {
+  return (w * total / nwg) / 64 * 64;
+}
+
+// The k-th piece of the share [g0, g1): unit (b, h), rows [t0, t1) of it,
+// whether the unit lies wholly inside the share, and the unit index.  Scans
+// the sequences again for every piece (few of them), so that nothing but k
+// stays live across the attention of a piece.
+struct Piece {
+  int b, h, t0, t1;
+  bool direct;
+  int64_t unit;
+};
+
+__device__ bool find_piece(const DecodeParams& p, int64_t g0, int64_t g1, int k, Piece& pc) {
+  int64_t base = 0;
+  int seen = 0;
+  for (int b = 0; b < p.batch && base < g1; ++b) {
+    const int64_t lb = padded_rows(p, b);
+    const int64_t span = lb * p.num_kv_heads;
+    if (lb > 0 && base + span > g0) {
+      for (int h = 0; h < p.num_kv_heads; ++h) {
+        const int64_t u0 = base + h * lb;
+        const int64_t u1 = u0 + lb;
+        if (u1 <= g0) continue;
+        if (u0 >= g1) break;
+        if (seen++ < k) continue;
+        const int len = PoolRows::tokens(p, b);
+        const int64_t end = (g1 < u1 ? g1 : u1) - u0;
+        pc.b = b;
+        pc.h = h;
+        pc.t0 = static_cast<int>((g0 > u0 ? g0 : u0) - u0);
+        pc.t1 = static_cast<int>(end < len ? end : static_cast<int64_t>(len));
+        if (pc.t1 < pc.t0) pc.t1 = pc.t0;
+        pc.direct = g0 <= u0 && u1 <= g1;
+        pc.unit = static_cast<int64_t>(b) * p.num_kv_heads + h;
+        return true;
+      }
+    }
+    base += span;
+  }
+  return false;
+}
+
+// 8 / NW workgroups per CU (two 4-wave or one 8-wave): two waves per SIMD, at
+// most 256 registers per lane.
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
+  __shared__ Smem<G, NW> sm;
+  const int64_t nwg = gridDim.x;
+  const int64_t w = blockIdx.x;
+  const int64_t total = pool_total(p);
+  const int64_t g0 = share_start(w, total, nwg);
+  const int64_t g1 = w + 1 == nwg ? total : share_start(w + 1, total, nwg);
+  Piece pc;
+  for (int k = 0; g0 < g1 && find_piece(p, g0, g1, k, pc); ++k)
+    attend_piece<G, PoolRows, NW>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct,
+                                  static_cast<size_t>(pc.unit + w));
+}
+
+// Combines the partials of one (sequence, query head) spread over several
+// workgroups (a separate launch, so the partials written by the attention
+// kernel are visible without any cross-workgroup fence):
 //   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
 //   lse = (M + log2 sum_s w_s) ln 2.
-// Sequences that fitted one split wrote their output directly and are
-// skipped.  256 threads = 8 split groups x 32 float4 columns, so every
-// partial row is read by independent loads in flight together.  Splits with
-// lse = -inf hold no row: weight 0, their partial is never read.
-__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p, int ragged) {
+// The partials of a (sequence, kv head) sit in consecutive slots: ring
+// splits at (b * Hkv + kv head) * num_splits + split; pool pieces at
+// u + w for the workgroups w whose share meets the unit (workgroups with an
+// empty share own no piece and are skipped).  A unit done by one workgroup
+// wrote its output directly and is skipped; a pool sequence of length 0 gets
+// out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
+// the partial rows are read by independent loads in flight together, and
+// slots with lse = -inf are dropped with selects.
+template <int PER>  // partial rows per thread held in registers
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
   __shared__ float s_lse[kMaxSplits];
   __shared__ float4 s_part[GROUPS][COLS];
   const size_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / p.num_q_heads);
-  const int ns = p.num_splits;
-  int nsb = ns;
-  if (ragged) {
-    const int ntok = PoolRows::tokens(p, b);
-    nsb = ntok > 0 ? (ntok + p.split_tokens - 1) / p.split_tokens : 1;
-  }
-  if (nsb <= 1) return;
-  const float* lse = p.ws_lse + bh * ns;
-  for (int s = threadIdx.x; s < nsb; s += 256) s_lse[s] = lse[s];
-  __syncthreads();
-  float mx = kNegInf;
-  for (int s = 0; s < nsb; ++s) mx = fmaxf(mx, s_lse[s]);
-  float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int hq = static_cast<int>(bh - static_cast<size_t>(b) * p.num_q_heads);
+  const int g = p.num_q_heads / p.num_kv_heads;
+  const int kvh = hq / g;
+  const int h = hq - kvh * g;
+  const int64_t unit = static_cast<int64_t>(b) * p.num_kv_heads + kvh;
   const int col = threadIdx.x % COLS;
   const int grp = threadIdx.x / COLS;
-  if (mx != kNegInf) {
-    for (int s = 0; s < nsb; ++s) wsum += s_lse[s] == kNegInf ? 0.f : exp2f(s_lse[s] - mx);
-    const float4* po = reinterpret_cast<const float4*>(p.ws_o + bh * ns * kD);
-#pragma unroll 4
-    for (int s = grp; s < nsb; s += GROUPS) {
-      const float l = s_lse[s];
-      if (l == kNegInf) continue;
-      const float w = exp2f(l - mx);
-      const float4 v = po[static_cast<size_t>(s) * COLS + col];
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+
+  int64_t first;  // slot of the first partial
+  int count;      // partials (consecutive slots)
+  int64_t w0 = 0, nwg = 1, total = 0;
+  if (!pool) {
+    first = unit * p.num_splits;
+    count = p.num_splits;
+  } else {
+    nwg = p.num_splits;
+    total = pool_total(p);
+    int64_t base = 0;
+    for (int bb = 0; bb < b; ++bb) base += padded_rows(p, bb) * p.num_kv_heads;
+    const int64_t lb = padded_rows(p, b);
+    if (lb == 0) {
+      count = 0;
+      first = 0;
+    } else {
+      const int64_t u0 = base + kvh * lb, u1 = u0 + lb;
+      auto owner = [&](int64_t x) {  // workgroup whose share holds row x
+        int64_t wq = x * nwg / total;
+        while (wq > 0 && share_start(wq, total, nwg) > x) --wq;
+        while (wq + 1 < nwg && share_start(wq + 1, total, nwg) <= x) ++wq;
+        return wq;
+      };
+      w0 = owner(u0);
+      const int64_t w1 = owner(u1 - 1);
+      count = static_cast<int>(w1 - w0 + 1);
+      first = unit + w0;
     }
+  }
+  if (count == 1) return;  // written directly by the attention kernel
+  auto present = [&](int k) {  // pool: the k-th workgroup of the run owns rows
+    if (!pool) return true;
+    const int64_t wk = w0 + k;
+    const int64_t a = share_start(wk, total, nwg);
+    const int64_t e = wk + 1 == nwg ? total : share_start(wk + 1, total, nwg);
+    return a < e;
+  };
+  const float* lse = p.ws_lse;
+  const float4* po = reinterpret_cast<const float4*>(p.ws_o);
+  const size_t stride = static_cast<size_t>(g) * COLS;  // float4s between consecutive slots
+  const size_t at0 = (static_cast<size_t>(first) * g + h) * COLS + col;
+  float4 v[PER];
+  float lv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int s = grp + GROUPS * k;
+    lv[k] = kNegInf;
+    if (s < count && present(s)) {
+      v[k] = po[at0 + s * stride];
+      lv[k] = lse[(static_cast<size_t>(first) + s) * g + h];
+    }
+  }
+  for (int s = threadIdx.x; s < count; s += 256)
+    s_lse[s] = present(s) ? lse[(static_cast<size_t>(first) + s) * g + h] : kNegInf;
+  __syncthreads();
+  float mx = kNegInf;
+  for (int s = 0; s < count; ++s) mx = fmaxf(mx, s_lse[s]);
+  float wsum = 0.f;
+  if (mx != kNegInf)
+    for (int s = 0; s < count; ++s) wsum += s_lse[s] == kNegInf ? 0.f : exp2f(s_lse[s] - mx);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const bool use = lv[k] != kNegInf && mx != kNegInf;
+    const float w = use ? exp2f(lv[k] - mx) : 0.f;
+    acc.x += use ? w * v[k].x : 0.f;
+    acc.y += use ? w * v[k].y : 0.f;
+    acc.z += use ? w * v[k].z : 0.f;
+    acc.w += use ? w * v[k].w : 0.f;
+  }
+  for (int s = grp + GROUPS * PER; s < count; s += GROUPS) {  // beyond the registers
+    const float l = s_lse[s];
+    if (l == kNegInf || mx == kNegInf) continue;
+    const float w = exp2f(l - mx);
+    const float4 t = po[at0 + s * stride];
+    acc.x = fmaf(w, t.x, acc.x);
+    acc.y = fmaf(w, t.y, acc.y);
+    acc.z = fmaf(w, t.z, acc.z);
+    acc.w = fmaf(w, t.w, acc.w);
   }
   s_part[grp][col] = acc;
   __syncthreads();
   if (threadIdx.x < COLS) {
     float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-      t.x += s_part[g][col].x;
-      t.y += s_part[g][col].y;
-      t.z += s_part[g][col].z;
-      t.w += s_part[g][col].w;
+    for (int gg = 0; gg < GROUPS; ++gg) {
+      t.x += s_part[gg][col].x;
+      t.y += s_part[gg][col].y;
+      t.z += s_part[gg][col].z;
+      t.w += s_part[gg][col].w;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const float vals[4] = {t.x * inv, t.y * inv, t.z * inv, t.w * inv};
@@ -495,45 +676,47 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p, int r
   }
 }
 
-template <class Rows, int NW>
-hipError_t launch_rows(const DecodeParams& p, int ragged, hipStream_t stream) {
-  const unsigned grid =
-      static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
-  switch (p.num_q_heads / p.num_kv_heads) {
-#define SWA_CASE(G)                                                             \
-  case G:                                                                       \
-    decode_mfma_kernel<G, Rows, NW><<<grid, NW * 64, 0, stream>>>(p);           \
-    break;
-    SWA_CASE(1)
-    SWA_CASE(2)
-    SWA_CASE(3)
-    SWA_CASE(4)
-    SWA_CASE(6)
-    SWA_CASE(8)
-#undef SWA_CASE
-    default:
-      return hipErrorInvalidValue;
+#define SWA_KERNEL_TABLE(NAME)                                                            \
+  template <int NW>                                                                       \
+  hipError_t NAME##_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {    \
+    switch (p.num_q_heads / p.num_kv_heads) {                                             \
+      case 1: NAME<1, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      case 2: NAME<2, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      case 3: NAME<3, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      case 4: NAME<4, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      case 6: NAME<6, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      case 8: NAME<8, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
+      default: return hipErrorInvalidValue;                                               \
+    }                                                                                     \
+    return hipGetLastError();                                                             \
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.num_splits == 1) return err;
-  const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  merge_splits_kernel<<<heads, 256, 0, stream>>>(p, ragged);
-  return hipGetLastError();
-}
+SWA_KERNEL_TABLE(decode_ring_kernel)
+SWA_KERNEL_TABLE(decode_pool_kernel)
+#undef SWA_KERNEL_TABLE
 
 }  // namespace
 
 hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
-  return launch_rows<RingRows, kRingWaves>(p, 0, stream);
+  const unsigned grid =
+      static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
+  hipError_t err = decode_ring_kernel_launch<kRingWaves>(p, grid, stream);
+  if (err != hipSuccess || p.num_splits == 1) return err;
+  const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
+  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream) {
-  // Many workgroups (ragged or long pools): 4-wave workgroups, two per CU, so
-  // one workgroup's start and end overlap the other's streaming.  Few
-  // workgroups: 8 waves each, to keep enough waves per CU.
-  const int64_t wgs = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
-  if (wgs >= kPoolManyWorkgroups) return launch_rows<PoolRows, 4>(p, 1, stream);
-  return launch_rows<PoolRows, 8>(p, 1, stream);
+  // p.num_splits carries the size of the balanced grid: kPoolGrid 4-wave
+  // workgroups, or half as many 8-wave ones for small pools
+  const unsigned grid = static_cast<unsigned>(p.num_splits);
+  hipError_t err = grid == static_cast<unsigned>(kPoolGrid)
+                       ? decode_pool_kernel_launch<4>(p, grid, stream)
+                       : decode_pool_kernel_launch<8>(p, grid, stream);
+  if (err != hipSuccess) return err;
+  const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
+  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 1);
+  return hipGetLastError();
 }
 
 }  // namespace swa

@@ -113,11 +113,19 @@ void fill_workspace_ptrs(swa::DecodeParams& p, void* workspace,
   p.ws_lse = reinterpret_cast<float*>(base + lay.lse_offset);
 }
 
+// Split grid of a decode call.  The paged bf16 / head_dim 128 path runs a
+// fixed balanced grid instead; num_splits then carries its size.
 swa::SplitPlan plan_for(int bf16, int32_t head_dim, int32_t batch, int32_t num_kv_heads,
-                        int32_t max_tokens, bool ragged) {
-  return swa::use_mfma_path(bf16, head_dim)
-             ? swa::plan_splits_mfma(batch, num_kv_heads, max_tokens, ragged)
-             : swa::plan_splits(batch, num_kv_heads, max_tokens);
+                        int32_t max_tokens, bool paged) {
+  if (!swa::use_mfma_path(bf16, head_dim)) return swa::plan_splits(batch, num_kv_heads, max_tokens);
+  if (!paged) return swa::plan_splits_mfma(batch, num_kv_heads, max_tokens);
+  // rows of the pool at most (every sequence at its capacity)
+  const int64_t rows = static_cast<int64_t>(batch) * num_kv_heads * max_tokens;
+  swa::SplitPlan plan;
+  plan.split_tokens = 0;
+  plan.num_splits = rows / swa::kPoolGrid < swa::kPoolSmallRows ? swa::kPoolGrid / 2
+                                                                : swa::kPoolGrid;
+  return plan;
 }
 
 int log2_exact(int32_t x) {

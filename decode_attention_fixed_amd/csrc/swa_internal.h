@@ -10,22 +10,19 @@
 namespace swa {
 
 constexpr int kMaxGroup = 8;
-// Tuning of the bf16 / head_dim 128 decode kernel: waves per workgroup for
-// ring caches, the workgroup count from which paged pools use 4-wave
-// workgroups, and the longest split of a ragged (paged) sequence.
+// Shapes of the bf16 / head_dim 128 decode kernel.  Ring caches: 8-wave
+// workgroups (one per CU, whole sequences).  Paged pools: a fixed balanced
+// grid of kPoolGrid 4-wave workgroups (two per CU), or kPoolGrid / 2 8-wave
+// workgroups when the pool holds fewer than kPoolSmallRows rows per
+// 4-wave workgroup (the per-workgroup start and the merge of many small
+// shares would dominate).
 #ifndef SWA_RING_WAVES
 #define SWA_RING_WAVES 8
 #endif
-#ifndef SWA_POOL_MANY_WGS
-#define SWA_POOL_MANY_WGS 1024
-#endif
-#ifndef SWA_RAGGED_SPLIT
-#define SWA_RAGGED_SPLIT 2048
-#endif
 constexpr int kRingWaves = SWA_RING_WAVES;
-constexpr int64_t kPoolManyWorkgroups = SWA_POOL_MANY_WGS;
-constexpr int kRaggedSplit = SWA_RAGGED_SPLIT;
-constexpr int kMaxMfmaSplits = 512;         // splits per sequence on that path
+constexpr int kPoolGrid = 512;
+constexpr int64_t kPoolSmallRows = 2048;
+constexpr int kMaxMfmaSplits = 512;             // ring splits per sequence on that path
 constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path
 
 struct AppendParams {
@@ -91,11 +88,12 @@ struct SplitPlan {
 // generic path runs one wave per split and a separate merge kernel.
 bool use_mfma_path(int bf16, int32_t head_dim);
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens);
-SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens,
-                           bool ragged);
+SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens);
 
 // Workspace layout: [partial outputs | partial lse], each region 256-byte
-// aligned.  Sized for whichever path needs more.
+// aligned, in partial slots of g = Hq/Hkv heads: enough slots for whichever
+// path needs most (B*Hkv*splits for split grids, B*Hkv + kPoolGrid for the
+// balanced pool grid).
 struct WorkspaceLayout {
   size_t o_offset;
   size_t lse_offset;
