@@ -13,13 +13,15 @@ Prints one JSON line:
                    (resident rows x Hkv x d x 2 x element bytes, summed over
                    the batch) x steps / time of the timed steps (HIP events
                    at the two ends of the region only).
-  roofline         for the dominant kernel (the decode kernel): algorithmic
-                   bytes per launch / its mean launch duration, from HIP events
-                   recorded on the launch stream around every decode call in a
-                   second timed region of the same steps, against the 8 TB/s
-                   HBM peak; `traffic` is the measured HBM bytes per launch
-                   from rocprofv3 counters (profiles/) when they were taken on
-                   the current kernel sources, else null.
+  roofline         for the dominant kernel (the decode attention kernel, with
+                   the small split-merge launch that follows it in the same
+                   call when there is one): algorithmic bytes per call / mean
+                   call duration, from HIP events recorded on the launch
+                   stream around every decode call in a second timed region
+                   of the same steps, against the 8 TB/s HBM peak; `traffic`
+                   is the measured HBM bytes per call from rocprofv3 counters
+                   (profiles/decode_<workload>_traffic.txt) when they were
+                   taken on the current kernel sources, else null.
   cpu_baseline     the float64 NumPy oracle on a bounded sample of the same
                    workload (inputs already in host memory), host cores.
 
@@ -41,7 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRCS = [os.path.join(ROOT, "decode_attention_fixed_amd", "csrc", f)
                for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
 
@@ -82,12 +84,14 @@ def kv_bytes_per_step(w) -> int:
     return resident_tokens(w) * w.kv_bytes_per_token()
 
 
-def traffic_record():
-    """Counter-measured HBM bytes per decode launch, if taken on this source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_record(name: str):
+    """Counter-measured HBM bytes per decode call of workload `name`, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(PROFILES, f"decode_{name}_traffic.txt")
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
@@ -308,13 +312,15 @@ def main() -> int:
     ms_per_step = res["total_ms"] / args.steps
     value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9
     achieved = kv_bytes / (res["decode_ms_mean"] / 1e3) / 1e9
-    traffic = traffic_record()
+    traffic = traffic_record(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": (int(float(traffic["fetch_bytes_per_launch"])
-                                + float(traffic["write_bytes_per_launch"]))
-                            if traffic and traffic.get("workload") == w.name else None),
-                "kernel": "decode kernel (one launch per decode call)",
+                "traffic": (int(float(traffic["fetch_bytes_per_call"])
+                                + float(traffic["write_bytes_per_call"]))
+                            if traffic else None),
+                "kernel": ("decode call: the attention kernel, plus the split merge "
+                           "launch when a head's rows are spread over several workgroups; "
+                           "both on the launch stream, timed together"),
                 "algorithmic_bytes": kv_bytes}
     out = {
         "metric": "decode-attention KV-read GB/s", "value": round(value_gbs, 1), "unit": "GB/s",

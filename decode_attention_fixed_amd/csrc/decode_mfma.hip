@@ -124,6 +124,8 @@ constexpr int kMaxSplits = 512;  // ring splits per sequence (the plan never exc
 // Ring: rows of head (b, h) are contiguous, slot t at row t; a row is
 // resident iff its slot holds a position.
 struct RingRows {
+  // a subtile may run past the last slot: rows beyond the range are clamped
+  static constexpr bool kWholeSubtiles = false;
   const int32_t* slot_pos;
   size_t head_base;  // element offset of slot 0 of head (b, h)
   __device__ RingRows(const DecodeParams& p, int b, int h)
@@ -146,6 +148,9 @@ struct RingRows {
 // invalid, negative or past the pool), so the row loop never waits on a
 // dependent table load.
 struct PoolRows {
+  // a subtile lies inside one block, which is allocated whole: rows past the
+  // range are read (and masked) without clamping
+  static constexpr bool kWholeSubtiles = true;
   const int32_t* table;
   const uint8_t* valid;
   int h;
@@ -170,7 +175,10 @@ struct PoolRows {
   }
   __device__ bool subtile(const DecodeParams& p, const int32_t* s_blk, int t0, int t,
                           size_t& base) const {
-    const int blk = s_blk[(t >> p.block_shift) - (t0 >> p.block_shift)];
+    // the same entry for every lane: keep the block id (and the row
+    // address built from it) in scalar registers
+    const int blk =
+        __builtin_amdgcn_readfirstlane(s_blk[(t >> p.block_shift) - (t0 >> p.block_shift)]);
     const int r = t & ((1 << p.block_shift) - 1);
     base = ((static_cast<size_t>(blk < 0 ? 0 : blk) * p.num_kv_heads + h) << p.block_shift) * kD +
            static_cast<size_t>(r) * kD;
@@ -268,11 +276,12 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
           const int tk = tu + lc;
           const bool okk = tk < c1 && rows.row_ok(tk);
           vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
+          const uint16_t* ks = kb + base[u];  // uniform: scalar base register
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rho = 4 * i + lq;
-            const size_t koff = base[u] + static_cast<size_t>(tu + rho < c1 ? rho : 0) * kD;
-            kr[u][i] = load16_stream(kb + koff + 8 * lc);
+            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
+            kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 8 * lc));
           }
         } else {
 #pragma unroll
@@ -283,11 +292,12 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
       for (int u = 0; u < NS; ++u) {
         const int tu = ts + 16 * u;
         if (live[u]) {
+          const uint16_t* vs = vb + base[u];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * lq + r;
-            const size_t voff = base[u] + static_cast<size_t>(tu + i < c1 ? i : 0) * kD;
-            vr[u][r] = load16_stream(vb + voff + 8 * lc);
+            const int row = Rows::kWholeSubtiles || tu + i < c1 ? i : 0;
+            vr[u][r] = load16_stream(vs + static_cast<uint32_t>(row * kD + 8 * lc));
           }
         } else {
 #pragma unroll
@@ -465,81 +475,233 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
                                 static_cast<size_t>(unit) * ns + split);
 }
 
-// Balanced schedule of a paged pool.  Row space: sequence b contributes Hkv
-// ranges of L_b = round_up(len_b, 64) rows (one per kv head, heads laid end
-// to end), sequences in order; total T = Hkv * sum_b L_b.  Workgroup w of W
-// owns rows [g(w), g(w+1)) with g(w) = floor(w T / W) rounded down to a
-// multiple of 64.  The piece of unit u = b * Hkv + h inside workgroup w uses
-// partial slot u + w (pieces in row order move u or w forward by one each, so
-// the slots are distinct and fewer than units + W).
-__device__ __forceinline__ int64_t padded_rows(const DecodeParams& p, int b) {
-  return (static_cast<int64_t>(PoolRows::tokens(p, b)) + 63) / 64 * 64;
+// Balanced schedule of a paged pool, in granules of 64 rows.  Sequence b
+// contributes Hkv ranges of n_b = ceil(len_b / 64) granules (one per kv head,
+// heads laid end to end), sequences in order; the total is
+// T = Hkv * sum_b n_b.  Workgroup w of W (a power of two) owns granules
+// [s(w), s(w+1)) with s(w) = floor(w T / W).  The piece of unit
+// u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
+// granule order move u or w forward by one each, so the slots are distinct
+// and fewer than units + W).
+__device__ __forceinline__ int granules(const DecodeParams& p, int b) {
+  return (PoolRows::tokens(p, b) + 63) >> 6;
 }
 
-__device__ __forceinline__ int64_t pool_total(const DecodeParams& p) {
-  int64_t t = 0;
-  for (int b = 0; b < p.batch; ++b) t += padded_rows(p, b);
-  return t * p.num_kv_heads;
-}
-
+// W is a power of two (the host launches kPoolGrid or kPoolGrid / 2): the
+// share boundaries need no 64-bit division.
 __device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg) {
-  return (w * total / nwg) / 64 * 64;
+  const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg));
+  return (w * total) >> shift;
 }
 
-// The k-th piece of the share [g0, g1): unit (b, h), rows [t0, t1) of it,
-// whether the unit lies wholly inside the share, and the unit index.  Scans
-// the sequences again for every piece (few of them), so that nothing but k
-// stays live across the attention of a piece.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Sums over the workgroup (NT threads) of one or two values, the same
+// result returned to every thread.  s_red holds 2 * NT / 64 entries.
+template <int NT>
+__device__ int64_t block_sum(int64_t x, int64_t* s_red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += s_red[w];
+  __syncthreads();  // s_red free again
+  return uniform64(t);
+}
+
+template <int NT>
+__device__ void block_sum2(int64_t& x, int64_t& y, int64_t* s_red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    x += __shfl_xor(x, off);
+    y += __shfl_xor(y, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_red[threadIdx.x >> 6] = x;
+    s_red[NT / 64 + (threadIdx.x >> 6)] = y;
+  }
+  __syncthreads();
+  int64_t tx = 0, ty = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    tx += s_red[w];
+    ty += s_red[NT / 64 + w];
+  }
+  __syncthreads();  // s_red free again
+  x = uniform64(tx);
+  y = uniform64(ty);
+}
+
+// Lengths (rows, clamped to the table) of NT consecutive sequences
+// [first, first + NT), the exclusive prefix sums of their granule counts, and
+// the state of a workgroup's walk over the units of its share (kept here, not
+// in registers, while a piece is attended).
+template <int NT>
+struct SeqChunk {
+  int32_t len[NT];
+  int32_t excl[NT];
+  int64_t red[2 * NT / 64];
+  int32_t wsum[NT / 64];
+  int64_t g0, g1;  // the workgroup's share of granules
+  int64_t base;    // granules per kv head of the sequences before the chunk
+  int32_t first, csum, i, h;  // chunk start and total; next sequence and kv head
+};
+
+// Loads the chunk of sequences starting at `first` into LDS; returns its total
+// granule count (per kv head).  Called by every thread.
+template <int NT>
+__device__ int32_t load_chunk(const DecodeParams& p, SeqChunk<NT>& sc, int first) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = first + static_cast<int>(threadIdx.x);
+  const int len = b < p.batch ? PoolRows::tokens(p, b) : 0;
+  const int x = (len + 63) >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sc.wsum[wave] = incl;
+  __syncthreads();  // also: the previous chunk's entries are no longer read
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int v = sc.wsum[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  sc.len[threadIdx.x] = len;
+  sc.excl[threadIdx.x] = before + incl - x;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// A piece: rows [t0, t1) of unit (b, h), whether the unit lies wholly inside
+// the share (its output is then final), and its partial slot.
 struct Piece {
   int b, h, t0, t1;
   bool direct;
-  int64_t unit;
+  size_t slot;
 };
 
-__device__ bool find_piece(const DecodeParams& p, int64_t g0, int64_t g1, int k, Piece& pc) {
-  int64_t base = 0;
-  int seen = 0;
-  for (int b = 0; b < p.batch && base < g1; ++b) {
-    const int64_t lb = padded_rows(p, b);
-    const int64_t span = lb * p.num_kv_heads;
-    if (lb > 0 && base + span > g0) {
-      for (int h = 0; h < p.num_kv_heads; ++h) {
-        const int64_t u0 = base + h * lb;
-        const int64_t u1 = u0 + lb;
-        if (u1 <= g0) continue;
-        if (u0 >= g1) break;
-        if (seen++ < k) continue;
-        const int len = PoolRows::tokens(p, b);
-        const int64_t end = (g1 < u1 ? g1 : u1) - u0;
-        pc.b = b;
-        pc.h = h;
-        pc.t0 = static_cast<int>((g0 > u0 ? g0 : u0) - u0);
-        pc.t1 = static_cast<int>(end < len ? end : static_cast<int64_t>(len));
-        if (pc.t1 < pc.t0) pc.t1 = pc.t0;
-        pc.direct = g0 <= u0 && u1 <= g1;
-        pc.unit = static_cast<int64_t>(b) * p.num_kv_heads + h;
-        return true;
-      }
+// Moves the walk on to the next piece of the workgroup's share; false when
+// the share holds no further piece.  Called by every thread.  Everything it
+// needs between pieces lives in LDS, so no register is held across a piece.
+template <int NT>
+__device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
+  const int64_t hkv = p.num_kv_heads;
+  const int64_t g0 = uniform64(sc.g0);
+  const int64_t g1 = uniform64(sc.g1);
+  int64_t base = uniform64(sc.base);
+  int first = __builtin_amdgcn_readfirstlane(sc.first);
+  int csum = __builtin_amdgcn_readfirstlane(sc.csum);
+  int i = __builtin_amdgcn_readfirstlane(sc.i);
+  int h = __builtin_amdgcn_readfirstlane(sc.h);
+  bool found = false;
+  for (;;) {
+    if (i == NT) {  // on into the next chunk
+      if (first + NT >= p.batch) break;
+      base += csum;
+      first += NT;
+      csum = load_chunk<NT>(p, sc, first);
+      i = 0;
+      h = 0;
     }
-    base += span;
+    const int b = first + i;
+    if (b >= p.batch) break;
+    const int len = __builtin_amdgcn_readfirstlane(sc.len[i]);
+    const int64_t n = (len + 63) >> 6;
+    const int64_t start = (base + __builtin_amdgcn_readfirstlane(sc.excl[i])) * hkv;
+    if (start >= g1) break;
+    if (n == 0 || h >= hkv) {
+      ++i;
+      h = 0;
+      continue;
+    }
+    const int64_t u0 = start + h * n;
+    const int64_t u1 = u0 + n;
+    if (u0 >= g1) break;
+    if (u1 > g0) {
+      const int64_t e = ((g1 < u1 ? g1 : u1) - u0) * 64;
+      pc.b = b;
+      pc.h = h;
+      pc.t0 = static_cast<int>(((g0 > u0 ? g0 : u0) - u0) * 64);
+      pc.t1 = static_cast<int>(e < len ? e : static_cast<int64_t>(len));
+      if (pc.t1 < pc.t0) pc.t1 = pc.t0;
+      pc.direct = g0 <= u0 && u1 <= g1;
+      pc.slot = static_cast<size_t>(static_cast<int64_t>(b) * hkv + h + blockIdx.x);
+      found = true;
+    }
+    ++h;
+    if (found) break;
   }
-  return false;
+  __syncthreads();  // every thread has read the walk state
+  if (threadIdx.x == 0) {
+    sc.base = base;
+    sc.first = first;
+    sc.csum = csum;
+    sc.i = i;
+    sc.h = h;
+  }
+  __syncthreads();
+  return found;
 }
 
 // 8 / NW workgroups per CU (two 4-wave or one 8-wave): two waves per SIMD, at
 // most 256 registers per lane.
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
+  constexpr int NT = NW * 64;
   __shared__ Smem<G, NW> sm;
+  __shared__ SeqChunk<NT> sc;
+  const int64_t hkv = p.num_kv_heads;
   const int64_t nwg = gridDim.x;
   const int64_t w = blockIdx.x;
-  const int64_t total = pool_total(p);
+
+  // Total granules: the first chunk's sum, plus a strided sum over the
+  // sequences past it when the batch is larger than the workgroup.
+  int32_t csum = load_chunk<NT>(p, sc, 0);
+  int64_t rest = 0;
+  for (int b = NT + threadIdx.x; b < p.batch; b += NT) rest += granules(p, b);
+  if (p.batch > NT) rest = block_sum<NT>(rest, sc.red);
+  const int64_t total = (csum + rest) * hkv;
   const int64_t g0 = share_start(w, total, nwg);
   const int64_t g1 = w + 1 == nwg ? total : share_start(w + 1, total, nwg);
+  if (g0 >= g1) return;
+
+  // Chunk holding the first sequence that ends past g0, and that sequence.
+  int first = 0;
+  int64_t base = 0;
+  while ((base + csum) * hkv <= g0) {
+    base += csum;
+    first += NT;
+    csum = load_chunk<NT>(p, sc, first);
+  }
+  // sequences of the chunk that end at or before g0 (the ends are sorted)
+  const int i = __builtin_amdgcn_readfirstlane(
+      __syncthreads_count((base + sc.excl[threadIdx.x] + ((sc.len[threadIdx.x] + 63) >> 6)) *
+                              hkv <= g0));
+  if (threadIdx.x == 0) {
+    sc.g0 = g0;
+    sc.g1 = g1;
+    sc.base = base;
+    sc.first = first;
+    sc.csum = csum;
+    sc.i = i;
+    sc.h = 0;
+  }
+  __syncthreads();
   Piece pc;
-  for (int k = 0; g0 < g1 && find_piece(p, g0, g1, k, pc); ++k)
-    attend_piece<G, PoolRows, NW>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct,
-                                  static_cast<size_t>(pc.unit + w));
+  while (next_piece<NT>(p, sc, pc))
+    attend_piece<G, PoolRows, NW>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct, pc.slot);
 }
 
 // Combines the partials of one (sequence, query head) spread over several
@@ -549,17 +711,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
 //   lse = (M + log2 sum_s w_s) ln 2.
 // The partials of a (sequence, kv head) sit in consecutive slots: ring
 // splits at (b * Hkv + kv head) * num_splits + split; pool pieces at
-// u + w for the workgroups w whose share meets the unit (workgroups with an
-// empty share own no piece and are skipped).  A unit done by one workgroup
-// wrote its output directly and is skipped; a pool sequence of length 0 gets
-// out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
+// u + w for the workgroups w whose share of granules meets the unit
+// (workgroups with an empty share own no piece and are skipped).  A unit
+// done by one workgroup wrote its output directly and is skipped; a pool
+// sequence of length 0 gets out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
 // the partial rows are read by independent loads in flight together, and
 // slots with lse = -inf are dropped with selects.
 template <int PER>  // partial rows per thread held in registers
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
+  static_assert(kMaxSplits <= 512, "two slots per thread");
   __shared__ float s_lse[kMaxSplits];
+  __shared__ float s_red_f[8];
   __shared__ float4 s_part[GROUPS][COLS];
   const size_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / p.num_q_heads);
@@ -578,18 +742,29 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
     first = unit * p.num_splits;
     count = p.num_splits;
   } else {
+    // granules of all sequences and of those before b, summed by the
+    // whole workgroup
+    __shared__ int64_t s_red[8];
+    const int64_t hkv = p.num_kv_heads;
     nwg = p.num_splits;
-    total = pool_total(p);
-    int64_t base = 0;
-    for (int bb = 0; bb < b; ++bb) base += padded_rows(p, bb) * p.num_kv_heads;
-    const int64_t lb = padded_rows(p, b);
-    if (lb == 0) {
+    const int64_t n = granules(p, b);
+    int64_t all = 0, pb = 0;
+    for (int bb = threadIdx.x; bb < p.batch; bb += 256) {
+      const int x = granules(p, bb);
+      all += x;
+      pb += bb < b ? x : 0;
+    }
+    block_sum2<256>(all, pb, s_red);
+    total = all * hkv;
+    if (n == 0) {
       count = 0;
       first = 0;
     } else {
-      const int64_t u0 = base + kvh * lb, u1 = u0 + lb;
-      auto owner = [&](int64_t x) {  // workgroup whose share holds row x
-        int64_t wq = x * nwg / total;
+      const int64_t u0 = pb * hkv + kvh * n, u1 = u0 + n;
+      auto owner = [&](int64_t x) {  // workgroup whose share holds granule x
+        int64_t wq = static_cast<int64_t>(static_cast<double>(x) * static_cast<double>(nwg) /
+                                          static_cast<double>(total));
+        wq = wq < 0 ? 0 : (wq >= nwg ? nwg - 1 : wq);
         while (wq > 0 && share_start(wq, total, nwg) > x) --wq;
         while (wq + 1 < nwg && share_start(wq + 1, total, nwg) <= x) ++wq;
         return wq;
@@ -623,14 +798,28 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
       lv[k] = lse[(static_cast<size_t>(first) + s) * g + h];
     }
   }
-  for (int s = threadIdx.x; s < count; s += 256)
-    s_lse[s] = present(s) ? lse[(static_cast<size_t>(first) + s) * g + h] : kNegInf;
+  // Every slot's lse (thread t holds slots t and t + 256; count <= 512),
+  // then the maximum and the weight sum by block reductions.
+  float la = kNegInf, lb = kNegInf;
+  const int sa = threadIdx.x, sb = threadIdx.x + 256;
+  if (sa < count && present(sa)) la = lse[(static_cast<size_t>(first) + sa) * g + h];
+  if (sb < count && present(sb)) lb = lse[(static_cast<size_t>(first) + sb) * g + h];
+  if (sa < count) s_lse[sa] = la;
+  if (sb < count) s_lse[sb] = lb;
+  float mx = fmaxf(la, lb);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0) s_red_f[threadIdx.x >> 6] = mx;
   __syncthreads();
-  float mx = kNegInf;
-  for (int s = 0; s < count; ++s) mx = fmaxf(mx, s_lse[s]);
+  mx = fmaxf(fmaxf(s_red_f[0], s_red_f[1]), fmaxf(s_red_f[2], s_red_f[3]));
   float wsum = 0.f;
   if (mx != kNegInf)
-    for (int s = 0; s < count; ++s) wsum += s_lse[s] == kNegInf ? 0.f : exp2f(s_lse[s] - mx);
+    wsum = (la == kNegInf ? 0.f : exp2f(la - mx)) + (lb == kNegInf ? 0.f : exp2f(lb - mx));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+  if ((threadIdx.x & 63) == 0) s_red_f[4 + (threadIdx.x >> 6)] = wsum;
+  __syncthreads();
+  wsum = (s_red_f[4] + s_red_f[5]) + (s_red_f[6] + s_red_f[7]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < PER; ++k) {

@@ -20,7 +20,8 @@ constexpr int kMaxGroup = 8;
 #define SWA_RING_WAVES 8
 #endif
 constexpr int kRingWaves = SWA_RING_WAVES;
-constexpr int kPoolGrid = 512;
+constexpr int kPoolGrid = 512;  // a power of two, and so is kPoolGrid / 2
+static_assert((kPoolGrid & (kPoolGrid - 1)) == 0, "balanced grid must be a power of two");
 constexpr int64_t kPoolSmallRows = 2048;
 constexpr int kMaxMfmaSplits = 512;             // ring splits per sequence on that path
 constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path

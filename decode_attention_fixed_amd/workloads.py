@@ -130,6 +130,8 @@ class PagedState:
 
     def _write(self, k: np.ndarray, v: np.ndarray, rows: np.ndarray, pos=None) -> None:
         w = self.w
+        if rows.size == 0:
+            return
         kd = to_device(k, w.dtype, self.device)
         vd = to_device(v, w.dtype, self.device)
         rd = torch.from_numpy(rows.astype(np.int32)).to(self.device)
