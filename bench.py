@@ -17,8 +17,9 @@ Prints one JSON line:
                    the small split-merge launch that follows it in the same
                    call when there is one): algorithmic bytes per call / mean
                    call duration, from HIP events recorded on the launch
-                   stream around every decode call in a second timed region
-                   of the same steps, against the 8 TB/s HBM peak; `traffic`
+                   stream at the two ends of a second region of `steps`
+                   decode calls issued back to back, against the 8 TB/s HBM
+                   peak; `traffic`
                    is the measured HBM bytes per call from rocprofv3 counters
                    (profiles/decode_<workload>_traffic.txt) when they were
                    taken on the current kernel sources, else null.
@@ -121,7 +122,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     from synth.draws import draw_rows_parallel
 
     torch.cuda.set_device(0)
-    total = warmup + 2 * steps  # warmup, then two timed regions of `steps` steps
+    total = warmup + steps  # steps with new tokens: warmup, then the timed steps
     t0 = time.time()
     if w.kind == "ring":
         st = RingState(w)
@@ -188,22 +189,20 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     wall = time.perf_counter() - wall0
     total_ms = begin.elapsed_time(end)
 
-    # Region 2: the same steps again, events around every decode call.  The
-    # ring cache keeps advancing (positions continue), so every step still
-    # appends a new token and attends over a full window.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # Region 2: `steps` decode calls back to back on the state the last step
+    # left (no appends in between), events at the two ends: the mean duration
+    # of one decode call as the kernels run in a stream.  Every call reads the
+    # whole resident cache again (larger than the last-level cache, or cycled
+    # through pool copies that together are).
+    last = warmup + steps - 1
     torch.cuda.synchronize()
+    begin.record()
     for s in range(steps):
-        i = warmup + steps + s
-        pre(i)
-        ev[s][0].record()
-        decode(i)
-        ev[s][1].record()
+        decode(last if w.kind == "ring" else warmup + steps + s)
+    end.record()
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    return {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": sum(dec_ms) / len(dec_ms),
-            "decode_ms_min": min(dec_ms)}
+    dec_ms = begin.elapsed_time(end) / steps
+    return {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
 
 
 # ---------------------------------------------------------------------------
@@ -211,8 +210,10 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
-    """Times the float64 oracle on whole sequences of decode step 0; inputs are
-    drawn beforehand (host memory), only the oracle's arithmetic is timed."""
+    """Times the float64 oracle on whole (sequence, decode step) samples, in
+    step order, until `budget_s` seconds of oracle arithmetic are timed; the
+    inputs of each sample are drawn beforehand (host memory) and only the
+    oracle's arithmetic is timed."""
     import numpy as np
     import threadpoolctl
 
@@ -222,17 +223,17 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     from oracle.rounding import round_store
     from synth import TENSOR_K, TENSOR_Q, TENSOR_V
 
-    def inputs(b):
+    def inputs(b, step):
         if w.kind == "ring":
-            t = int(w.decode_positions(0)[b])
+            t = int(w.decode_positions(step)[b])
             pos = np.asarray(resident_positions(t, w.sinks, w.window))
             return (pos, t, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos),
                     w.rows(TENSOR_Q, b, [t])[0])
         if w.kind == "paged":
             pos = np.arange(int(w.lengths[b]))
-            return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, 0)
+            return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
         pos = w.resident_positions(b)
-        return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, 0)
+        return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
 
     def oracle_step(pos, t, k_raw, v, q_raw):
         if w.kind == "ring":
@@ -245,23 +246,29 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
             q = q_raw.astype(np.float64)
         return attend_heads(q, k, v.astype(np.float64))
 
-    timed, n, b = 0.0, 0, 0
-    while n < w.batch and (n == 0 or timed < budget_s):
-        args = inputs(b)
-        t0 = time.perf_counter()
-        oracle_step(*args)
-        timed += time.perf_counter() - t0
-        n += 1
-        b += 1
+    oracle_step(*inputs(0, 0))  # untimed: first-touch of the arrays and BLAS start-up
+    timed, n, step, done = 0.0, 0, 0, False
+    while not done:
+        for b in range(w.batch):
+            args = inputs(b, step)
+            t0 = time.perf_counter()
+            oracle_step(*args)
+            timed += time.perf_counter() - t0
+            n += 1
+            if timed >= budget_s:
+                done = True
+                break
+        step += 1
+        done = done or step >= w.decode_steps
     per_seq = timed / n
     steps_per_s = 1.0 / (per_seq * w.batch)
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     return {"value": round(steps_per_s * kv_bytes_per_step(w) / 1e9, 4), "unit": "GB/s",
             "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
-            "sample": (f"decode step 0 of {w.name}, {n} of {w.batch} sequences (all heads), "
-                       f"inputs pre-drawn in host memory; float64 NumPy, {timed:.1f} s timed; "
-                       f"BLAS threads {threads}, elementwise ops on one thread; "
-                       f"scaled to the full batch")}
+            "sample": (f"{n} (sequence, decode step) samples of {w.name} (sequences in order, "
+                       f"steps from 0; all heads), inputs pre-drawn in host memory; float64 "
+                       f"NumPy, {timed:.1f} s timed; BLAS threads {threads}, elementwise ops "
+                       f"on one thread; scaled to one step of the full batch")}
 
 
 def copy_calibration(nbytes: int = 1 << 30) -> None:
