@@ -2,9 +2,10 @@
 """Decode-step benchmark on one MI355X.
 
 A step is one pass of the whole decode path over one batch: for the ring
-workloads, the fused RoPE append of the new token (which also rotates the
-query) followed by the split-K decode and its merge; for the paged / pool
-workloads, the decode and its merge.  Inputs are synthetic (synth/), resident
+workloads, the RoPE append of the new token and the split-K decode, both done
+by one decode_step_ring call (one launch, plus the split merge when a head is
+spread over several workgroups; --unfused: kv_append_rope, then
+decode_attn_ring); for the paged / pool workloads, the decode and its merge.  Inputs are synthetic (synth/), resident
 in HBM before the timed region; every step's new-token rows and query are
 staged on the device beforehand.
 
@@ -112,7 +113,7 @@ def decode_source_sha() -> str:
 # GPU side
 # ---------------------------------------------------------------------------
 
-def run_gpu(w, steps: int, warmup: int) -> dict:
+def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
     import numpy as np
     import torch
 
@@ -122,7 +123,9 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     from synth.draws import draw_rows_parallel
 
     torch.cuda.set_device(0)
-    total = warmup + steps  # steps with new tokens: warmup, then the timed steps
+    # steps with new tokens: warmup, then two timed regions (ring caches); the
+    # pools read the same state every step
+    total = warmup + 2 * steps
     t0 = time.time()
     if w.kind == "ring":
         st = RingState(w)
@@ -144,11 +147,19 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
             (start[None, :] + np.arange(total)[:, None]).astype(np.int32)).cuda()
         handle = st.cache.handle
 
-        def pre(i):
-            B.kv_append_rope(handle, k_all[i], v_all[i], pos_all[i], q_all[i])
+        if unfused:  # the two entry points: append (rotating q in place), then decode
+            def pre(i):
+                B.kv_append_rope(handle, k_all[i], v_all[i], pos_all[i], q_all[i])
 
-        def decode(i):
-            B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse)
+            def decode(i):
+                B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse)
+        else:  # one call per step: the decode launch appends the token itself
+            def pre(i):
+                pass
+
+            def decode(i):
+                B.decode_step_ring(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i],
+                                   q_all[i][:, 0], st.out, st.workspace, st.lse)
     else:
         st = PagedState(w, out_dtype=torch.float32)
         st.fill()
@@ -189,16 +200,17 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     wall = time.perf_counter() - wall0
     total_ms = begin.elapsed_time(end)
 
-    # Region 2: `steps` decode calls back to back on the state the last step
-    # left (no appends in between), events at the two ends: the mean duration
-    # of one decode call as the kernels run in a stream.  Every call reads the
-    # whole resident cache again (larger than the last-level cache, or cycled
-    # through pool copies that together are).
-    last = warmup + steps - 1
+    # Region 2: `steps` decode calls back to back, events at the two ends: the
+    # mean duration of one decode call as the kernels run in a stream.  Ring
+    # caches: the fused steps go on with new tokens (with --unfused, the
+    # decode call alone, repeated on the state the last step left).  Every
+    # call reads the whole resident cache again (larger than the last-level
+    # cache, or cycled through pool copies that together are).
     torch.cuda.synchronize()
     begin.record()
     for s in range(steps):
-        decode(last if w.kind == "ring" else warmup + steps + s)
+        i = warmup + steps + s
+        decode(warmup + steps - 1 if unfused and w.kind == "ring" else i)
     end.record()
     torch.cuda.synchronize()
     dec_ms = begin.elapsed_time(end) / steps
@@ -300,6 +312,9 @@ def main() -> int:
     ap.add_argument("--workload", default="mha-ring")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="ring caches: kv_append_rope + decode_attn_ring per step instead of "
+                         "decode_step_ring")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -314,7 +329,7 @@ def main() -> int:
 
     from synth import WORKLOADS
     w = WORKLOADS[args.workload]
-    res = run_gpu(w, args.steps, args.warmup)
+    res = run_gpu(w, args.steps, args.warmup, args.unfused)
     kv_bytes = kv_bytes_per_step(w)
     ms_per_step = res["total_ms"] / args.steps
     value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9

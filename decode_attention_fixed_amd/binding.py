@@ -62,6 +62,8 @@ _PROTOS = {
                                                    ctypes.POINTER(ctypes.c_size_t)]),
     "decode_attn_ring": (ctypes.c_int, [_vp, _vp, _i32, ctypes.c_float, _vp, _i32, _vp, _vp,
                                         ctypes.c_size_t, _vp]),
+    "decode_step_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _i32,
+                                        _vp, _vp, ctypes.c_size_t, _vp]),
     "decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
@@ -196,6 +198,20 @@ def decode_attn_ring(handle: int, q: torch.Tensor, out: torch.Tensor,
                                 _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
                                 _ptr(workspace, "workspace"), workspace.numel() *
                                 workspace.element_size(), _stream(stream)))
+
+
+def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                     q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+    """Append of one token per sequence + decode in one call.  k_new, v_new
+    [B, Hkv, d]; pos [B] int32; q [B, Hq, d] NOT rotated (left unchanged);
+    out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
+    _check("decode_step_ring",
+           LIB.decode_step_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                                _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1], scale,
+                                _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+                                _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -7,10 +7,9 @@
 // the storage dtype before the store ([pool] "bake RoPE into K"), V is copied
 // bit for bit, and the slot's true position is recorded ([ring] §3.2, §7).
 //
-// One workgroup per (sequence, token).  The d/2 rotation angles of the token
-// are computed once per workgroup in float64 (pos * theta reduced by the f64
-// sincos), so positions up to 2^31 lose no accuracy; the rotation itself is
-// done in f64 and rounded once to the storage dtype.
+// The rotation angles pos * theta_i are formed and reduced in float64 (the
+// theta_i come from the host), so positions up to 2^31 lose no accuracy; the
+// rotation itself is done in f64 and rounded once to the storage dtype.
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -35,13 +34,13 @@ struct Elem<false> {
   __device__ static void store(T* p, int i, double x) { p[i] = static_cast<float>(x); }
 };
 
-// Angles of the token: cos/sin(pos * base^(-2i/d)), i < d/2.
-__device__ void rope_angles(double pos, double base, int head_dim, double* s_cos, double* s_sin) {
+// Angles of the token: cos/sin(pos * theta_i), i < d/2.
+__device__ void rope_angles(double pos, const RopeFreq& freq, int head_dim, double* s_cos,
+                            double* s_sin) {
   const int half = head_dim / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
     double s, c;
-    sincos(pos * theta, &s, &c);
+    rope_sincos(pos, freq.theta[i], &s, &c);
     s_cos[i] = c;
     s_sin[i] = s;
   }
@@ -63,11 +62,10 @@ __device__ void rotate_rows(const typename Elem<BF16>::T* src, size_t src_stride
     const int i1 = rope_half ? i + half : 2 * i + 1;
     const typename E::T* s = src + static_cast<size_t>(r) * src_stride;
     typename E::T* d = dst + static_cast<size_t>(r) * dst_stride;
-    const double x0 = E::load(s, i0);
-    const double x1 = E::load(s, i1);
-    const double c = s_cos[i], sn = s_sin[i];
-    E::store(d, i0, x0 * c - x1 * sn);
-    E::store(d, i1, x0 * sn + x1 * c);
+    double o0, o1;
+    rope_rotate_pair(E::load(s, i0), E::load(s, i1), s_cos[i], s_sin[i], &o0, &o1);
+    E::store(d, i0, o0);
+    E::store(d, i1, o1);
   }
 }
 
@@ -117,9 +115,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
     const int w = is_k ? item : item - k_items;
     const int h = w / half;
     const int i = w - h * half;
-    const double theta = pow(p.rope_base, -2.0 * static_cast<double>(i) / static_cast<double>(d));
     double sn, cs;
-    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+    rope_sincos(static_cast<double>(pos), p.freq.theta[i], &sn, &cs);
     const int i0 = p.rope_half ? i : 2 * i;
     const int i1 = p.rope_half ? i + half : 2 * i + 1;
     const T* src;
@@ -134,10 +131,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
             ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
       src = dst;
     }
-    const double x0 = E::load(src, i0);
-    const double x1 = E::load(src, i1);
-    E::store(dst, i0, x0 * cs - x1 * sn);
-    E::store(dst, i1, x0 * sn + x1 * cs);
+    double o0, o1;
+    rope_rotate_pair(E::load(src, i0), E::load(src, i1), cs, sn, &o0, &o1);
+    E::store(dst, i0, o0);
+    E::store(dst, i1, o1);
     if (is_k && item == 0) p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
     return;
   }
@@ -169,7 +166,7 @@ __global__ __launch_bounds__(kAppendThreads) void write_paged_kernel(PagedWriteP
   const int32_t pos = rotate ? p.pos[n] : 0;
   if (pos < 0) return;
   if (rotate) {
-    rope_angles(static_cast<double>(pos), p.rope_base, p.head_dim, s_cos, s_sin);
+    rope_angles(static_cast<double>(pos), p.freq, p.head_dim, s_cos, s_sin);
     __syncthreads();
   }
   const int d = p.head_dim;

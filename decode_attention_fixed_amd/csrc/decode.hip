@@ -382,7 +382,8 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
   WorkspaceLayout w;
   w.o_offset = 0;
   w.lse_offset = up(slots * g * head_dim * sizeof(float));
-  w.total = w.lse_offset + up(slots * g * sizeof(float));
+  w.q_offset = w.lse_offset + up(slots * g * sizeof(float));
+  w.total = w.q_offset + up(static_cast<size_t>(batch) * num_q_heads * head_dim * sizeof(float));
   return w;
 }
 

@@ -128,6 +128,7 @@ struct RingRows {
   static constexpr bool kWholeSubtiles = false;
   const int32_t* slot_pos;
   size_t head_base;  // element offset of slot 0 of head (b, h)
+  int skip = -1;     // slot taken out of the stream (the fused step's new token)
   __device__ RingRows(const DecodeParams& p, int b, int h)
       : slot_pos(p.slot_pos + static_cast<size_t>(b) * p.slots),
         head_base((static_cast<size_t>(b) * p.num_kv_heads + h) * p.slots * kD) {}
@@ -139,7 +140,7 @@ struct RingRows {
     base = head_base + static_cast<size_t>(t) * kD;
     return true;
   }
-  __device__ bool row_ok(int t) const { return slot_pos[t] >= 0; }
+  __device__ bool row_ok(int t) const { return slot_pos[t] >= 0 && t != skip; }
 };
 
 // Pool: token t lives in block block_table[b][t >> shift], row t & (bs - 1);
@@ -185,6 +186,7 @@ struct PoolRows {
     return blk >= 0;
   }
   __device__ bool row_ok(int) const { return true; }
+  int skip = -1;  // unused: pools have no fused step
 };
 
 // Row subtiles (16 rows each) per wave tile: 4 when few query heads share the
@@ -208,14 +210,130 @@ struct Smem {
   int32_t blk[kMaxSplitBlocks];
 };
 
+// Fused decode step (ring caches): the token appended in the same launch.
+// Every workgroup of the sequence rotates the query itself; the workgroup
+// whose rows hold the token's slot also rotates and stores the token's K row,
+// V row and position, takes that slot out of its stream (it may hold the
+// evicted row, and the new row is being written meanwhile) and folds the new
+// token in from LDS at the workgroup merge, so no workgroup reads a row
+// written by this launch.
+struct NewToken {
+  bool app = false;   // the position is valid (>= 0): the token is appended
+  bool mine = false;  // this workgroup attends the token's slot
+  int slot = -1;
+  int32_t pos = 0;
+  double theta = 0.0;  // theta_(tid % 64), read first of all loads (they complete in order)
+};
+
+template <int G>
+struct NewRow {
+  double cs[kD / 2], sn[kD / 2];  // the token's rotation angles
+  uint16_t q[G][kD];              // rotated query heads (bf16, as an append stores them)
+  float k[kD], v[kD];             // its rotated K row and its V row
+  float x[G];                     // its score per head (log2 units)
+};
+
+// The fused step's work before the row loop, by every thread: read the raw
+// query pairs and the new token's K pair / V chunk (unconditionally, every
+// address is valid, so nothing waits on them early), compute the angles
+// (threads < 64) meanwhile, then rotate the query heads into nr.q (one pair
+// per thread) and, in the workgroup that attends the token's slot, store the
+// rotated K row, the V row and the position, and compute the token's score
+// per head into nr.x.  Angles, rotation and rounding are the append
+// kernel's, so the cache is bit-identical to an append.
+template <int G, int NW>
+__device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const NewToken& nt,
+                                    int b, int kvh, RingRows& rows) {
+  constexpr int kHalf = kD / 2;
+  constexpr int kItems = (G + 1) * kHalf;  // the query pairs, then the K pairs
+  constexpr int kPer = (kItems + NW * 64 - 1) / (NW * 64);
+  const int tid = threadIdx.x;
+  if (nt.mine) rows.skip = nt.slot;
+  const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
+  const size_t nrow = (static_cast<size_t>(b) * p.num_kv_heads + kvh) * kD;
+  const uint16_t* qb = static_cast<const uint16_t*>(p.q) + head0 * kD;
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + nrow;
+  uint16_t r0[kPer], r1[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int w = min(tid + j * NW * 64, kItems - 1);
+    const int h = w / kHalf, i = w - h * kHalf;
+    const int i0 = p.rope_half ? i : 2 * i;
+    const int i1 = p.rope_half ? i + kHalf : 2 * i + 1;
+    const uint16_t* src = h < G ? qb + h * kD : kn;
+    r0[j] = src[i0];
+    r1[j] = src[i1];
+  }
+  const Vec16 vraw = load16(static_cast<const uint16_t*>(p.v_new) + nrow + 8 * (tid & 15));
+  if (nt.app && tid < kHalf) {
+    double sn, cs;
+    rope_sincos(static_cast<double>(nt.pos), nt.theta, &sn, &cs);
+    nr.cs[tid] = cs;
+    nr.sn[tid] = sn;
+  }
+  __syncthreads();
+  const size_t crow = ((static_cast<size_t>(b) * p.num_kv_heads + kvh) * p.slots + nt.slot) * kD;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int w = tid + j * NW * 64;
+    if (w >= kItems) break;
+    const int h = w / kHalf, i = w - h * kHalf;
+    if (h == G && !nt.mine) break;
+    const int i0 = p.rope_half ? i : 2 * i;
+    const int i1 = p.rope_half ? i + kHalf : 2 * i + 1;
+    uint16_t o0 = r0[j], o1 = r1[j];
+    if (nt.app) {
+      double x0, x1;
+      rope_rotate_pair(static_cast<double>(bf16_to_f32(r0[j])),
+                       static_cast<double>(bf16_to_f32(r1[j])), nr.cs[i], nr.sn[i], &x0, &x1);
+      o0 = f64_to_bf16_rne(x0);
+      o1 = f64_to_bf16_rne(x1);
+    }
+    if (h < G) {
+      nr.q[h][i0] = o0;
+      nr.q[h][i1] = o1;
+    } else {  // the K row, rotated, into the cache and LDS
+      uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k)) + crow;
+      kc[i0] = o0;
+      kc[i1] = o1;
+      nr.k[i0] = bf16_to_f32(o0);
+      nr.k[i1] = bf16_to_f32(o1);
+    }
+  }
+  if (nt.mine && tid < kD / 8) {  // the V row
+    store16(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.v)) + crow + 8 * tid, vraw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nr.v[8 * tid + 2 * e] = bf16_lo(vraw.w[e]);
+      nr.v[8 * tid + 2 * e + 1] = bf16_hi(vraw.w[e]);
+    }
+  }
+  if (nt.mine && kvh == 0 && tid == 0)
+    const_cast<int32_t*>(p.slot_pos)[static_cast<size_t>(b) * p.slots + nt.slot] = nt.pos;
+  __syncthreads();
+  if (nt.mine) {  // the token's score: wave h sums head h
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    for (int h = wave; h < G; h += NW) {
+      float d = bf16_to_f32(nr.q[h][2 * lane]) * nr.k[2 * lane] +
+                bf16_to_f32(nr.q[h][2 * lane + 1]) * nr.k[2 * lane + 1];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (lane == 0) nr.x[h] = d * p.score_scale_log2;
+    }
+    // nr.x is read after the barriers of the row loop
+  }
+}
+
 // Attention of the G query heads of (b, kvh) over rows [t0, t1) by the whole
 // workgroup.  Writes the output and lse (direct) or, for a piece of a longer
 // sequence, the normalised partial output and base-2 lse at partial slot
 // `slot` (layout [slot][head][d]).  Every thread of the workgroup must call it
 // with the same arguments; it returns with LDS free for reuse.
-template <int G, class Rows, int NW>
+template <int G, class Rows, int NW, bool FUSED = false>
 __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int kvh, int t0,
-                             int t1, bool direct, size_t slot) {
+                             int t1, bool direct, size_t slot, NewRow<G>* nr = nullptr,
+                             NewToken nt = NewToken{}) {
   constexpr int NS = Smem<G, NW>::NS;
   constexpr int TILE = Smem<G, NW>::TILE;
   constexpr int KBUF = Smem<G, NW>::KBUF;
@@ -224,18 +342,25 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
   const int lq = lane >> 4;
   const int lc = lane & 15;
   const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
-  const Rows rows(p, b, kvh);
+  Rows rows(p, b, kvh);
   const uint16_t* kb = static_cast<const uint16_t*>(p.k);
   const uint16_t* vb = static_cast<const uint16_t*>(p.v);
 
-  // B operand: the g query heads of this kv head, zero-padded to 16.
+  // B operand: the g query heads of this kv head, zero-padded to 16 (the
+  // fused step rotates them into LDS first).
+  if constexpr (FUSED) fused_step_prologue<G, NW>(p, *nr, nt, b, kvh, rows);
   bf16x8_t qop[kKSteps];
   {
     const uint16_t* qb = static_cast<const uint16_t*>(p.q);
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) {
       Vec16 v{};
-      if (lc < G) v = load16(qb + (head0 + lc) * kD + 32 * s + 8 * lq);
+      if (lc < G) {
+        if constexpr (FUSED)
+          v = load16(&nr->q[lc][32 * s + 8 * lq]);
+        else
+          v = load16(qb + (head0 + lc) * kD + 32 * s + 8 * lq);
+      }
       qop[s] = as_bf16x8(v);
     }
   }
@@ -432,6 +557,11 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm.m[w][h]);
+    bool add_new = false;
+    if constexpr (FUSED) {
+      add_new = nt.mine;
+      if (add_new) mx = fmaxf(mx, nr->x[h]);
+    }
     float lt = 0.f, o = 0.f;
     if (mx != kNegInf) {
 #pragma unroll
@@ -439,6 +569,13 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
         const float sc = sm.m[w][h] == kNegInf ? 0.f : exp2f(sm.m[w][h] - mx);
         lt = fmaf(sm.l[w][h], sc, lt);
         o = fmaf(s_acc[w][h][d], sc, o);
+      }
+      if constexpr (FUSED) {
+        if (add_new) {  // the new token, as one more wave holding a single row
+          const float sc = exp2f(nr->x[h] - mx);
+          lt += sc;
+          o = fmaf(nr->v[d], sc, o);
+        }
       }
     }
     const float val = lt > 0.f ? o / lt : 0.f;
@@ -460,7 +597,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
 
 // Ring caches: grid of (b, kv head, split), one piece per workgroup; partial
 // slot (b * Hkv + kv head) * num_splits + split.
-template <int G, int NW>
+template <int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
   __shared__ Smem<G, NW> sm;
   const int ns = p.num_splits;
@@ -471,8 +608,21 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
   const int ntok = p.slots;
   const int t0 = split * p.split_tokens;
   const int t1 = min(t0 + p.split_tokens, ntok);
-  attend_piece<G, RingRows, NW>(p, sm, b, kvh, t0, t1, ns == 1,
-                                static_cast<size_t>(unit) * ns + split);
+  const size_t slot = static_cast<size_t>(unit) * ns + split;
+  if constexpr (FUSED) {
+    __shared__ NewRow<G> nr;
+    NewToken nt;
+    nt.theta = p.freq.theta[threadIdx.x & 63];
+    nt.pos = p.new_pos[b];
+    nt.app = nt.pos >= 0;
+    if (nt.app) {
+      nt.slot = nt.pos < p.sinks ? nt.pos : p.sinks + nt.pos % p.window;
+      nt.mine = nt.slot >= t0 && nt.slot < t1;
+    }
+    attend_piece<G, RingRows, NW, true>(p, sm, b, kvh, t0, t1, ns == 1, slot, &nr, nt);
+  } else {
+    attend_piece<G, RingRows, NW>(p, sm, b, kvh, t0, t1, ns == 1, slot);
+  }
 }
 
 // Balanced schedule of a paged pool, in granules of 64 rows.  Sequence b
@@ -879,16 +1029,32 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
     }                                                                                     \
     return hipGetLastError();                                                             \
   }
-SWA_KERNEL_TABLE(decode_ring_kernel)
 SWA_KERNEL_TABLE(decode_pool_kernel)
 #undef SWA_KERNEL_TABLE
+
+template <int NW, bool FUSED>
+hipError_t decode_ring_kernel_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {
+  switch (p.num_q_heads / p.num_kv_heads) {
+    case 1: decode_ring_kernel<1, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 2: decode_ring_kernel<2, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 3: decode_ring_kernel<3, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 4: decode_ring_kernel<4, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 6: decode_ring_kernel<6, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 8: decode_ring_kernel<8, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace
 
 hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
   const unsigned grid =
       static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
-  hipError_t err = decode_ring_kernel_launch<kRingWaves>(p, grid, stream);
+  // p.new_pos set: the fused step (append of one token per sequence + decode)
+  hipError_t err = p.new_pos != nullptr
+                       ? decode_ring_kernel_launch<kRingWaves, true>(p, grid, stream)
+                       : decode_ring_kernel_launch<kRingWaves, false>(p, grid, stream);
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);

@@ -37,6 +37,32 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// cos / sin of the RoPE angle pos * theta_i of one pair (theta_i =
+// base^(-2i/d), computed once on the host in float64).  The angle is formed
+// in float64 and reduced modulo 2 pi with a two-part 2 pi (Cody and Waite)
+// before the float64 sincos, which then stays on its short-argument path.
+// Every kernel that rotates a row takes its angles from here, so rows
+// written by different entry points are bit-identical.
+__device__ __forceinline__ void rope_sincos(double pos, double theta, double* s, double* c) {
+  constexpr double kTwoPiHi = 6.283185307179586232;       // 2 pi rounded to float64
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;     // 2 pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189533577;
+  const double a = pos * theta;
+  const double k = rint(a * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, a);
+  r = fma(-k, kTwoPiLo, r);
+  sincos(r, s, c);
+}
+
+// Rotation of one RoPE pair (x0, x1) by the angle with cosine c and sine s,
+// in float64 with explicit fused multiply-adds (no contraction choice is left
+// to the compiler, so every kernel computes the same bits).
+__device__ __forceinline__ void rope_rotate_pair(double x0, double x1, double c, double s,
+                                                 double* o0, double* o1) {
+  *o0 = fma(x0, c, -(x1 * s));
+  *o1 = fma(x0, s, x1 * c);
+}
+
 struct alignas(16) Vec16 {
   uint32_t w[4];
 };

@@ -211,7 +211,7 @@ swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new
   p.head_dim = cache->cfg.head_dim;
   p.window = cache->cfg.window;
   p.sinks = cache->cfg.num_sinks;
-  p.rope_base = cache->cfg.rope_base;
+  p.freq = swa::make_rope_freq(cache->cfg.rope_base, cache->cfg.head_dim);
   p.rope_half = cache->cfg.rope_style == SWA_ROPE_HALF;
   p.bf16 = cache->cfg.dtype == SWA_BF16;
   return from_hip(swa::launch_append_rope(p, static_cast<hipStream_t>(stream)), "kv_append_rope");
@@ -230,9 +230,12 @@ swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
   return ok();
 }
 
-swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
-                            float scale, void* out, swa_dtype out_dtype, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+// Checks a ring decode call and fills its parameters (shared by the plain
+// and the fused step).
+static swa_status ring_decode_params(const swa_cache* cache, const void* q, int32_t num_q_heads,
+                                     float scale, void* out, swa_dtype out_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     swa::DecodeParams& p, swa::WorkspaceLayout& lay) {
   if (cache == nullptr) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
   const swa_cache_config& cfg = cache->cfg;
   swa_status st = check_group(num_q_heads, cfg.num_kv_heads);
@@ -243,12 +246,11 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
                 static_cast<long long>(swa::kMaxMfmaTokens));
   const swa::SplitPlan plan =
       plan_for(cfg.dtype == SWA_BF16, cfg.head_dim, cfg.batch, cfg.num_kv_heads, slots, false);
-  const swa::WorkspaceLayout lay =
-      swa::workspace_layout(cfg.batch, num_q_heads, cfg.num_kv_heads, cfg.head_dim, slots);
+  lay = swa::workspace_layout(cfg.batch, num_q_heads, cfg.num_kv_heads, cfg.head_dim, slots);
   st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, lay.total);
   if (st != SWA_OK) return st;
 
-  swa::DecodeParams p{};
+  p = swa::DecodeParams{};
   p.q = q;
   p.k = cache->k;
   p.v = cache->v;
@@ -265,9 +267,75 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
   p.lse = lse;
   p.out_bf16 = out_dtype == SWA_BF16;
   p.bf16 = cfg.dtype == SWA_BF16;
+  p.sinks = cfg.num_sinks;
+  p.window = cfg.window;
+  p.rope_half = cfg.rope_style == SWA_ROPE_HALF;
+  p.freq = swa::make_rope_freq(cfg.rope_base, cfg.head_dim);
   fill_workspace_ptrs(p, workspace, lay);
+  return SWA_OK;
+}
+
+swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
+                            float scale, void* out, swa_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  swa::DecodeParams p;
+  swa::WorkspaceLayout lay;
+  const swa_status st = ring_decode_params(cache, q, num_q_heads, scale, out, out_dtype, lse,
+                                           workspace, workspace_bytes, p, lay);
+  if (st != SWA_OK) return st;
   return from_hip(swa::launch_decode_ring(p, static_cast<hipStream_t>(stream)),
                   "decode_attn_ring");
+}
+
+swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_new,
+                            const int32_t* pos, const void* q, int32_t num_q_heads, float scale,
+                            void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  swa::DecodeParams p;
+  swa::WorkspaceLayout lay;
+  swa_status st = ring_decode_params(cache, q, num_q_heads, scale, out, out_dtype, lse, workspace,
+                                     workspace_bytes, p, lay);
+  if (st != SWA_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || pos == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "k_new, v_new and pos must not be NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
+    return fail(SWA_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (swa::use_mfma_path(p.bf16, p.head_dim)) {  // one launch (plus the split merge)
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.new_pos = pos;
+    return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
+  }
+  // Other shapes: the append (rotating a copy of q kept in the workspace),
+  // then the decode over that copy.
+  void* q_copy = static_cast<char*>(workspace) + lay.q_offset;
+  const size_t q_bytes = static_cast<size_t>(p.batch) * num_q_heads * p.head_dim *
+                         (p.bf16 ? sizeof(uint16_t) : sizeof(float));
+  hipError_t err = hipMemcpyAsync(q_copy, q, q_bytes, hipMemcpyDeviceToDevice, s);
+  if (err != hipSuccess) return from_hip(err, "decode_step_ring");
+  swa::AppendParams a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos = pos;
+  a.q_inout = q_copy;
+  a.k_cache = cache->k;
+  a.v_cache = cache->v;
+  a.slot_pos = cache->slot_pos;
+  a.batch = p.batch;
+  a.n_tokens = 1;
+  a.num_kv_heads = p.num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = p.head_dim;
+  a.window = p.window;
+  a.sinks = p.sinks;
+  a.freq = p.freq;
+  a.rope_half = p.rope_half;
+  a.bf16 = p.bf16;
+  err = swa::launch_append_rope(a, s);
+  if (err != hipSuccess) return from_hip(err, "decode_step_ring");
+  p.q = q_copy;
+  return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
 }
 
 static swa_status check_paged_desc(const swa_paged_desc* d) {
@@ -370,7 +438,7 @@ swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool
   p.head_dim = desc->head_dim;
   p.block_size = desc->block_size;
   p.num_phys_blocks = desc->num_phys_blocks;
-  p.rope_base = rope_base;
+  p.freq = swa::make_rope_freq(rope_base, desc->head_dim);
   p.rope_half = rope_style == SWA_ROPE_HALF;
   p.bf16 = desc->dtype == SWA_BF16;
   return from_hip(swa::launch_write_paged(p, static_cast<hipStream_t>(stream)), "kv_write_paged");

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace swa {
 
 constexpr int kMaxGroup = 8;
@@ -26,6 +28,19 @@ constexpr int64_t kPoolSmallRows = 2048;
 constexpr int kMaxMfmaSplits = 512;             // ring splits per sequence on that path
 constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path
 
+// RoPE frequencies theta_i = base^(-2i/d), i < d/2 (d <= 128), computed on
+// the host in float64 and passed by value to every kernel that rotates.
+constexpr int kMaxRopePairs = 64;
+struct RopeFreq {
+  double theta[kMaxRopePairs];
+};
+inline RopeFreq make_rope_freq(double base, int head_dim) {
+  RopeFreq f{};
+  for (int i = 0; i < head_dim / 2 && i < kMaxRopePairs; ++i)
+    f.theta[i] = std::pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+  return f;
+}
+
 struct AppendParams {
   const void* k_new;      // [B, T, Hkv, d]
   const void* v_new;      // [B, T, Hkv, d]
@@ -35,7 +50,7 @@ struct AppendParams {
   void* v_cache;
   int32_t* slot_pos;      // [B, S+W]
   int32_t batch, n_tokens, num_kv_heads, num_q_heads, head_dim, window, sinks;
-  double rope_base;
+  RopeFreq freq;
   int rope_half;          // 0: pairs (2i, 2i+1); 1: pairs (i, i + d/2)
   int bf16;               // storage dtype
 };
@@ -48,7 +63,7 @@ struct PagedWriteParams {
   void* k_pool;           // [Nphys, Hkv, bs, d]
   void* v_pool;
   int32_t n_tokens, num_kv_heads, head_dim, block_size, num_phys_blocks;
-  double rope_base;
+  RopeFreq freq;
   int rope_half;
   int bf16;
 };
@@ -76,6 +91,14 @@ struct DecodeParams {
   float* lse;                 // [B, Hq] or null
   int out_bf16;
   int bf16;
+  // Fused decode step (ring): the new token of each sequence is appended by
+  // the decode launch itself.  new_pos null: plain decode.
+  const void* k_new;          // [B, Hkv, d], not rotated
+  const void* v_new;          // [B, Hkv, d]
+  const int32_t* new_pos;     // [B]
+  int32_t sinks, window;
+  int32_t rope_half;
+  RopeFreq freq;
 };
 
 struct SplitPlan {
@@ -98,6 +121,7 @@ SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_t
 struct WorkspaceLayout {
   size_t o_offset;
   size_t lse_offset;
+  size_t q_offset;  // [B, Hq, d] query copy of a fused step that runs as two launches
   size_t total;
 };
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

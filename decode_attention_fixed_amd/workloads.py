@@ -83,8 +83,14 @@ class RingState:
             pos=torch.from_numpy(t.astype(np.int32)).to(self.device),
         )
 
-    def step(self, inputs: dict, scale: float = 0.0) -> None:
-        """One decode step: append the new token (rotating q in place), then attend."""
+    def step(self, inputs: dict, scale: float = 0.0, fused: bool = False) -> None:
+        """One decode step.  fused: decode_step_ring (one call; q left as
+        given); else kv_append_rope (rotating q in place), then decode_attn_ring."""
+        if fused:
+            B.decode_step_ring(self.cache.handle, inputs["k"][:, 0], inputs["v"][:, 0],
+                               inputs["pos"], inputs["q"][:, 0], self.out, self.workspace,
+                               self.lse, scale)
+            return
         B.kv_append_rope(self.cache.handle, inputs["k"], inputs["v"], inputs["pos"], inputs["q"])
         B.decode_attn_ring(self.cache.handle, inputs["q"][:, 0], self.out, self.workspace,
                            self.lse, scale)

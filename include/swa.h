@@ -117,7 +117,8 @@ swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new
                           const int32_t* pos, int32_t n_tokens, void* q_inout,
                           int32_t num_q_heads, void* stream);
 
-/* Workspace (device bytes) that decode_attn_ring / decode_attn_paged need for
+/* Workspace (device bytes) that decode_attn_ring / decode_step_ring /
+ * decode_attn_paged need for
  * these sizes; max_kv_tokens = S + W for a ring cache, max_blocks_per_seq *
  * block_size for a paged pool.  0 bytes is never returned.
  *
@@ -147,6 +148,32 @@ swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
 swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q_heads,
                             float scale, void* out, swa_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* A whole decode step on a ring cache in one call: appends one new token per
+ * sequence and attends with its query ([ring] §4.3: append, then attend; the
+ * write half as kv_append_rope, the read half as decode_attn_ring).
+ *
+ *   k_new, v_new  [B, Hkv, d] in the cache dtype, device: the new token.
+ *   pos           [B] int32, device: its absolute position.
+ *   q             [B, Hq, d] in the cache dtype, device, NOT rotated: it is
+ *                 rotated at pos[b] (as kv_append_rope's q_inout would be)
+ *                 for the attention, and left unchanged in memory.
+ *   num_q_heads, scale, out, out_dtype, lse, workspace: as decode_attn_ring.
+ *
+ * Equivalent to kv_append_rope(cache, k_new, v_new, pos, 1, q', Hq) followed
+ * by decode_attn_ring(cache, q', ...) on a copy q' of q: the cache ends in
+ * the same state bit for bit, and out / lse agree up to float32 rounding (the
+ * new token's score is summed in another order).  A sequence with
+ * pos[b] < 0 appends nothing and attends with q as given, as that pair of
+ * calls does.  bf16 caches with d = 128 do both in the decode launch itself
+ * (the workgroup whose rows hold the new token's slot writes the token and
+ * takes it into its softmax from on-chip memory); other configurations run
+ * the two steps as separate launches on `stream`.  The cache is updated by
+ * the same launch that reads it: do not read it concurrently. */
+swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_new,
+                            const int32_t* pos, const void* q, int32_t num_q_heads, float scale,
+                            void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Paged pool: fixed-size blocks addressed through a block table.             */

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -157,6 +157,33 @@ def test_decode_ring_validation():
         assert call(hq=32 * 5) == B.SWA_ERR_UNSUPPORTED
         assert L.decode_attn_ring(None, FAKE, 32, 0.0, FAKE, 0, None, FAKE, need, None) == \
             B.SWA_ERR_INVALID_ARG
+    finally:
+        B.swa_cache_destroy(h)
+
+
+def test_decode_step_ring_validation():
+    h = _create()
+    L = B.LIB
+    need = B.decode_attn_workspace_bytes(8, 32, 32, 128, 4100)
+    try:
+        args = dict(k=FAKE, v=FAKE, pos=FAKE, q=FAKE, hq=32, out=FAKE, ws=FAKE, wsb=need)
+
+        def call(**kw):
+            a = dict(args)
+            a.update(kw)
+            return L.decode_step_ring(h, a["k"], a["v"], a["pos"], a["q"], a["hq"], 0.0, a["out"],
+                                      B.SWA_F32, None, a["ws"], a["wsb"], None)
+
+        assert call(k=None) == B.SWA_ERR_INVALID_ARG
+        assert call(v=None) == B.SWA_ERR_INVALID_ARG
+        assert call(pos=None) == B.SWA_ERR_INVALID_ARG
+        assert call(k=FAKE + 8) == B.SWA_ERR_INVALID_ARG   # not 16-byte aligned
+        assert call(pos=FAKE + 2) == B.SWA_ERR_INVALID_ARG
+        assert call(q=None) == B.SWA_ERR_INVALID_ARG
+        assert call(hq=48) == B.SWA_ERR_INVALID_ARG
+        assert call(wsb=need - 1) == B.SWA_ERR_WORKSPACE
+        assert L.decode_step_ring(None, FAKE, FAKE, FAKE, FAKE, 32, 0.0, FAKE, 0, None, FAKE, need,
+                                  None) == B.SWA_ERR_INVALID_ARG
     finally:
         B.swa_cache_destroy(h)
 

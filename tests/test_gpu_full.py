@@ -1,5 +1,6 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (same entry points, same split plan), on sampled outputs the
+benchmark times (same entry points: decode_step_ring for the ring caches,
+decode_attn_paged for the pools; same split plan), on sampled outputs the
 oracle computes one by one: every decode step runs on the GPU, a few steps x
 a few sequences (all heads) are checked against the float64 oracle, and the
 ring slot tables are checked bit for bit after the history and at every
@@ -66,7 +67,7 @@ def test_ring_workload_full(name):
         _log(f"{name}: history loaded, slot tables exact")
         checks = _checkpoints(w.decode_steps)
         for step in range(w.decode_steps):
-            st.step(st.step_inputs(step))
+            st.step(st.step_inputs(step), fused=True)  # the step the benchmark times
             if step not in checks:
                 continue
             torch.cuda.synchronize()
