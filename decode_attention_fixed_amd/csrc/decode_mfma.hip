@@ -190,14 +190,16 @@ struct PoolRows {
 };
 
 // Row subtiles (16 rows each) per wave tile: 4 when few query heads share the
-// kv head, fewer when the P*V accumulators take more registers (8-wave
-// workgroups cap a wave at 256 VGPRs).
-template <int G>
-constexpr int subtiles() { return G <= 2 ? 4 : (G < 8 ? 2 : 1); }
+// kv head, fewer when the P*V accumulators take more registers (two waves per
+// SIMD cap a wave at 256 VGPRs).  Pools stream best with one subtile per tile
+// for g >= 3 (measured: 1-1.5% over two on the paged and pool workloads);
+// ring caches with two for g = 3..6.
+template <int G, bool POOL>
+constexpr int subtiles() { return G <= 2 ? 4 : (G < 8 && !POOL ? 2 : 1); }
 
-template <int G, int NW>
+template <int G, int NW, int NS_>
 struct Smem {
-  static constexpr int NS = subtiles<G>();
+  static constexpr int NS = NS_;
   static constexpr int TILE = 16 * NS;
   static constexpr int KBUF = TILE * 16;  // 16-byte chunks per wave: TILE rows x 256 B
   static constexpr size_t KBYTES = static_cast<size_t>(NW) * KBUF * 16;
@@ -330,13 +332,14 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
 // sequence, the normalised partial output and base-2 lse at partial slot
 // `slot` (layout [slot][head][d]).  Every thread of the workgroup must call it
 // with the same arguments; it returns with LDS free for reuse.
-template <int G, class Rows, int NW, bool FUSED = false>
-__device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int kvh, int t0,
+template <int G, class Rows, int NW, bool FUSED = false, int NS_>
+__device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b, int kvh, int t0,
                              int t1, bool direct, size_t slot, NewRow<G>* nr = nullptr,
                              NewToken nt = NewToken{}) {
-  constexpr int NS = Smem<G, NW>::NS;
-  constexpr int TILE = Smem<G, NW>::TILE;
-  constexpr int KBUF = Smem<G, NW>::KBUF;
+  using Sm = Smem<G, NW, NS_>;
+  constexpr int NS = Sm::NS;
+  constexpr int TILE = Sm::TILE;
+  constexpr int KBUF = Sm::KBUF;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane >> 4;
@@ -599,7 +602,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW>& sm, int b, int 
 // slot (b * Hkv + kv head) * num_splits + split.
 template <int G, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
-  __shared__ Smem<G, NW> sm;
+  __shared__ Smem<G, NW, subtiles<G, false>()> sm;
   const int ns = p.num_splits;
   const int split = blockIdx.x % ns;
   const int unit = blockIdx.x / ns;
@@ -810,7 +813,7 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
   constexpr int NT = NW * 64;
-  __shared__ Smem<G, NW> sm;
+  __shared__ Smem<G, NW, subtiles<G, true>()> sm;
   __shared__ SeqChunk<NT> sc;
   const int64_t hkv = p.num_kv_heads;
   const int64_t nwg = gridDim.x;
