@@ -129,6 +129,11 @@ def test_tiny_ring_every_step():
     dict(dtype="f32", num_q_heads=8, num_kv_heads=4, head_dim=64, window=50, sinks=2,
          history="chunks:40:3"),
     dict(history="sinks+window", pos0_range=(5000, 70000), window=512, batch=3),
+    # positions near 2^31: the f64 angle and its reduction modulo 2 pi
+    dict(history="sinks+window", pos0_range=(2_147_000_000, 2_147_480_000), window=300, batch=2,
+         num_q_heads=8, num_kv_heads=2),
+    dict(window=1, sinks=4, history="chunks:10:2", num_q_heads=8, num_kv_heads=2),  # W = 1
+    dict(window=2, sinks=8, history="prefill:20", num_q_heads=8, num_kv_heads=2),   # S > W
 ])
 def test_ring_variants(kw):
     w = _W(**kw)

@@ -89,6 +89,8 @@ def _compare(a, b, step):
          history="prefill:25000", decode_steps=4),                          # many splits + merge
     dict(dtype="f32", head_dim=64, num_q_heads=8, num_kv_heads=4, window=50, sinks=2,
          history="chunks:40:3"),                                            # two-launch path
+    dict(window=1, sinks=4, history="chunks:10:2", num_q_heads=8, num_kv_heads=2),  # W = 1
+    dict(window=2, sinks=8, history="prefill:3", num_q_heads=8, num_kv_heads=2),    # S > W
 ])
 def test_fused_step_equals_two_calls(kw):
     w = _W(**kw)
@@ -130,6 +132,8 @@ def test_fused_step_negative_position():
     dict(num_q_heads=16, num_kv_heads=4, window=512, history="sinks+window",
          pos0_range=(3000, 50000), batch=4),
     dict(num_q_heads=12, num_kv_heads=2, window=700, history="chunks:256:4"),
+    dict(num_q_heads=8, num_kv_heads=2, window=300, history="sinks+window",
+         pos0_range=(2_147_000_000, 2_147_480_000)),                        # positions near 2^31
 ])
 def test_fused_step_oracle(kw):
     """Decode steps run through decode_step_ring only, against the oracle."""
