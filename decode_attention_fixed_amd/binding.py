@@ -64,6 +64,10 @@ _PROTOS = {
                                         ctypes.c_size_t, _vp]),
     "decode_step_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _i32,
                                         _vp, _vp, ctypes.c_size_t, _vp]),
+    "prefill_attn_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "prefill_attn_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
+                                         _i32, _vp, _vp, ctypes.c_size_t, _vp]),
     "decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
@@ -212,6 +216,35 @@ def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos:
                                 _ptr(out, "out"), _DTYPE_CODE[out.dtype],
                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def prefill_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                 n_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check("prefill_attn_workspace_bytes",
+           LIB.prefill_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_tokens,
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def new_prefill_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          n_tokens: int, device="cuda") -> torch.Tensor:
+    n = prefill_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill_attn_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                      q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                      lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+    """Chunked prefill: k_new, v_new [B, T, Hkv, d]; pos [B] int32 (position of
+    token 0); q [B, T, Hq, d] NOT rotated (left unchanged); out [B, T, Hq, d]
+    float32 or bf16; lse [B, T, Hq] float32 or None."""
+    _check("prefill_attn_ring",
+           LIB.prefill_attn_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                                 _ptr(pos, "pos", torch.int32), k_new.shape[1], _ptr(q, "q"),
+                                 q.shape[2], scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

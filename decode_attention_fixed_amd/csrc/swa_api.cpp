@@ -338,6 +338,108 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
   return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
 }
 
+swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t n_tokens, size_t* bytes) {
+  if (bytes == nullptr) return fail(SWA_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || num_kv_heads < 1 || n_tokens < 1)
+    return fail(SWA_ERR_INVALID_ARG, "batch, num_kv_heads, n_tokens must be >= 1");
+  swa_status st = check_group(num_q_heads, num_kv_heads);
+  if (st != SWA_OK) return st;
+  if (head_dim != 128) return fail(SWA_ERR_UNSUPPORTED, "prefill needs head_dim 128");
+  *bytes = swa::prefill_layout(batch, num_q_heads, num_kv_heads, head_dim, n_tokens).total;
+  return ok();
+}
+
+swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_new,
+                             const int32_t* pos, int32_t n_tokens, const void* q,
+                             int32_t num_q_heads, float scale, void* out, swa_dtype out_dtype,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache == nullptr) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+  const swa_cache_config& cfg = cache->cfg;
+  if (cfg.dtype != SWA_BF16 || cfg.head_dim != 128)
+    return fail(SWA_ERR_UNSUPPORTED, "prefill needs a bf16 cache with head_dim 128");
+  swa_status st = check_group(num_q_heads, cfg.num_kv_heads);
+  if (st != SWA_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || pos == nullptr || q == nullptr || out == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "k_new, v_new, pos, q and out must not be NULL");
+  if (n_tokens < 1) return fail(SWA_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", n_tokens);
+  if (static_cast<int64_t>(n_tokens) * cfg.batch * num_q_heads > INT32_MAX)
+    return fail(SWA_ERR_INVALID_ARG, "batch * n_tokens * num_q_heads too large");
+  if (!dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q, 16) || !aligned(out, 16) ||
+      !aligned(pos, 4) || (lse != nullptr && !aligned(lse, 4)))
+    return fail(SWA_ERR_INVALID_ARG, "k_new / v_new / q / out must be 16-byte aligned");
+  const swa::PrefillLayout lay =
+      swa::prefill_layout(cfg.batch, num_q_heads, cfg.num_kv_heads, cfg.head_dim, n_tokens);
+  if (workspace == nullptr) return fail(SWA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(SWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(SWA_ERR_WORKSPACE, "workspace too small: %zu bytes, need %zu", workspace_bytes,
+                lay.total);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const swa::RopeFreq freq = swa::make_rope_freq(cfg.rope_base, cfg.head_dim);
+
+  swa::RotateChunkParams r{};
+  r.q = q;
+  r.k = k_new;
+  r.pos = pos;
+  r.q_rot = ws + lay.q_offset;
+  r.k_rot = ws + lay.k_offset;
+  r.batch = cfg.batch;
+  r.n_tokens = n_tokens;
+  r.num_q_heads = num_q_heads;
+  r.num_kv_heads = cfg.num_kv_heads;
+  r.rope_half = cfg.rope_style == SWA_ROPE_HALF;
+  r.freq = freq;
+  hipError_t err = swa::launch_rotate_chunk(r, s);
+  if (err != hipSuccess) return from_hip(err, "prefill_attn_ring");
+
+  swa::PrefillParams p{};
+  p.q_rot = r.q_rot;
+  p.k_rot = r.k_rot;
+  p.v_new = v_new;
+  p.k_cache = cache->k;
+  p.v_cache = cache->v;
+  p.slot_pos = cache->slot_pos;
+  p.pos = pos;
+  p.batch = cfg.batch;
+  p.n_tokens = n_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cfg.num_kv_heads;
+  p.slots = cfg.num_sinks + cfg.window;
+  p.sinks = cfg.num_sinks;
+  p.window = cfg.window;
+  const int32_t tokens_per_wg = 64 / (num_q_heads / cfg.num_kv_heads);
+  p.token_blocks = (n_tokens + tokens_per_wg - 1) / tokens_per_wg;
+  p.score_scale_log2 = resolve_scale(scale, cfg.head_dim);
+  p.out = out;
+  p.lse = lse;
+  p.out_bf16 = out_dtype == SWA_BF16;
+  err = swa::launch_prefill(p, s);
+  if (err != hipSuccess) return from_hip(err, "prefill_attn_ring");
+
+  swa::AppendParams a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos = pos;
+  a.q_inout = nullptr;
+  a.k_cache = cache->k;
+  a.v_cache = cache->v;
+  a.slot_pos = cache->slot_pos;
+  a.batch = cfg.batch;
+  a.n_tokens = n_tokens;
+  a.num_kv_heads = cfg.num_kv_heads;
+  a.num_q_heads = 0;
+  a.head_dim = cfg.head_dim;
+  a.window = cfg.window;
+  a.sinks = cfg.num_sinks;
+  a.freq = freq;
+  a.rope_half = cfg.rope_style == SWA_ROPE_HALF;
+  a.bf16 = 1;
+  return from_hip(swa::launch_append_rope(a, s), "prefill_attn_ring");
+}
+
 static swa_status check_paged_desc(const swa_paged_desc* d) {
   if (d == nullptr) return fail(SWA_ERR_INVALID_ARG, "desc is NULL");
   if (d->batch < 1 || d->num_kv_heads < 1 || d->max_blocks_per_seq < 1 || d->num_phys_blocks < 1)

@@ -137,4 +137,43 @@ hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream);
 
 bool group_supported(int g);
 
+// Chunked prefill over a ring cache (bf16, head_dim 128): T new tokens per
+// sequence attend the ring as it was before the chunk plus the chunk itself,
+// causally, each with its own window; then the chunk is appended.
+struct RotateChunkParams {
+  const void* q;          // [B, T, Hq, d], not rotated
+  const void* k;          // [B, T, Hkv, d], not rotated
+  const int32_t* pos;     // [B]: position of token 0
+  void* q_rot;            // [B, T, Hq, d]
+  void* k_rot;            // [B, T, Hkv, d]
+  int32_t batch, n_tokens, num_q_heads, num_kv_heads;
+  int rope_half;
+  RopeFreq freq;
+};
+
+struct PrefillParams {
+  const void* q_rot;          // [B, T, Hq, d] bf16, rotated
+  const void* k_rot;          // [B, T, Hkv, d] bf16, rotated
+  const void* v_new;          // [B, T, Hkv, d] bf16
+  const void* k_cache;        // [B, Hkv, slots, d]: the ring before the chunk
+  const void* v_cache;
+  const int32_t* slot_pos;    // [B, slots]
+  const int32_t* pos;         // [B]: position of token 0
+  int32_t batch, n_tokens, num_q_heads, num_kv_heads, slots, sinks, window;
+  int32_t token_blocks;       // workgroups per (sequence, kv head)
+  float score_scale_log2;
+  void* out;                  // [B, T, Hq, d] f32 or bf16
+  float* lse;                 // [B, T, Hq] or null
+  int out_bf16;
+};
+
+// Workspace of a prefill call: rotated queries, then rotated K rows.
+struct PrefillLayout {
+  size_t q_offset, k_offset, total;
+};
+PrefillLayout prefill_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t n_tokens);
+hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 }  // namespace swa

@@ -95,6 +95,28 @@ class RingState:
         B.decode_attn_ring(self.cache.handle, inputs["q"][:, 0], self.out, self.workspace,
                            self.lse, scale)
 
+    def chunk_inputs(self, first_step: int, n: int) -> dict:
+        """Raw inputs of decode steps first_step .. first_step + n - 1 as one
+        prefill chunk: k, v [B, n, Hkv, d], q [B, n, Hq, d], pos [B]."""
+        t = self.w.decode_positions(first_step)
+        return dict(
+            k=to_device(self._rows(TENSOR_K, t, n), self.w.dtype, self.device),
+            v=to_device(self._rows(TENSOR_V, t, n), self.w.dtype, self.device),
+            q=to_device(self._rows(TENSOR_Q, t, n), self.w.dtype, self.device),
+            pos=torch.from_numpy(t.astype(np.int32)).to(self.device),
+        )
+
+    def prefill_chunk(self, inputs: dict, out: torch.Tensor, lse: torch.Tensor | None = None,
+                      scale: float = 0.0, workspace: torch.Tensor | None = None) -> None:
+        """prefill_attn_ring over one chunk (see chunk_inputs)."""
+        w = self.w
+        n = inputs["k"].shape[1]
+        if workspace is None:
+            workspace = B.new_prefill_workspace(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                w.head_dim, n, self.device)
+        B.prefill_attn_ring(self.cache.handle, inputs["k"], inputs["v"], inputs["pos"],
+                            inputs["q"], out, workspace, lse, scale)
+
     def close(self) -> None:
         self.cache.close()
 

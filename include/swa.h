@@ -175,6 +175,44 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Workspace (device bytes) of a prefill_attn_ring call with n_tokens tokens
+ * per sequence.  Needs no initialisation. */
+swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t n_tokens, size_t* bytes);
+
+/* Chunked prefill on a ring cache ([pool] chunked prefill): n_tokens new
+ * tokens per sequence, at positions pos[b] .. pos[b] + n_tokens - 1, are
+ * attended and then appended.
+ *
+ *   k_new, v_new  [B, n_tokens, Hkv, d] in the cache dtype, device.
+ *   pos           [B] int32, device: position of token 0 of sequence b.
+ *   q             [B, n_tokens, Hq, d] in the cache dtype, device, NOT rotated
+ *                 (rotated at its position for the attention, left unchanged
+ *                 in memory).
+ *   out           [B, n_tokens, Hq, d] of out_dtype; lse [B, n_tokens, Hq]
+ *                 float32 natural-log, or NULL.
+ *   workspace     prefill_attn_workspace_bytes(B, Hq, Hkv, d, n_tokens) bytes,
+ *                 device, 256-byte aligned.
+ *
+ * Query row (b, j, h) equals what a decode step at position t = pos[b] + j
+ * would give after the tokens before it were appended: attention over the
+ * keys at positions p <= t with p < S or p > t - W ([sink] cache formula;
+ * [ring] §2.2), from the ring as it was before the call (positions below
+ * pos[b]) and from the chunk itself (causal).  Afterwards the cache is in the
+ * state kv_append_rope(cache, k_new, v_new, pos, n_tokens, NULL) leaves, bit
+ * for bit.  A token at a negative position is neither attended nor appended;
+ * its query row gets out = 0, lse = -inf.
+ *
+ * Supported: bf16 caches with d = 128, Hq / Hkv in {1, 2, 3, 4, 6, 8}
+ * (SWA_ERR_UNSUPPORTED otherwise).  The product P V runs in fp16 with fp32
+ * accumulation: V must stay below 65504 in magnitude.  Three launches on
+ * `stream` (rotation, attention, append); the call reads and then writes the
+ * cache: do not read it concurrently. */
+swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_new,
+                             const int32_t* pos, int32_t n_tokens, const void* q,
+                             int32_t num_q_heads, float scale, void* out, swa_dtype out_dtype,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Paged pool: fixed-size blocks addressed through a block table.             */
 /* ------------------------------------------------------------------------- */

@@ -10,6 +10,10 @@ Ring workloads (sink + sliding window, [sink] cache formula, [ring] §2.2):
   [ring] demo does, §4.3).  Cached K rows carry RoPE at their absolute
   position, rounded to the storage dtype ([pool] "bake RoPE into K"); V rows
   are stored as given; the query is rotated at t and stored the same way.
+Chunked prefill on a ring ([pool] chunked prefill): a chunk of T new tokens
+  at positions p0 .. p0 + T - 1; query row j is exactly decode step j of the
+  same workload (position p0 + j attends R(p0 + j) after the tokens before it
+  were appended), so the expected rows are the decode steps' outputs.
 Paged workloads (block table with a shared prefix, [share] §3.1-§3.2):
   plain causal attention over all len_b tokens of sequence b; K rows are used
   as given (no RoPE on this workload).
@@ -52,6 +56,16 @@ def ring_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
     pos = resident_positions(t, w.sinks, w.window)
     k, v = ring_rows(w, b, pos, style)
     return attend_heads(ring_query(w, b, t, style), k, v, scale)
+
+
+def ring_prefill_expected(w, b: int, first_step: int, n_tokens: int, scale=None,
+                          style: str = "interleaved", rows=None):
+    """(out [n, Hq, d], lse [n, Hq]) of a prefill chunk made of decode steps
+    first_step .. first_step + n - 1 of sequence b; `rows` restricts to a
+    subset of the chunk's rows (indices into the chunk)."""
+    idx = range(n_tokens) if rows is None else rows
+    res = [ring_expected(w, b, first_step + j, scale, style) for j in idx]
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
 
 
 def ring_appended_positions(w, b: int, through_step: int | None = None) -> list:

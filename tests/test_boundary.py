@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 13, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -186,6 +186,41 @@ def test_decode_step_ring_validation():
                                   None) == B.SWA_ERR_INVALID_ARG
     finally:
         B.swa_cache_destroy(h)
+
+
+def test_prefill_validation():
+    h = _create()
+    L = B.LIB
+    need = B.prefill_attn_workspace_bytes(8, 32, 32, 128, 64)
+    assert need >= 8 * 64 * (32 + 32) * 128 * 2 and need % 256 == 0
+    try:
+        args = dict(k=FAKE, v=FAKE, pos=FAKE, n=64, q=FAKE, hq=32, out=FAKE, ws=FAKE, wsb=need)
+
+        def call(handle=h, **kw):
+            a = dict(args)
+            a.update(kw)
+            return L.prefill_attn_ring(handle, a["k"], a["v"], a["pos"], a["n"], a["q"], a["hq"],
+                                       0.0, a["out"], B.SWA_F32, None, a["ws"], a["wsb"], None)
+
+        assert call(k=None) == B.SWA_ERR_INVALID_ARG
+        assert call(q=None) == B.SWA_ERR_INVALID_ARG
+        assert call(n=0) == B.SWA_ERR_INVALID_ARG
+        assert call(hq=48) == B.SWA_ERR_INVALID_ARG
+        assert call(out=FAKE + 4) == B.SWA_ERR_INVALID_ARG
+        assert call(wsb=need - 1) == B.SWA_ERR_WORKSPACE
+        assert call(ws=FAKE + 16) == B.SWA_ERR_WORKSPACE
+        assert call(handle=None) == B.SWA_ERR_INVALID_ARG
+    finally:
+        B.swa_cache_destroy(h)
+    for kw in (dict(dtype="f32"), dict(head_dim=64)):   # only bf16, d = 128
+        h = _create(**kw)
+        try:
+            assert L.prefill_attn_ring(h, FAKE, FAKE, FAKE, 8, FAKE, 32, 0.0, FAKE, B.SWA_F32,
+                                       None, FAKE, 1 << 30, None) == B.SWA_ERR_UNSUPPORTED
+        finally:
+            B.swa_cache_destroy(h)
+    with pytest.raises(B.SwaError):
+        B.prefill_attn_workspace_bytes(8, 32, 32, 64, 64)
 
 
 def _desc(**kw):

@@ -178,3 +178,28 @@ def test_pins_catch_planted_mistakes():
 
     for bad in (no_scale, misindexed_values, unnormalised):
         assert not np.allclose(bad(q, K, V), want, atol=1e-6), bad.__name__
+
+
+@pytest.mark.parametrize("sinks,window,first", [(4, 16, 30), (0, 8, 5), (2, 64, 1), (3, 5, 0)])
+def test_prefill_rows_are_windowed_causal_attention(sinks, window, first):
+    """A prefill chunk's expected rows (decode steps of the workload) equal one
+    masked scaled_dot_product_attention over the whole history: query j at
+    t = first + j keeps the positions p <= t with p < S or p > t - W."""
+    from oracle.decode import ring_prefill_expected
+    T = 12
+    w = RingWorkload(name="p", seed=7, batch=1, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                     dtype="f32", window=window, sinks=sinks, rope_base=10000.0, scale=1.0,
+                     decode_steps=T, history=f"prefill:{first}")
+    n = first + T
+    K, V = ring_rows(w, 0, range(n))                       # [n, Hkv, d]
+    Q = np.stack([ring_query(w, 0, first + j) for j in range(T)])  # [T, Hq, d]
+    t = first + np.arange(T)[:, None]
+    p = np.arange(n)[None, :]
+    keep = (p <= t) & ((p < sinks) | (p > t - window))
+    qt = torch.from_numpy(Q).permute(1, 0, 2)[None]        # [1, Hq, T, d]
+    kt = torch.from_numpy(np.ascontiguousarray(K)).permute(1, 0, 2)[None].contiguous()
+    vt = torch.from_numpy(np.ascontiguousarray(V)).permute(1, 0, 2)[None].contiguous()
+    want = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(keep),
+                                          enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    got, _ = ring_prefill_expected(w, 0, 0, T)
+    assert np.abs(got - want).max() < 1e-12
