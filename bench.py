@@ -27,6 +27,13 @@ Prints one JSON line:
   cpu_baseline     the float64 NumPy oracle on a bounded sample of the same
                    workload (inputs already in host memory), host cores.
 
+Prefill workloads (mha-prefill, gqa-prefill): a step is one prefill_attn_ring
+call over a chunk of new tokens per sequence (rotation of the chunk, the
+windowed causal attention, the append); `value` and `roofline` are then in
+TFLOP/s of useful attention arithmetic (4 x d flops per visible (query head,
+key) pair: S = Q K^T and O = P V) against the 2.5 PFLOP/s dense bf16 / fp16
+MFMA peak; `roofline` times the whole call (its three launches).
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
@@ -45,9 +52,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRCS = [os.path.join(ROOT, "decode_attention_fixed_amd", "csrc", f)
-               for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
+_CSRC = os.path.join(ROOT, "decode_attention_fixed_amd", "csrc")
+DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
+PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill.hip", "append_rope.hip",
+                                                 "device_common.h")]
 
 
 def log(msg: str) -> None:
@@ -56,9 +66,11 @@ def log(msg: str) -> None:
 
 def describe(w) -> dict:
     if w.kind == "ring":
+        what = (f"{w.chunk}-token prefill chunk per sequence per step" if w.chunk
+                else "append+decode per step")
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, W={w.window} + {w.sinks} sinks, "
-                f"history {w.history}, append+decode per step")
+                f"history {w.history}, {what}")
     elif w.kind == "paged":
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.block_size}-token blocks, lengths "
@@ -86,10 +98,26 @@ def kv_bytes_per_step(w) -> int:
     return resident_tokens(w) * w.kv_bytes_per_token()
 
 
-def traffic_record(name: str):
-    """Counter-measured HBM bytes per decode call of workload `name`, if they
-    were taken on the current kernel sources."""
-    path = os.path.join(PROFILES, f"decode_{name}_traffic.txt")
+def visible_keys(w, t):
+    """Keys a query at position t attends on a sink + window ring (t >= 0):
+    the last min(t + 1, W) positions, plus the sinks that fall before them."""
+    import numpy as np
+    t = np.asarray(t, dtype=np.int64)
+    return np.minimum(t + 1, w.window) + np.minimum(w.sinks, np.maximum(0, t + 1 - w.window))
+
+
+def prefill_flops(w, first_positions) -> int:
+    """Useful flops of one prefill call whose chunks start at first_positions
+    [B]: 2 per multiply-add of S = Q K^T and of O = P V, over visible keys."""
+    import numpy as np
+    t = np.asarray(first_positions, dtype=np.int64)[:, None] + np.arange(w.chunk)[None, :]
+    return int(visible_keys(w, t).sum()) * w.num_q_heads * w.head_dim * 4
+
+
+def traffic_record(name: str, prefix: str = "decode"):
+    """Counter-measured HBM bytes per call of workload `name`, if they were
+    taken on the current kernel sources."""
+    path = os.path.join(PROFILES, f"{prefix}_{name}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -97,16 +125,20 @@ def traffic_record(name: str):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != decode_source_sha():
+    if rec.get("source_sha256") != source_sha(prefix):
         return None
     return rec
 
 
-def decode_source_sha() -> str:
+def source_sha(prefix: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in DECODE_SRCS:
+    for f in (PREFILL_SRCS if prefix == "prefill" else DECODE_SRCS):
         h.update(open(f, "rb").read())
     return h.hexdigest()
+
+
+def decode_source_sha() -> str:
+    return source_sha("decode")
 
 
 # ---------------------------------------------------------------------------
@@ -127,7 +159,27 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
     # pools read the same state every step
     total = warmup + 2 * steps
     t0 = time.time()
-    if w.kind == "ring":
+    if w.kind == "ring" and w.chunk:
+        # One chunk of rows drawn from the workload, reused by every call at
+        # advancing positions (each call rotates and appends it anew).
+        st = RingState(w)
+        st.prefill()
+        inp = st.chunk_inputs(0, w.chunk)
+        ws = B.new_prefill_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                     w.chunk, "cuda")
+        out = torch.empty(w.batch, w.chunk, w.num_q_heads, w.head_dim, dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.empty(w.batch, w.chunk, w.num_q_heads, dtype=torch.float32, device="cuda")
+        first = w.decode_start[None, :] + w.chunk * np.arange(total)[:, None]
+        pos_all = torch.from_numpy(first.astype(np.int32)).cuda()
+        handle = st.cache.handle
+
+        def pre(i):
+            pass
+
+        def decode(i):
+            B.prefill_attn_ring(handle, inp["k"], inp["v"], pos_all[i], inp["q"], out, ws, lse)
+    elif w.kind == "ring":
         st = RingState(w)
         st.prefill()
         start = w.decode_start
@@ -210,11 +262,17 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
     begin.record()
     for s in range(steps):
         i = warmup + steps + s
-        decode(warmup + steps - 1 if unfused and w.kind == "ring" else i)
+        decode(warmup + steps - 1 if unfused and w.kind == "ring" and not w.chunk else i)
     end.record()
     torch.cuda.synchronize()
     dec_ms = begin.elapsed_time(end) / steps
-    return {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
+    res = {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
+    if w.kind == "ring" and w.chunk:
+        first = w.decode_start[None, :] + w.chunk * np.arange(total)[:, None]
+        res["flops_region1"] = sum(prefill_flops(w, first[warmup + s]) for s in range(steps))
+        res["flops_region2"] = sum(prefill_flops(w, first[warmup + steps + s])
+                                   for s in range(steps))
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -259,7 +317,7 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         return attend_heads(q, k, v.astype(np.float64))
 
     oracle_step(*inputs(0, 0))  # untimed: first-touch of the arrays and BLAS start-up
-    timed, n, step, done = 0.0, 0, 0, False
+    timed, n, step, done, flops = 0.0, 0, 0, False, 0
     while not done:
         for b in range(w.batch):
             args = inputs(b, step)
@@ -267,6 +325,8 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
             oracle_step(*args)
             timed += time.perf_counter() - t0
             n += 1
+            if w.kind == "ring" and w.chunk:
+                flops += int(visible_keys(w, args[1])) * w.num_q_heads * w.head_dim * 4
             if timed >= budget_s:
                 done = True
                 break
@@ -275,6 +335,15 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     per_seq = timed / n
     steps_per_s = 1.0 / (per_seq * w.batch)
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    if w.kind == "ring" and w.chunk:
+        return {"value": round(flops / timed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle",
+                "sample": (f"{n} (sequence, chunk row) samples of {w.name} (sequences in "
+                           f"order, rows from the first chunk's first; all heads; a chunk "
+                           f"row is the decode step at its position), inputs pre-drawn in "
+                           f"host memory; float64 NumPy, {timed:.1f} s timed; BLAS threads "
+                           f"{threads}, elementwise ops on one thread; useful flops of the "
+                           f"sampled rows / time")}
     return {"value": round(steps_per_s * kv_bytes_per_step(w) / 1e9, 4), "unit": "GB/s",
             "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
             "sample": (f"{n} (sequence, decode step) samples of {w.name} (sequences in order, "
@@ -304,6 +373,31 @@ def copy_calibration(nbytes: int = 1 << 30) -> None:
                       "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def prefill_line(w, args, res) -> dict:
+    ms_per_step = res["total_ms"] / args.steps
+    value = res["flops_region1"] / (res["total_ms"] / 1e3) / 1e12
+    per_call = res["flops_region2"] / args.steps
+    achieved = per_call / (res["decode_ms_mean"] / 1e3) / 1e12
+    traffic = traffic_record(w.name, "prefill")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": (int(float(traffic["fetch_bytes_per_call"])
+                                + float(traffic["write_bytes_per_call"]))
+                            if traffic else None),
+                "kernel": ("prefill call: chunk rotation, the windowed causal attention "
+                           "kernel (S in bf16, P V in fp16 MFMA, fp32 accumulation) and the "
+                           "append, on the launch stream, timed together"),
+                "algorithmic_flops": int(per_call)}
+    return {
+        "metric": "prefill-attention TFLOP/s", "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": describe(w),
+        "tokens_per_s": round(w.batch * w.chunk * 1e3 / ms_per_step, 1),
+        "roofline": roofline,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +424,12 @@ def main() -> int:
     from synth import WORKLOADS
     w = WORKLOADS[args.workload]
     res = run_gpu(w, args.steps, args.warmup, args.unfused)
+    if w.kind == "ring" and w.chunk:
+        out = prefill_line(w, args, res)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(w)
+        print(json.dumps(out), flush=True)
+        return 0
     kv_bytes = kv_bytes_per_step(w)
     ms_per_step = res["total_ms"] / args.steps
     value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9

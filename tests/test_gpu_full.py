@@ -4,13 +4,16 @@ decode_attn_paged for the pools; same split plan), on sampled outputs the
 oracle computes one by one: every decode step runs on the GPU, a few steps x
 a few sequences (all heads) are checked against the float64 oracle, and the
 ring slot tables are checked bit for bit after the history and at every
-checked step."""
+checked step.  The prefill workloads run their chunks through
+prefill_attn_ring with the benchmark's output dtype (bf16) and check sampled
+rows of sampled sequences."""
 
 import numpy as np
 import pytest
 import torch
 
-from oracle.decode import paged_expected, pool_expected, ring_expected, ring_slot_table
+from oracle.decode import (paged_expected, pool_expected, ring_expected, ring_prefill_expected,
+                           ring_slot_table)
 from oracle.ring import slot_contents
 from synth import WORKLOADS
 
@@ -88,6 +91,39 @@ def test_ring_workload_full(name):
                 assert err <= TOL, (name, step, b, err)
                 assert np.abs(lse[b] - want_lse).max() <= 1e-2
             _log(f"{name}: step {step} max-abs error {worst:.2e}")
+    finally:
+        st.close()
+
+
+@pytest.mark.parametrize("name", ["mha-prefill", "gqa-prefill"])
+def test_prefill_workload_full(name):
+    from decode_attention_fixed_amd.workloads import RingState
+    w = WORKLOADS[name]
+    rng = np.random.default_rng(77)
+    st = RingState(w)
+    try:
+        st.prefill()
+        n = w.chunk
+        out = torch.empty(w.batch, n, w.num_q_heads, w.head_dim, dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.empty(w.batch, n, w.num_q_heads, device="cuda")
+        for c in range(2):
+            first = c * n
+            st.prefill_chunk(st.chunk_inputs(first, n), out, lse)
+            torch.cuda.synchronize()
+            sp = st.cache.slot_pos.cpu().numpy()
+            o = out.float().cpu().numpy()
+            l = lse.cpu().numpy()
+            rows = [0, 1, n // 2, n - 1]
+            worst = 0.0
+            for b in _sample(w.batch, rng, k=2):
+                assert np.array_equal(sp[b], ring_slot_table(w, b, first + n - 1)), (b, c)
+                want, want_lse = ring_prefill_expected(w, b, first, n, rows=rows)
+                err = float(np.abs(o[b][rows] - want).max())
+                worst = max(worst, err)
+                assert err <= TOL, (name, c, b, err)
+                assert np.abs(l[b][rows] - want_lse).max() <= 1e-2
+            _log(f"{name}: chunk {c} max-abs error {worst:.2e}")
     finally:
         st.close()
 

@@ -87,3 +87,16 @@ def test_pool_workload_structure():
     # sequence 0 is the same in the batch-1 and batch-16 variants
     assert np.array_equal(WORKLOADS["long-pool-b1"].slot_blocks[0],
                           WORKLOADS["long-pool-b16"].slot_blocks[0])
+
+
+def test_prefill_workloads_continue_the_ring_workloads():
+    """The prefill workloads are the ring workloads' caches, taken a chunk of
+    decode steps per call."""
+    for pre, ring in (("mha-prefill", "mha-ring"), ("gqa-prefill", "gqa-ring")):
+        p, r = WORKLOADS[pre], WORKLOADS[ring]
+        assert p.chunk > 0 and p.decode_steps % p.chunk == 0
+        assert np.array_equal(p.decode_start, r.decode_start)
+        assert p.history_calls()[-1][1] == r.history_calls()[-1][1]
+        a = p.rows(TENSOR_K, 1, [7, int(p.decode_start[1]) + 3])
+        b = r.rows(TENSOR_K, 1, [7, int(r.decode_start[1]) + 3])
+        assert np.array_equal(a, b)
