@@ -17,28 +17,38 @@
 // chunk still see).
 //
 // Attention kernel.  A workgroup of 4 waves takes one (sequence, kv head) and
-// a block of 64 / g tokens, i.e. up to 64 query rows (row rho = g * token +
-// head, wave w owning rows 16w .. 16w + 15), and streams the keys of the ring
-// and then of the chunk in tiles of 32, double-buffered in LDS (the next
-// tile's loads are in flight while the current one is used).  Per tile and
-// wave, with v_mfma_f32_16x16x32 (A: lane l holds A[l % 16][8(l / 16) .. +7],
-// B: lane l holds B[8(l / 16) .. +7][l % 16], D: lane l register r holds
-// D[4(l / 16) + r][l % 16]):
+// a block of 128 / g tokens, i.e. up to 128 query rows (row rho = g * token +
+// head; wave w owns the two 16-row blocks 32w .. 32w + 31), and streams the
+// keys of the ring and then of the chunk in tiles of 64, double-buffered in
+// LDS (the next tile's loads are in flight while the current one is used).
+// Per tile and wave, with v_mfma_f32_16x16x32 (A: lane l holds
+// A[l % 16][8(l / 16) .. +7], B: lane l holds B[8(l / 16) .. +7][l % 16],
+// D: lane l register r holds D[4(l / 16) + r][l % 16]):
 //   S^T = K Q^T in bf16 (exact products, fp32 accumulation): A = 16 keys of
-//         the tile from LDS (chunk c of key r stored at c ^ (r & 15), so the
-//         16 lanes of a row read 16 different bank groups), B = the wave's 16
-//         query rows (registers).  Lane l holds the scores of query row
-//         l % 16 for keys 4(l / 16) + r of each 16-key half.
-//   mask, online softmax per query row (its 8 scores per lane, then the four
-//         lanes of the column), P = 2^(x - m).
-//   O^T += V^T P^T in fp16 with fp32 accumulation: B = P^T, the lane's own 8
-//         probabilities, if the keys of the PV product are taken in the order
-//         kappa = 8 (r / 4) + 4 (key / 16) + r % 4 (r = key % 16) -- the
-//         order the lane holds them in; A = V^T in that key order, which the
-//         tile loader writes to LDS transposed (and converted to fp16) so a
-//         lane reads its operand with one 16-byte access.  P and V in fp16
-//         (11-bit significands) keep the rounding of P well inside the
-//         tolerance; fp16's range limits |V| to below 65504.
+//         the tile from LDS, B = 16 query rows (registers); every K operand
+//         read from LDS serves both row blocks.  Lane l holds the scores of
+//         query row l % 16 for keys 16 kb + 4(l / 16) + r.
+//   mask (only in tiles that some row sees partly), online softmax per query
+//         row: its 16 scores per lane, then the four lanes of the column.  The
+//         running maximum m is raised only when a tile's maximum exceeds it by
+//         more than 8 (log2 units), so the accumulators are rescaled rarely;
+//         P = 2^(s c - m) <= 2^8 stays well inside fp16.
+//   O^T += V^T P^T in fp16 with fp32 accumulation: B = P^T, the lane's own
+//         probabilities, if the 32 keys of each product are taken in the order
+//         kappa = 8 ((key % 16) / 4) + 4 (key / 16) + key % 4 -- the order the
+//         lane holds them in; A = V^T in that key order, written to LDS
+//         transposed (and converted to fp16) by the tile loader.  A ninth
+//         product with A = ones gives the row sums of the same fp16 P.  P and
+//         V in fp16 (11-bit significands) keep the rounding of P well inside
+//         the tolerance; fp16's range limits |V| to below 65504.
+// LDS layouts (16-byte units u of a row, stored at u ^ swizzle(row), so that
+// the lanes of every read and write reach distinct banks and each lane's
+// read addresses differ only by constants): K [64 keys][16 units], swizzle
+// key % 16; V^T [128 dims][8 units], swizzle (d ^ (d / 4)) % 8.
+// Each tile carries two flags, set by the loader from the key positions and
+// the workgroup's first and last query positions: some key is not visible
+// to every row (mask needed), some key is visible to some row (else the tile
+// is skipped).
 // The workgroups of one (sequence, kv head) are placed on one XCD (XCD of a
 // workgroup = its index mod 8), so the tiles they all stream come through one
 // L2.
@@ -51,31 +61,41 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kKSteps = kD / 32;
-constexpr int kKeys = 32;            // keys per tile
+constexpr int kKSteps = kD / 32;     // k-steps of one S^T product
+constexpr int kKeys = 64;            // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 16 * kWaves;   // query rows per workgroup
-constexpr int kVtStride = 40;        // fp16 per transposed V row (32 keys + 8 of padding)
+constexpr int kRowBlocks = 2;        // 16-row blocks per wave
+constexpr int kRows = 16 * kRowBlocks * kWaves;  // query rows per workgroup
 constexpr int kXcds = 8;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kRescaleSlack = 8.f;  // log2 units
 
 struct Tile {
-  uint4 k[kKeys * 16];                                // K: chunk c of key r at r * 16 + (c ^ (r & 15))
-  __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];  // V^T in fp16: [dim][kappa]
-  int32_t pos[kKeys];                                 // key positions, -1: no key
+  u32x4_t k[kKeys * 16];  // K (bf16): unit c of key r at r * 16 + (c ^ (r % 16))
+  u32x4_t vt[kD * 8];     // V^T (fp16): unit u of dim d at d * 8 + (u ^ vt_swizzle(d))
+  int32_t pos[kKeys];    // key positions, -1: no key
 };
 
-__device__ __forceinline__ int kappa(int key) {
-  return 8 * ((key & 15) >> 2) + 4 * (key >> 4) + (key & 3);
+__device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 2)) & 7; }
+
+// The bf16 in the low (hi = false) or high half of w, as a float.
+__device__ __forceinline__ float bf16_half_to_f32(uint32_t w, bool hi) {
+  return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
 }
 
-__device__ __forceinline__ uint16_t f16_bits_from_bf16(uint16_t x) {
-  const _Float16 h = static_cast<_Float16>(bf16_to_f32(x));
-  return __builtin_bit_cast(uint16_t, h);
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to fp16 (round to nearest even), lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
 __global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) {
@@ -118,7 +138,7 @@ __global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) 
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int TB = kRows / G;  // tokens per workgroup
   __shared__ Tile tiles[2];
 
@@ -127,12 +147,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int xcd = blockIdx.x % kXcds;
   const int kx = blockIdx.x / kXcds;
   const int unit = (kx / p.token_blocks) * kXcds + xcd;
-  const int tb = kx % p.token_blocks;
+  const int tblk = kx % p.token_blocks;
   if (unit >= p.batch * p.num_kv_heads) return;
   const int b = unit / p.num_kv_heads;
   const int kvh = unit - b * p.num_kv_heads;
   const int T = p.n_tokens;
-  const int j0 = tb * TB;
+  const int j0 = tblk * TB;
   if (j0 >= T) return;
   const int j_last = min(j0 + TB, T) - 1;
 
@@ -141,22 +161,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int lane = tid & 63;
   const int lq = lane >> 4;
   const int lc = lane & 15;
-  const int rho = 16 * wave + lc;  // this lane's query row
-  const int jr = j0 + rho / G;
-  const int hr = rho % G;
-  const bool row_ok = rho < TB * G && jr < T;
   const int32_t p0 = p.pos[b];
-  const int64_t t_row = static_cast<int64_t>(p0) + jr;  // the row's query position
-  const size_t qrow = (static_cast<size_t>(b) * T + jr) * p.num_q_heads +
-                      static_cast<size_t>(kvh) * G + hr;
+  const int64_t t_first = static_cast<int64_t>(p0) + j0;  // query positions of the block
+  const int64_t t_last = static_cast<int64_t>(p0) + j_last;
 
-  // B operand of S^T: the wave's 16 query rows.
-  bf16x8_t qop[kKSteps];
+  // This lane's query row in each row block.  t_row = -1: the row sees no
+  // key (no such row, or its position is negative or beyond 2^31 - 1).
+  bool row_ok[kRowBlocks];
+  int32_t t_row[kRowBlocks], t_win[kRowBlocks];
+  size_t qrow[kRowBlocks];
+  bf16x8_t qop[kRowBlocks][kKSteps];  // B operand of S^T
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s) {
-    Vec16 v{};
-    if (row_ok) v = load16(static_cast<const uint16_t*>(p.q_rot) + qrow * kD + 32 * s + 8 * lq);
-    qop[s] = __builtin_bit_cast(bf16x8_t, v);
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    const int rho = 32 * wave + 16 * rb + lc;
+    const int jr = j0 + rho / G;
+    row_ok[rb] = rho < TB * G && jr < T;
+    const int64_t t = static_cast<int64_t>(p0) + jr;
+    t_row[rb] = row_ok[rb] && t >= 0 && t <= INT32_MAX ? static_cast<int32_t>(t) : -1;
+    t_win[rb] = t_row[rb] - p.window;  // no overflow: window <= 2^31 - 1
+    qrow[rb] = (static_cast<size_t>(b) * T + jr) * p.num_q_heads +
+               static_cast<size_t>(kvh) * G + rho % G;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+      Vec16 v{};
+      if (row_ok[rb])
+        v = load16(static_cast<const uint16_t*>(p.q_rot) + qrow[rb] * kD + 32 * s + 8 * lq);
+      qop[rb][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
 
   // Keys: ring slots 0 .. slots-1, then chunk rows 0 .. j_last.
@@ -164,66 +195,124 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int n_tiles = (n_keys + kKeys - 1) / kKeys;
   const size_t ring_row0 = static_cast<size_t>(unit) * p.slots;  // row (b, kvh, slot 0)
   const int32_t* sp = p.slot_pos + static_cast<size_t>(b) * p.slots;
+  const size_t chunk_row0 = static_cast<size_t>(b) * T * p.num_kv_heads + kvh;
+  const size_t chunk_stride = static_cast<size_t>(p.num_kv_heads) * kD;  // elements per chunk row
 
-  // Tile loader: thread tid moves 16-byte chunk tid % 16 of keys tid / 16 and
-  // tid / 16 + 16, of K and of V; the thread with chunk 0 also moves the two
-  // keys' positions.
-  const int part = tid & 15;
-  Vec16 kreg[2], vreg[2];
-  int32_t kp[2];
+  // Tile loader.  K: thread moves 16-byte unit kpart = tid % 16 of keys
+  // kq + 16e (kq = tid / 16, e < 4).  V: thread moves dims 4 vd .. 4 vd + 3
+  // (vd = tid % 32) of the eight keys whose kappa positions in PV chunk vc
+  // are 8 vj .. 8 vj + 7 (tid / 32 = 4 vc + vj): keys 32 vc + 4 vj + i and
+  // 32 vc + 16 + 4 vj + i (i < 4); the threads with vd = 0 also move those
+  // keys' positions and set the tile's flags.
+  const int kpart = tid & 15;
+  const int kq = tid >> 4;
+  const int vd = tid & 31;
+  const int vc = tid >> 7;
+  const int vj = (tid >> 5) & 3;
+  u32x4_t kreg[4];
+  u32x2_t vreg[8];
+  int32_t vpos[8];
+  auto v_key = [&](int i) { return 32 * vc + 16 * (i >> 2) + 4 * vj + (i & 3); };
   auto load = [&](int tile) {
+    const int base = tile * kKeys;
+    if (base + kKeys <= p.slots) {  // the whole tile from the ring (uniform branch)
+      const uint16_t* kr = static_cast<const uint16_t*>(p.k_cache) + (ring_row0 + base) * kD;
+      const uint16_t* vr = static_cast<const uint16_t*>(p.v_cache) + (ring_row0 + base) * kD;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = (tid >> 4) + 16 * e;
-      const int kk = tile * kKeys + key;
-      kreg[e] = Vec16{};
-      vreg[e] = Vec16{};
-      kp[e] = -1;
-      if (kk < p.slots) {
-        const size_t off = (ring_row0 + kk) * kD + 8 * part;
-        kreg[e] = load16(static_cast<const uint16_t*>(p.k_cache) + off);
-        vreg[e] = load16(static_cast<const uint16_t*>(p.v_cache) + off);
-        const int32_t pp = sp[kk];
-        kp[e] = pp < p0 ? pp : -1;  // a position the chunk brings again is taken from the chunk
-      } else if (kk < n_keys) {
-        const int i = kk - p.slots;
-        const size_t off =
-            ((static_cast<size_t>(b) * T + i) * p.num_kv_heads + kvh) * kD + 8 * part;
-        kreg[e] = load16(static_cast<const uint16_t*>(p.k_rot) + off);
-        vreg[e] = load16(static_cast<const uint16_t*>(p.v_new) + off);
-        const int64_t pp = static_cast<int64_t>(p0) + i;
-        kp[e] = pp >= 0 && pp <= INT32_MAX ? static_cast<int32_t>(pp) : -1;
+      for (int e = 0; e < 4; ++e)
+        kreg[e] = *reinterpret_cast<const u32x4_t*>(kr + (kq + 16 * e) * kD + 8 * kpart);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        vreg[i] = *reinterpret_cast<const u32x2_t*>(vr + v_key(i) * kD + 4 * vd);
+        const int32_t rp = sp[base + v_key(i)];
+        vpos[i] = (rp >= 0) & (rp < p0) ? rp : -1;  // a later position comes from the chunk
       }
+      return;
+    }
+    // Ring rows, chunk rows, and past the end the last chunk row (absent key).
+    auto row = [&](int kk, const void* ring, const void* chunk) {
+      const int i = min(max(kk - p.slots, 0), j_last);
+      const uint16_t* r = static_cast<const uint16_t*>(ring) + (ring_row0 + kk) * kD;
+      const uint16_t* c = static_cast<const uint16_t*>(chunk) + chunk_row0 * kD + i * chunk_stride;
+      return kk < p.slots ? r : c;
+    };
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      kreg[e] = *reinterpret_cast<const u32x4_t*>(row(base + kq + 16 * e, p.k_cache, p.k_rot) +
+                                                  8 * kpart);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = base + v_key(i);
+      vreg[i] = *reinterpret_cast<const u32x2_t*>(row(kk, p.v_cache, p.v_new) + 4 * vd);
+      const int32_t rp = sp[min(kk, p.slots - 1)];
+      const int64_t cp = static_cast<int64_t>(p0) + (kk - p.slots);
+      const bool ring_ok = (rp >= 0) & (rp < p0);
+      const bool chunk_ok = (kk < n_keys) & (cp >= 0) & (cp <= INT32_MAX);
+      vpos[i] = kk < p.slots ? (ring_ok ? rp : -1) : (chunk_ok ? static_cast<int32_t>(cp) : -1);
     }
   };
   auto store = [&](int buf) {
     Tile& t = tiles[buf];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = (tid >> 4) + 16 * e;
-      t.k[key * 16 + (part ^ (key & 15))] =
-          make_uint4(kreg[e].w[0], kreg[e].w[1], kreg[e].w[2], kreg[e].w[3]);
-      const int kap = kappa(key);
-      // An empty slot's V bytes are whatever the allocation held; its weight is
-      // 0, but 0 * NaN is not, so such rows enter P V as zeros.
-      const bool live = kp[e] >= 0;
+    for (int e = 0; e < 4; ++e) t.k[(kq + 16 * e) * 16 + (kpart ^ kq)] = kreg[e];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t wv = live ? vreg[e].w[q] : 0u;
-        t.vt[(8 * part + 2 * q) * kVtStride + kap] = f16_bits_from_bf16(static_cast<uint16_t>(wv));
-        t.vt[(8 * part + 2 * q + 1) * kVtStride + kap] =
-            f16_bits_from_bf16(static_cast<uint16_t>(wv >> 16));
+    for (int r = 0; r < 4; ++r) {
+      const int d = 4 * vd + r;
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a = vpos[2 * m] >= 0 ? (r < 2 ? vreg[2 * m].x : vreg[2 * m].y) : 0u;
+        const uint32_t c = vpos[2 * m + 1] >= 0 ? (r < 2 ? vreg[2 * m + 1].x : vreg[2 * m + 1].y)
+                                                : 0u;
+        w[m] = pack_f16x2(bf16_half_to_f32(a, r & 1), bf16_half_to_f32(c, r & 1));
       }
-      if (part == 0) t.pos[key] = kp[e];
+      t.vt[d * 8 + ((4 * vc + vj) ^ vt_swizzle(d))] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    if (vd == 0) {
+      *reinterpret_cast<i32x4_t*>(&t.pos[32 * vc + 4 * vj]) =
+          i32x4_t{vpos[0], vpos[1], vpos[2], vpos[3]};
+      *reinterpret_cast<i32x4_t*>(&t.pos[32 * vc + 16 + 4 * vj]) =
+          i32x4_t{vpos[4], vpos[5], vpos[6], vpos[7]};
     }
   };
 
-  const float c = p.score_scale_log2;
-  float m = kNegInf;  // running max of this lane's row (log2 units)
-  float lsum = 0.f;   // this lane's share of the row's running sum
-  f32x4_t acc[kD / 16];
+  // Per-lane LDS read offsets (in uint4 units) of the MFMA A operands.
+  int k_off[kKSteps];
 #pragma unroll
-  for (int blk = 0; blk < kD / 16; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kKSteps; ++s) k_off[s] = lc * 16 + ((4 * s + lq) ^ lc);
+  const int vt_g = (lc ^ (lc >> 2)) & 7;
+  const int vt_off[2] = {lc * 8 + ((0 + lq) ^ vt_g), lc * 8 + ((4 + lq) ^ vt_g)};
+
+  const float c = p.score_scale_log2;
+  float m[kRowBlocks];   // running maximum of the row's scaled scores (log2 units)
+  f32x4_t acc[kRowBlocks][kD / 16 + 1];  // O^T blocks, then the row sums
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    m[rb] = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk <= kD / 16; ++blk) acc[rb][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  f16x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<_Float16>(1.f);
+
+  // A key at position kp (-1: none) is visible to every query row of the
+  // workgroup iff it lies in [0, all_a] or [all_b, t_first], and to some row
+  // iff it lies in [0, any_a] or [any_b, t_last] (sinks, then the window;
+  // empty intervals have a < 0 or b > end).
+  const int64_t sink_end = static_cast<int64_t>(p.sinks) - 1;
+  const int32_t t_lo = static_cast<int32_t>(min<int64_t>(max<int64_t>(t_first, -1), INT32_MAX));
+  const int32_t t_hi = static_cast<int32_t>(min<int64_t>(max<int64_t>(t_last, -1), INT32_MAX));
+  const int32_t all_a = static_cast<int32_t>(min<int64_t>(t_lo, sink_end));
+  const int32_t any_a = static_cast<int32_t>(min<int64_t>(t_hi, sink_end));
+  const int32_t all_b = static_cast<int32_t>(
+      min<int64_t>(max<int64_t>(t_last - p.window + 1, 0), static_cast<int64_t>(INT32_MAX)));
+  const int32_t any_b = static_cast<int32_t>(
+      min<int64_t>(max<int64_t>(t_first - p.window + 1, 0), static_cast<int64_t>(INT32_MAX)));
+  auto in = [](int32_t x, int32_t a, int32_t b) {  // a <= x <= b (x >= -1, a >= 0)
+    const uint32_t ua = static_cast<uint32_t>(a);
+    return b >= a && static_cast<uint32_t>(x) - ua <= static_cast<uint32_t>(b) - ua;
+  };
 
   load(0);
   store(0);
@@ -232,79 +321,128 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int cur = it & 1;
     if (it + 1 < n_tiles) load(it + 1);
     const Tile& t = tiles[cur];
-
-    // S^T for the two 16-key halves
-    f32x4_t d[2];
+    // Tile flags from the 64 key positions, one per lane: bit 0 some key is
+    // not visible to every row (mask needed), bit 1 some key is visible.
+    const int32_t kp_l = t.pos[lane];
+    const bool all_l = in(kp_l, 0, all_a) || in(kp_l, all_b, t_lo);
+    const bool any_l = in(kp_l, 0, any_a) || in(kp_l, any_b, t_hi);
+    const int flags = (__ballot(!all_l) != 0 ? 1 : 0) | (__ballot(any_l) != 0 ? 2 : 0);
+    if (flags & 2) {
+      // S^T for the four 16-key blocks of the tile, both row blocks
+      f32x4_t sc[kRowBlocks][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      d[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const uint4 a = t.k[(16 * kb + lc) * 16 + ((4 * s + lq) ^ lc)];
-        d[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qop[s],
-                                                        d[kb], 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb) sc[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, t.k[k_off[s] + 256 * kb]);
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb)
+            sc[rb][kb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[rb][s], sc[rb][kb], 0, 0, 0);
+        }
+      if (flags & 1) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const i32x4_t kp = *reinterpret_cast<const i32x4_t*>(&t.pos[16 * kb + 4 * lq]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int rb = 0; rb < kRowBlocks; ++rb) {
+              const bool vis = (kp[r] >= 0) & (kp[r] <= t_row[rb]) &
+                               ((kp[r] < p.sinks) | (kp[r] > t_win[rb]));
+              sc[rb][kb][r] = vis ? sc[rb][kb][r] : kNegInf;
+            }
+        }
       }
+      // online softmax: tile maximum per row, rare rescale, P = 2^(s c - m)
+      float mt[kRowBlocks];
+      bool need[kRowBlocks];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        float x = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x = fmaxf(x, sc[rb][kb][r]);
+        x = fmaxf(x, __shfl_xor(x, 16));
+        x = fmaxf(x, __shfl_xor(x, 32));
+        mt[rb] = x * c;
+        need[rb] = mt[rb] > m[rb] + kRescaleSlack;
+      }
+      if (__any(need[0] | need[1])) {
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+          const float mn = need[rb] ? mt[rb] : m[rb];
+          const float alpha = need[rb] ? __builtin_amdgcn_exp2f(m[rb] - mn) : 1.f;
+#pragma unroll
+          for (int blk = 0; blk <= kD / 16; ++blk) acc[rb][blk] *= alpha;
+          m[rb] = mn;
+        }
+      }
+      f16x8_t pb[kRowBlocks][2];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const float mu = m[rb] == kNegInf ? 0.f : m[rb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            pb[rb][kb >> 1][4 * (kb & 1) + r] =
+                static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(sc[rb][kb][r], c, -mu)));
+      }
+      // O^T += V^T P^T, and the row sums
+#pragma unroll
+      for (int blk = 0; blk < kD / 16; ++blk)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const f16x8_t a =
+              __builtin_bit_cast(f16x8_t, t.vt[vt_off[pc ^ (blk & 1)] + 128 * blk]);
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb)
+            acc[rb][blk] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[rb][pc], acc[rb][blk], 0, 0, 0);
+        }
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+          acc[rb][kD / 16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rb][pc],
+                                                                    acc[rb][kD / 16], 0, 0, 0);
     }
-    // mask and running max of the lane's row
-    float x[2][4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t kpos = t.pos[16 * kb + 4 * lq + r];
-        const bool vis = row_ok && kpos >= 0 && kpos <= t_row &&
-                         (kpos < p.sinks || kpos > t_row - p.window);
-        x[kb][r] = vis ? d[kb][r] * c : kNegInf;
-        tmax = fmaxf(tmax, x[kb][r]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
-    m = mn;
-    f16x8_t pb;
-    float tsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = x[kb][r] == kNegInf ? 0.f : exp2f(x[kb][r] - mn);
-        tsum += pr;
-        pb[4 * kb + r] = static_cast<_Float16>(pr);
-      }
-    lsum = lsum * alpha + tsum;
-    // O^T = O^T * alpha + V^T P^T
-#pragma unroll
-    for (int blk = 0; blk < kD / 16; ++blk) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&t.vt[(16 * blk + lc) * kVtStride + 8 * lq]);
-      f32x4_t o = acc[blk] * alpha;
-      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), pb, o,
-                                                        0, 0, 0);
-    }
-    if (it + 1 < n_tiles) store(cur ^ 1);  // that buffer was last read before the barrier below
+    if (it + 1 < n_tiles) store(cur ^ 1);  // that buffer was last read in tile it - 1
     __syncthreads();
   }
 
-  // Row totals over the four lanes of the column, then out = O / l.
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (!row_ok) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // out = O / l
 #pragma unroll
-  for (int blk = 0; blk < kD / 16; ++blk) {
-    const size_t at = qrow * kD + 16 * blk + 4 * lq;
-    if (p.out_bf16) {
-      uint16_t* o = static_cast<uint16_t*>(p.out) + at;
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    if (!row_ok[rb]) continue;
+    const float l = acc[rb][kD / 16][0];
+    const bool seen = t_row[rb] >= 0 && l > 0.f;
+    const float inv = seen ? 1.f / l : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_rne(acc[blk][r] * inv);
-    } else {
-      float* o = static_cast<float*>(p.out) + at;
-      *reinterpret_cast<float4*>(o) =
-          make_float4(acc[blk][0] * inv, acc[blk][1] * inv, acc[blk][2] * inv, acc[blk][3] * inv);
+    for (int blk = 0; blk < kD / 16; ++blk) {
+      const size_t at = qrow[rb] * kD + 16 * blk + 4 * lq;
+      const f32x4_t o = acc[rb][blk] * inv;
+      if (p.out_bf16) {
+        uint16_t* dst = static_cast<uint16_t*>(p.out) + at;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(static_cast<uint32_t>(f32_to_bf16_rne(o[0])) |
+                           (static_cast<uint32_t>(f32_to_bf16_rne(o[1])) << 16),
+                       static_cast<uint32_t>(f32_to_bf16_rne(o[2])) |
+                           (static_cast<uint32_t>(f32_to_bf16_rne(o[3])) << 16));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + at) =
+            make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
+    if (p.lse != nullptr && lq == 0)
+      p.lse[qrow[rb]] = seen ? (m[rb] + __log2f(l)) * kLn2 : kNegInf;
   }
-  if (p.lse != nullptr && lq == 0) p.lse[qrow] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : kNegInf;
 }
 
 }  // namespace
@@ -328,6 +466,8 @@ hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream) {
   rotate_chunk_kernel<<<static_cast<unsigned>(grid), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
+
+int prefill_tokens_per_block(int group) { return kRows / group; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int units = p.batch * p.num_kv_heads;

@@ -410,7 +410,7 @@ swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_
   p.slots = cfg.num_sinks + cfg.window;
   p.sinks = cfg.num_sinks;
   p.window = cfg.window;
-  const int32_t tokens_per_wg = 64 / (num_q_heads / cfg.num_kv_heads);
+  const int32_t tokens_per_wg = swa::prefill_tokens_per_block(num_q_heads / cfg.num_kv_heads);
   p.token_blocks = (n_tokens + tokens_per_wg - 1) / tokens_per_wg;
   p.score_scale_log2 = resolve_scale(scale, cfg.head_dim);
   p.out = out;

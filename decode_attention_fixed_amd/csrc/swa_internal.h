@@ -173,6 +173,8 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t n_tokens);
+// Tokens of one attention workgroup for a group of g = Hq / Hkv query heads.
+int prefill_tokens_per_block(int group);
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
