@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
   const int d = p.head_dim;
   const int half = d / 2;
   const int slots = p.sinks + p.window;
-  const int k_items = p.num_kv_heads * half;
+  const bool k_copy = p.k_rotated != nullptr;
+  const int k_items = k_copy ? 0 : p.num_kv_heads * half;
   const int q_items = p.q_inout != nullptr ? p.num_q_heads * half : 0;
   // A later token of this call lands in the same ring slot: leave it the slot.
   const bool overwritten = pos >= p.sinks && j + p.window <= p.n_tokens - 1;
@@ -139,17 +140,22 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
     return;
   }
   if (overwritten) return;
-  // V: 16-byte chunks of the token's Hkv rows
+  // V (then the pre-rotated K rows): 16-byte chunks of the token's Hkv rows
   const int per_row = d * static_cast<int>(sizeof(T)) / 16;
-  const int w = item - k_items - q_items;
+  int w = item - k_items - q_items;
+  const bool is_v = w < p.num_kv_heads * per_row;
+  if (!is_v) w -= p.num_kv_heads * per_row;
   const int h = w / per_row;
   const int c = w - h * per_row;
   const uint4* src = reinterpret_cast<const uint4*>(
-      static_cast<const T*>(p.v_new) +
+      static_cast<const T*>(is_v ? p.v_new : p.k_rotated) +
       ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_kv_heads + h) * d);
   uint4* dst = reinterpret_cast<uint4*>(
-      static_cast<T*>(p.v_cache) + ((static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot) * d);
+      static_cast<T*>(is_v ? p.v_cache : p.k_cache) +
+      ((static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot) * d);
   dst[c] = src[c];
+  if (k_copy && !is_v && w == 0)
+    p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
 }
 
 template <bool BF16>
@@ -207,8 +213,10 @@ hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t st
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
   const int half = p.head_dim / 2;
   const int elem = p.bf16 ? 2 : 4;
-  const int items = p.num_kv_heads * half + (p.q_inout != nullptr ? p.num_q_heads * half : 0) +
-                    p.num_kv_heads * (p.head_dim * elem / 16);
+  const int copies = p.k_rotated != nullptr ? 2 : 1;  // V, and K when it is copied
+  const int items = (p.k_rotated != nullptr ? 0 : p.num_kv_heads * half) +
+                    (p.q_inout != nullptr ? p.num_q_heads * half : 0) +
+                    copies * p.num_kv_heads * (p.head_dim * elem / 16);
   const int wgs = (items + kAppendThreads - 1) / kAppendThreads;
   const size_t grid = static_cast<size_t>(p.batch) * p.n_tokens * wgs;
   if (grid > 0x7fffffffu) return hipErrorInvalidValue;

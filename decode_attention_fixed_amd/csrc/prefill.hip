@@ -98,43 +98,48 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
+// Rotation of the chunk: one thread per (token, pair i) forms the angle once
+// and rotates pair i of every query and key head of the token (rounding as
+// the append kernel: f64 rotation, one rounding to bf16).
 __global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) {
   constexpr int kHalf = kD / 2;
-  const int heads = p.num_q_heads + p.num_kv_heads;
-  const int64_t items = static_cast<int64_t>(p.batch) * p.n_tokens * heads * kHalf;
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (w >= items) return;
-  const int i = static_cast<int>(w % kHalf);
-  const int64_t row = w / kHalf;  // (b, j, head)
-  const int h = static_cast<int>(row % heads);
-  const int64_t bj = row / heads;
-  const int b = static_cast<int>(bj / p.n_tokens);
-  const int j = static_cast<int>(bj - static_cast<int64_t>(b) * p.n_tokens);
+  const int64_t token = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // b * T + j
+  if (token >= static_cast<int64_t>(p.batch) * p.n_tokens) return;
+  const int i = threadIdx.x & 63;
+  const int b = static_cast<int>(token / p.n_tokens);
+  const int j = static_cast<int>(token - static_cast<int64_t>(b) * p.n_tokens);
   const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
-  const uint16_t* src;
-  uint16_t* dst;
-  if (h < p.num_q_heads) {
-    const size_t off = (static_cast<size_t>(bj) * p.num_q_heads + h) * kD;
-    src = static_cast<const uint16_t*>(p.q) + off;
-    dst = static_cast<uint16_t*>(p.q_rot) + off;
-  } else {
-    const size_t off = (static_cast<size_t>(bj) * p.num_kv_heads + (h - p.num_q_heads)) * kD;
-    src = static_cast<const uint16_t*>(p.k) + off;
-    dst = static_cast<uint16_t*>(p.k_rot) + off;
-  }
-  const int i0 = p.rope_half ? i : 2 * i;
-  const int i1 = p.rope_half ? i + kHalf : 2 * i + 1;
-  uint16_t o0 = src[i0], o1 = src[i1];
-  if (pos >= 0 && pos <= INT32_MAX) {  // a token at a negative position is never attended
-    double sn, cs, x0, x1;
-    rope_sincos(static_cast<double>(pos), p.freq.theta[i], &sn, &cs);
-    rope_rotate_pair(static_cast<double>(bf16_to_f32(o0)), static_cast<double>(bf16_to_f32(o1)),
-                     cs, sn, &x0, &x1);
-    o0 = f64_to_bf16_rne(x0);
-    o1 = f64_to_bf16_rne(x1);
-  }
-  dst[i0] = o0;
-  dst[i1] = o1;
+  const bool rot = pos >= 0 && pos <= INT32_MAX;  // a token at such a position is never attended
+  double sn = 0.0, cs = 1.0;
+  if (rot) rope_sincos(static_cast<double>(pos), p.freq.theta[i], &sn, &cs);
+  auto rotate = [&](uint16_t& a, uint16_t& c) {
+    if (!rot) return;
+    double x0, x1;
+    rope_rotate_pair(static_cast<double>(bf16_to_f32(a)), static_cast<double>(bf16_to_f32(c)), cs,
+                     sn, &x0, &x1);
+    a = f64_to_bf16_rne(x0);
+    c = f64_to_bf16_rne(x1);
+  };
+  auto rows = [&](const void* src, void* dst, int heads) {
+    const size_t row0 = static_cast<size_t>(token) * heads;
+    for (int h = 0; h < heads; ++h) {
+      const uint16_t* sr = static_cast<const uint16_t*>(src) + (row0 + h) * kD;
+      uint16_t* dr = static_cast<uint16_t*>(dst) + (row0 + h) * kD;
+      if (p.rope_half) {  // pairs (i, i + d/2)
+        uint16_t a = sr[i], c = sr[i + kHalf];
+        rotate(a, c);
+        dr[i] = a;
+        dr[i + kHalf] = c;
+      } else {            // pairs (2i, 2i + 1), one 32-bit word
+        const uint32_t w = reinterpret_cast<const uint32_t*>(sr)[i];
+        uint16_t a = static_cast<uint16_t>(w), c = static_cast<uint16_t>(w >> 16);
+        rotate(a, c);
+        reinterpret_cast<uint32_t*>(dr)[i] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
+      }
+    }
+  };
+  rows(p.q, p.q_rot, p.num_q_heads);
+  rows(p.k, p.k_rot, p.num_kv_heads);
 }
 
 template <int G>
@@ -459,9 +464,8 @@ PrefillLayout prefill_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_
 }
 
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(p.batch) * p.n_tokens *
-                        (p.num_q_heads + p.num_kv_heads) * (kD / 2);
-  const int64_t grid = (items + 255) / 256;
+  const int64_t tokens = static_cast<int64_t>(p.batch) * p.n_tokens;
+  const int64_t grid = (tokens + 3) / 4;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   rotate_chunk_kernel<<<static_cast<unsigned>(grid), 256, 0, stream>>>(p);
   return hipGetLastError();

@@ -424,6 +424,7 @@ swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_
   a.v_new = v_new;
   a.pos = pos;
   a.q_inout = nullptr;
+  a.k_rotated = r.k_rot;  // rotated by the first launch exactly as the append would
   a.k_cache = cache->k;
   a.v_cache = cache->v;
   a.slot_pos = cache->slot_pos;
