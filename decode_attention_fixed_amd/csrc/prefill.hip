@@ -85,6 +85,38 @@ struct Tile {
 
 __device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 2)) & 7; }
 
+// Raw buffer resource over `bytes` bytes at `base` (loads beyond return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Loads that write LDS: lane l of the wave stores its 16 bytes at lds + 16 l
+// (lds is the same for the whole wave).
+__device__ __forceinline__ void buffer_load_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds,
+                                                     int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void global_load_to_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+// Waits until every vector memory load of the wave, those that write LDS
+// included, has completed.
+__device__ __forceinline__ void wait_vector_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one
+// column of an MFMA result).  permlane16_swap(x, x) leaves in every lane the
+// pair {x of its own row, x of the neighbouring row} (rows of 16 lanes, 0-1
+// and 2-3 paired); permlane32_swap(x, x) the pair {x, x of the other half}.
+__device__ __forceinline__ float column_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 // The bf16 in the low (hi = false) or high half of w, as a float.
 __device__ __forceinline__ float bf16_half_to_f32(uint32_t w, bool hi) {
   return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
@@ -202,35 +234,76 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int32_t* sp = p.slot_pos + static_cast<size_t>(b) * p.slots;
   const size_t chunk_row0 = static_cast<size_t>(b) * T * p.num_kv_heads + kvh;
   const size_t chunk_stride = static_cast<size_t>(p.num_kv_heads) * kD;  // elements per chunk row
+  const uint32_t chunk_row_bytes = static_cast<uint32_t>(chunk_stride * 2);
+  const uint32_t ring_bytes = static_cast<uint32_t>(p.slots) * kD * 2;
+  const uint32_t chunk_bytes = static_cast<uint32_t>(T - 1) * chunk_row_bytes + kD * 2;
+  const __amdgpu_buffer_rsrc_t k_ring =
+      buffer_rsrc(static_cast<const uint16_t*>(p.k_cache) + ring_row0 * kD, ring_bytes);
+  const __amdgpu_buffer_rsrc_t v_ring =
+      buffer_rsrc(static_cast<const uint16_t*>(p.v_cache) + ring_row0 * kD, ring_bytes);
+  const __amdgpu_buffer_rsrc_t sp_ring = buffer_rsrc(sp, static_cast<uint32_t>(p.slots) * 4);
+  const __amdgpu_buffer_rsrc_t k_chunk =
+      buffer_rsrc(static_cast<const uint16_t*>(p.k_rot) + chunk_row0 * kD, chunk_bytes);
+  const __amdgpu_buffer_rsrc_t v_chunk =
+      buffer_rsrc(static_cast<const uint16_t*>(p.v_new) + chunk_row0 * kD, chunk_bytes);
 
-  // Tile loader.  K: thread moves 16-byte unit kpart = tid % 16 of keys
-  // kq + 16e (kq = tid / 16, e < 4).  V: thread moves dims 4 vd .. 4 vd + 3
+  // Tile loader.  K goes straight from memory to LDS (loads that write LDS:
+  // lane l of a wave's instruction fills the 16 bytes at the wave's LDS base
+  // + 16 l): instruction e of wave w fills K rows 16 e + 4 w .. + 3, so lane
+  // (kq = tid / 16, kpart = tid % 16) fills physical unit kpart of key row
+  // kq + 16 e, i.e. fetches that row's logical unit kpart ^ kq.  V: thread
+  // moves dims 4 vd .. 4 vd + 3
   // (vd = tid % 32) of the eight keys whose kappa positions in PV chunk vc
   // are 8 vj .. 8 vj + 7 (tid / 32 = 4 vc + vj): keys 32 vc + 4 vj + i and
-  // 32 vc + 16 + 4 vj + i (i < 4); the threads with vd = 0 also move those
-  // keys' positions and set the tile's flags.
+  // 32 vc + 16 + 4 vj + i (i < 4), and their positions.  Tiles wholly in the
+  // ring or wholly in the chunk's rows take the per-tile offset in a scalar
+  // register (buffer loads); the others form each row's address.
   const int kpart = tid & 15;
   const int kq = tid >> 4;
   const int vd = tid & 31;
   const int vc = tid >> 7;
   const int vj = (tid >> 5) & 3;
-  u32x4_t kreg[4];
+  const int vkey0 = 32 * vc + 4 * vj;
+  const int k_unit = kpart ^ kq;  // logical unit of K that this lane fetches
   u32x2_t vreg[8];
   int32_t vpos[8];
-  auto v_key = [&](int i) { return 32 * vc + 16 * (i >> 2) + 4 * vj + (i & 3); };
+  auto v_key = [&](int i) { return vkey0 + 16 * (i >> 2) + (i & 3); };
   auto load = [&](int tile) {
     const int base = tile * kKeys;
+    u32x4_t* k_lds = &tiles[tile & 1].k[(4 * wave) * 16];  // this wave's rows 4w .. 4w + 3
     if (base + kKeys <= p.slots) {  // the whole tile from the ring (uniform branch)
-      const uint16_t* kr = static_cast<const uint16_t*>(p.k_cache) + (ring_row0 + base) * kD;
-      const uint16_t* vr = static_cast<const uint16_t*>(p.v_cache) + (ring_row0 + base) * kD;
+      const int sb = base * kD * 2;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        kreg[e] = *reinterpret_cast<const u32x4_t*>(kr + (kq + 16 * e) * kD + 8 * kpart);
+        buffer_load_to_lds16(k_ring, k_lds + 256 * e, kq * 256 + k_unit * 16, sb + 4096 * e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b64(v_ring, vkey0 * 256 + vd * 8 + (i & 3) * 256,
+                                                       sb + 4096 * (i >> 2), 0);
+      const i32x4_t r0 = __builtin_bit_cast(
+          i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp_ring, vkey0 * 4, base * 4, 0));
+      const i32x4_t r1 = __builtin_bit_cast(
+          i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp_ring, vkey0 * 4 + 64, base * 4, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // a position at or after the chunk's start comes from the chunk
+        vpos[i] = ((r0[i] >= 0) & (r0[i] < p0)) ? r0[i] : -1;
+        vpos[4 + i] = ((r1[i] >= 0) & (r1[i] < p0)) ? r1[i] : -1;
+      }
+      return;
+    }
+    const int i0 = base - p.slots;  // chunk row of the tile's first key
+    if (i0 >= 0 && i0 + kKeys - 1 <= j_last) {  // the whole tile from the chunk (uniform)
+      const int sb = i0 * static_cast<int>(chunk_row_bytes);
+      const int rs = static_cast<int>(chunk_row_bytes);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        buffer_load_to_lds16(k_chunk, k_lds + 256 * e, kq * rs + k_unit * 16, sb + 16 * rs * e);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        vreg[i] = *reinterpret_cast<const u32x2_t*>(vr + v_key(i) * kD + 4 * vd);
-        const int32_t rp = sp[base + v_key(i)];
-        vpos[i] = (rp >= 0) & (rp < p0) ? rp : -1;  // a later position comes from the chunk
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b64(v_chunk, vkey0 * rs + vd * 8,
+                                                       sb + rs * (16 * (i >> 2) + (i & 3)), 0);
+        const int64_t cp = static_cast<int64_t>(p0) + i0 + v_key(i);
+        vpos[i] = ((cp >= 0) & (cp <= INT32_MAX)) ? static_cast<int32_t>(cp) : -1;
       }
       return;
     }
@@ -243,8 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     };
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      kreg[e] = *reinterpret_cast<const u32x4_t*>(row(base + kq + 16 * e, p.k_cache, p.k_rot) +
-                                                  8 * kpart);
+      global_load_to_lds16(row(base + kq + 16 * e, p.k_cache, p.k_rot) + 8 * k_unit,
+                           k_lds + 256 * e);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int kk = base + v_key(i);
@@ -258,17 +331,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   };
   auto store = [&](int buf) {
     Tile& t = tiles[buf];
+    // An absent key's V bytes are whatever the memory held; its weight is 0,
+    // but 0 * NaN is not, so such rows enter P V as zeros.
+    bool live = true;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t.k[(kq + 16 * e) * 16 + (kpart ^ kq)] = kreg[e];
+    for (int i = 0; i < 8; ++i) live &= vpos[i] >= 0;
+    if (!__all(live)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (vpos[i] < 0) vreg[i] = u32x2_t{0u, 0u};
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int d = 4 * vd + r;
       uint32_t w[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t a = vpos[2 * m] >= 0 ? (r < 2 ? vreg[2 * m].x : vreg[2 * m].y) : 0u;
-        const uint32_t c = vpos[2 * m + 1] >= 0 ? (r < 2 ? vreg[2 * m + 1].x : vreg[2 * m + 1].y)
-                                                : 0u;
+        const uint32_t a = r < 2 ? vreg[2 * m].x : vreg[2 * m].y;
+        const uint32_t c = r < 2 ? vreg[2 * m + 1].x : vreg[2 * m + 1].y;
         w[m] = pack_f16x2(bf16_half_to_f32(a, r & 1), bf16_half_to_f32(c, r & 1));
       }
       t.vt[d * 8 + ((4 * vc + vj) ^ vt_swizzle(d))] = u32x4_t{w[0], w[1], w[2], w[3]};
@@ -321,6 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
   load(0);
   store(0);
+  wait_vector_loads();  // the K rows written to LDS by the loads
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int cur = it & 1;
@@ -373,9 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) x = fmaxf(x, sc[rb][kb][r]);
-        x = fmaxf(x, __shfl_xor(x, 16));
-        x = fmaxf(x, __shfl_xor(x, 32));
-        mt[rb] = x * c;
+        mt[rb] = column_max(x) * c;
         need[rb] = mt[rb] > m[rb] + kRescaleSlack;
       }
       if (__any(need[0] | need[1])) {
@@ -419,6 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                                                                     acc[rb][kD / 16], 0, 0, 0);
     }
     if (it + 1 < n_tiles) store(cur ^ 1);  // that buffer was last read in tile it - 1
+    wait_vector_loads();
     __syncthreads();
   }
 

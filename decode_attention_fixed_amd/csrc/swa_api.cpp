@@ -365,6 +365,12 @@ swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_
   if (n_tokens < 1) return fail(SWA_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", n_tokens);
   if (static_cast<int64_t>(n_tokens) * cfg.batch * num_q_heads > INT32_MAX)
     return fail(SWA_ERR_INVALID_ARG, "batch * n_tokens * num_q_heads too large");
+  // The attention kernel addresses one sequence's ring rows and one chunk's
+  // rows of a kv head with 32-bit byte offsets.
+  if ((static_cast<int64_t>(cfg.num_sinks) + cfg.window) * cfg.head_dim * 2 > INT32_MAX ||
+      static_cast<int64_t>(n_tokens) * cfg.num_kv_heads * cfg.head_dim * 2 > INT32_MAX)
+    return fail(SWA_ERR_UNSUPPORTED, "prefill needs (S + W) * d * 2 and n_tokens * Hkv * d * 2 "
+                                     "below 2^31 bytes");
   if (!dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q, 16) || !aligned(out, 16) ||
       !aligned(pos, 4) || (lse != nullptr && !aligned(lse, 4)))

@@ -200,11 +200,12 @@ swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
  * [ring] §2.2), from the ring as it was before the call (positions below
  * pos[b]) and from the chunk itself (causal).  Afterwards the cache is in the
  * state kv_append_rope(cache, k_new, v_new, pos, n_tokens, NULL) leaves, bit
- * for bit.  A token at a negative position is neither attended nor appended;
- * its query row gets out = 0, lse = -inf.
+ * for bit.  A token at a negative position, or at one beyond 2^31 - 1, is
+ * neither attended nor appended; its query row gets out = 0, lse = -inf.
  *
- * Supported: bf16 caches with d = 128, Hq / Hkv in {1, 2, 3, 4, 6, 8}
- * (SWA_ERR_UNSUPPORTED otherwise).  The product P V runs in fp16 with fp32
+ * Supported: bf16 caches with d = 128, Hq / Hkv in {1, 2, 3, 4, 6, 8},
+ * (S + W) * 256 and n_tokens * Hkv * 256 below 2^31 (SWA_ERR_UNSUPPORTED
+ * otherwise).  The product P V runs in fp16 with fp32
  * accumulation: V must stay below 65504 in magnitude.  Three launches on
  * `stream` (rotation, attention, append); the call reads and then writes the
  * cache: do not read it concurrently. */
