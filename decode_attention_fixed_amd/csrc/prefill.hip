@@ -6,9 +6,9 @@
 // the sinks united with its window ([sink] cache formula; [ring] §2.2, the
 // current token included) -- taken from the ring as it was before the chunk
 // (positions < p0) and from the chunk itself (positions p0 .. t, causal
-// within the chunk; [pool] chunked prefill).  Then the chunk is appended as
-// kv_append_rope appends it.  Unlike a decode step this is compute-bound:
-// every key tile is used by a block of query rows.
+// within the chunk; [pool] "paging": prefill in chunks of 128-256 tokens).
+// Then the chunk is appended as kv_append_rope appends it.  Unlike a decode
+// step this is compute-bound: every key tile is used by a block of query rows.
 //
 // Three launches: (1) rotate the chunk's queries and K rows into the
 // workspace (angles and rounding of the append kernel), (2) the attention,
@@ -52,6 +52,8 @@
 // The workgroups of one (sequence, kv head) are placed on one XCD (XCD of a
 // workgroup = its index mod 8), so the tiles they all stream come through one
 // L2.
+#include <algorithm>
+
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -80,7 +82,7 @@ constexpr float kRescaleSlack = 8.f;  // log2 units
 struct Tile {
   u32x4_t k[kKeys * 16];  // K (bf16): unit c of key r at r * 16 + (c ^ (r % 16))
   u32x4_t vt[kD * 8];     // V^T (fp16): unit u of dim d at d * 8 + (u ^ vt_swizzle(d))
-  int32_t pos[kKeys];    // key positions, -1: no key
+  int32_t pos[kKeys];    // positions: ring slots as recorded, chunk rows p0 + i; -1: no key
 };
 
 __device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 2)) & 7; }
@@ -130,10 +132,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
-// Rotation of the chunk: one thread per (token, pair i) forms the angle once
-// and rotates pair i of every query and key head of the token (rounding as
-// the append kernel: f64 rotation, one rounding to bf16).
-__global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) {
+// Rotation of the chunk: one thread per (token, pair i, group of
+// `group_heads` heads) forms the angle once and rotates pair i of those heads
+// (query heads first, then key heads; rounding as the append kernel: f64
+// rotation, one rounding to bf16).  Small chunks split the heads into more
+// groups so that enough threads are in flight.
+__global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p, int group_heads) {
   constexpr int kHalf = kD / 2;
   const int64_t token = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // b * T + j
   if (token >= static_cast<int64_t>(p.batch) * p.n_tokens) return;
@@ -152,9 +156,10 @@ __global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) 
     a = f64_to_bf16_rne(x0);
     c = f64_to_bf16_rne(x1);
   };
-  auto rows = [&](const void* src, void* dst, int heads) {
+  const int h0 = blockIdx.y * group_heads;  // first head of this thread's group
+  auto rows = [&](const void* src, void* dst, int heads, int first, int end) {
     const size_t row0 = static_cast<size_t>(token) * heads;
-    for (int h = 0; h < heads; ++h) {
+    for (int h = max(first, 0); h < min(end, heads); ++h) {
       const uint16_t* sr = static_cast<const uint16_t*>(src) + (row0 + h) * kD;
       uint16_t* dr = static_cast<uint16_t*>(dst) + (row0 + h) * kD;
       if (p.rope_half) {  // pairs (i, i + d/2)
@@ -170,8 +175,8 @@ __global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) 
       }
     }
   };
-  rows(p.q, p.q_rot, p.num_q_heads);
-  rows(p.k, p.k_rot, p.num_kv_heads);
+  rows(p.q, p.q_rot, p.num_q_heads, h0, h0 + group_heads);
+  rows(p.k, p.k_rot, p.num_kv_heads, h0 - p.num_q_heads, h0 + group_heads - p.num_q_heads);
 }
 
 template <int G>
@@ -285,9 +290,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const i32x4_t r1 = __builtin_bit_cast(
           i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp_ring, vkey0 * 4 + 64, base * 4, 0));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // a position at or after the chunk's start comes from the chunk
-        vpos[i] = ((r0[i] >= 0) & (r0[i] < p0)) ? r0[i] : -1;
-        vpos[4 + i] = ((r1[i] >= 0) & (r1[i] < p0)) ? r1[i] : -1;
+      for (int i = 0; i < 4; ++i) {  // raw slot positions (-1: empty)
+        vpos[i] = r0[i];
+        vpos[4 + i] = r1[i];
       }
       return;
     }
@@ -324,9 +329,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       vreg[i] = *reinterpret_cast<const u32x2_t*>(row(kk, p.v_cache, p.v_new) + 4 * vd);
       const int32_t rp = sp[min(kk, p.slots - 1)];
       const int64_t cp = static_cast<int64_t>(p0) + (kk - p.slots);
-      const bool ring_ok = (rp >= 0) & (rp < p0);
       const bool chunk_ok = (kk < n_keys) & (cp >= 0) & (cp <= INT32_MAX);
-      vpos[i] = kk < p.slots ? (ring_ok ? rp : -1) : (chunk_ok ? static_cast<int32_t>(cp) : -1);
+      vpos[i] = kk < p.slots ? rp : (chunk_ok ? static_cast<int32_t>(cp) : -1);
     }
   };
   auto store = [&](int buf) {
@@ -405,11 +409,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int cur = it & 1;
-    if (it + 1 < n_tiles) load(it + 1);
+    const bool more = it + 1 < n_tiles;
+    if (more) load(it + 1);
     const Tile& t = tiles[cur];
+    const int tile_base = it * kKeys;
+    // A ring slot holding a position at or after the chunk's start is
+    // superseded by the chunk: no key.
+    auto key_pos = [&](int32_t raw, int key) {
+      return ((tile_base + key < p.slots) & (raw >= p0)) ? -1 : raw;
+    };
     // Tile flags from the 64 key positions, one per lane: bit 0 some key is
     // not visible to every row (mask needed), bit 1 some key is visible.
-    const int32_t kp_l = t.pos[lane];
+    const int32_t kp_l = key_pos(t.pos[lane], lane);
     const bool all_l = in(kp_l, 0, all_a) || in(kp_l, all_b, t_lo);
     const bool any_l = in(kp_l, 0, any_a) || in(kp_l, any_b, t_hi);
     const int flags = (__ballot(!all_l) != 0 ? 1 : 0) | (__ballot(any_l) != 0 ? 2 : 0);
@@ -433,15 +444,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       if (flags & 1) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const i32x4_t kp = *reinterpret_cast<const i32x4_t*>(&t.pos[16 * kb + 4 * lq]);
+          const i32x4_t raw = *reinterpret_cast<const i32x4_t*>(&t.pos[16 * kb + 4 * lq]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r) {
+            const int32_t kp = key_pos(raw[r], 16 * kb + 4 * lq + r);
 #pragma unroll
             for (int rb = 0; rb < kRowBlocks; ++rb) {
-              const bool vis = (kp[r] >= 0) & (kp[r] <= t_row[rb]) &
-                               ((kp[r] < p.sinks) | (kp[r] > t_win[rb]));
+              const bool vis = (kp >= 0) & (kp <= t_row[rb]) &
+                               ((kp < p.sinks) | (kp > t_win[rb]));
               sc[rb][kb][r] = vis ? sc[rb][kb][r] : kNegInf;
             }
+          }
         }
       }
       // online softmax: tile maximum per row, rare rescale, P = 2^(s c - m)
@@ -467,22 +480,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           m[rb] = mn;
         }
       }
+      float mu[kRowBlocks];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) mu[rb] = m[rb] == kNegInf ? 0.f : m[rb];
+      // P for the keys of PV chunk pc (key blocks 2 pc, 2 pc + 1)
       f16x8_t pb[kRowBlocks][2];
+      auto probs = [&](int pc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const float mu = m[rb] == kNegInf ? 0.f : m[rb];
+        for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            pb[rb][kb >> 1][4 * (kb & 1) + r] =
-                static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(sc[rb][kb][r], c, -mu)));
-      }
-      // O^T += V^T P^T, and the row sums
+            for (int r = 0; r < 4; ++r)
+              pb[rb][pc][4 * h + r] = static_cast<_Float16>(
+                  __builtin_amdgcn_exp2f(fmaf(sc[rb][2 * pc + h][r], c, -mu[rb])));
+      };
+      // O^T += V^T P^T over PV chunk pc, and the row sums
+      auto pv = [&](int pc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int blk = 0; blk < kD / 16; ++blk)
-#pragma unroll
-        for (int pc = 0; pc < 2; ++pc) {
+        for (int blk = 0; blk < kD / 16; ++blk) {
           const f16x8_t a =
               __builtin_bit_cast(f16x8_t, t.vt[vt_off[pc ^ (blk & 1)] + 128 * blk]);
 #pragma unroll
@@ -491,13 +507,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                 __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[rb][pc], acc[rb][blk], 0, 0, 0);
         }
 #pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
           acc[rb][kD / 16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rb][pc],
                                                                     acc[rb][kD / 16], 0, 0, 0);
+      };
+      probs(0);
+      pv(0);
+      probs(1);
+      pv(1);
     }
-    if (it + 1 < n_tiles) store(cur ^ 1);  // that buffer was last read in tile it - 1
+    if (more) store(cur ^ 1);  // that buffer was last read in tile it - 1
     wait_vector_loads();
     __syncthreads();
   }
@@ -546,8 +565,15 @@ PrefillLayout prefill_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream) {
   const int64_t tokens = static_cast<int64_t>(p.batch) * p.n_tokens;
   const int64_t grid = (tokens + 3) / 4;
+  // About 2M threads: head groups = 2^21 / (tokens * 64), at least 1.
+  const int heads = p.num_q_heads + p.num_kv_heads;
+  const int64_t want = ((int64_t{1} << 21) + tokens * 64 - 1) / (tokens * 64);
+  const int groups_wanted = static_cast<int>(std::min<int64_t>(std::max<int64_t>(want, 1), heads));
+  const int group_heads = (heads + groups_wanted - 1) / groups_wanted;
+  const int groups = (heads + group_heads - 1) / group_heads;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  rotate_chunk_kernel<<<static_cast<unsigned>(grid), 256, 0, stream>>>(p);
+  rotate_chunk_kernel<<<dim3(static_cast<unsigned>(grid), static_cast<unsigned>(groups)), 256, 0,
+                        stream>>>(p, group_heads);
   return hipGetLastError();
 }
 

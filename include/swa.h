@@ -180,7 +180,8 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t n_tokens, size_t* bytes);
 
-/* Chunked prefill on a ring cache ([pool] chunked prefill): n_tokens new
+/* Chunked prefill on a ring cache ([pool] "paging": prefill in chunks of
+ * 128-256 tokens; [ring] §1.3, [share] §2.3: prefill vs decode): n_tokens new
  * tokens per sequence, at positions pos[b] .. pos[b] + n_tokens - 1, are
  * attended and then appended.
  *

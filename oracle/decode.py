@@ -10,10 +10,11 @@ Ring workloads (sink + sliding window, [sink] cache formula, [ring] §2.2):
   [ring] demo does, §4.3).  Cached K rows carry RoPE at their absolute
   position, rounded to the storage dtype ([pool] "bake RoPE into K"); V rows
   are stored as given; the query is rotated at t and stored the same way.
-Chunked prefill on a ring ([pool] chunked prefill): a chunk of T new tokens
-  at positions p0 .. p0 + T - 1; query row j is exactly decode step j of the
-  same workload (position p0 + j attends R(p0 + j) after the tokens before it
-  were appended), so the expected rows are the decode steps' outputs.
+Chunked prefill on a ring ([pool] "paging", chunks of 128-256 tokens): a
+  chunk of T new tokens at positions p0 .. p0 + T - 1; query row j is exactly
+  decode step j of the same workload (position p0 + j attends R(p0 + j) after
+  the tokens before it were appended), so the expected rows are the decode
+  steps' outputs.
 Paged workloads (block table with a shared prefix, [share] §3.1-§3.2):
   plain causal attention over all len_b tokens of sequence b; K rows are used
   as given (no RoPE on this workload).

@@ -304,15 +304,15 @@ WORKLOADS = {
         dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=128,
         history="sinks+window", pos0_range=(4096, 65536)),
     # Chunked prefill on the two ring caches: the tokens after the history
-    # arrive 512 per sequence per call.
+    # arrive 256 per sequence per call (chunks of 128-256 tokens).
     "mha-prefill": RingWorkload(
         name="mha-prefill", seed=2, batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128,
-        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=2048,
-        history="chunks:256:32", chunk=512),
+        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=1024,
+        history="chunks:256:32", chunk=256),
     "gqa-prefill": RingWorkload(
         name="gqa-prefill", seed=3, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
-        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=1024,
-        history="sinks+window", pos0_range=(4096, 65536), chunk=512),
+        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=512,
+        history="sinks+window", pos0_range=(4096, 65536), chunk=256),
     "paged": PagedWorkload(
         name="paged", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
         dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
