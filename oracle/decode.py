@@ -22,6 +22,10 @@ Pool workloads (fixed pool + validity mask, [pool] "paging" and "mask"):
   attention over exactly the tokens of the resident blocks; absent blocks
   are as if they did not exist.  Resident K rows carry RoPE at their
   absolute position; the query is taken as given (already rotated).
+Pager workloads ([pool] "paging", LRU residency): the blocks a decode step
+  sees are those the LRU pool (oracle/paging.py) holds at that moment, with
+  the copies for the next step in flight; attention over their tokens as for
+  the pool workloads.
 """
 
 from __future__ import annotations
@@ -31,6 +35,7 @@ import numpy as np
 from synth import TENSOR_K, TENSOR_Q, TENSOR_V
 
 from .attention import attend_heads
+from .paging import LruPool
 from .ring import resident_positions, simulate_appends
 from .rope import rope
 from .rounding import round_store
@@ -106,4 +111,35 @@ def pool_rows(w, b: int, style: str = "interleaved"):
 
 def pool_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
     _, k, v = pool_rows(w, b, style)
+    return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)
+
+
+def pager_schedule(w, b: int):
+    """(visible, slots): for each decode step of sequence b, the blocks it
+    sees (sorted) and the logical block held by every pool slot (-1 = empty).
+
+    The call order the harness follows: the history streams in (one advance
+    per prefill request), step 0's request is met in full, then before
+    decode step t the request of step t + 1 is advanced, so step t sees the
+    pool with those copies in flight."""
+    pool = LruPool(w.pool_slots)
+    for r in w.prefill_requests():
+        pool.advance(r)
+    pool.request(w.step_request(b, 0))
+    visible, slots = [], []
+    for step in range(w.decode_steps):
+        if step + 1 < w.decode_steps:
+            pool.advance(w.step_request(b, step + 1))
+        visible.append(sorted(pool.visible()))
+        slots.append(list(pool.slot_block))
+    return visible, slots
+
+
+def pager_expected(w, b: int, step: int, blocks, scale=None, style: str = "interleaved"):
+    """(out [Hq, d], lse [Hq]) of decode step `step` over the given blocks."""
+    blocks = np.asarray(sorted(blocks), dtype=np.int64)
+    pos = (blocks[:, None] * w.block_size + np.arange(w.block_size)[None, :]).reshape(-1)
+    k_raw = w.rows(TENSOR_K, b, pos)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    k = round_store(rope(k_raw, pos[:, None], w.rope_base, style), w.dtype)
     return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)

@@ -22,6 +22,7 @@ from .draws import (  # noqa: F401
 from .workloads import (  # noqa: F401
     WORKLOADS,
     PagedWorkload,
+    PagerWorkload,
     PoolWorkload,
     RingWorkload,
     workload,

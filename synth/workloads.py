@@ -11,6 +11,10 @@ Three kinds of workload:
 * PoolWorkload   - one long logical context split in 64-token blocks, of which
   only a fixed-size pool of slots is resident; a per-slot validity mask marks
   the filled slots; read-only decode steps.
+* PagerWorkload  - the same long context held whole in host memory, with a
+  device pool of slots filled on demand: a string of block requests (a
+  chunked prefill streaming the history, then one request per decode step:
+  the window's blocks, a drifting focus region and a few random revisits).
 
 Everything here is an input: shapes, draws, lengths, start positions, which
 logical block sits in which pool slot, and the physical block ids.  How a
@@ -35,6 +39,8 @@ _S_PERM = 102
 _S_RESIDENT = 103
 _S_SUBSET = 104
 _S_PLACE = 105
+_S_FOCUS = 106
+_S_REVISIT = 107
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -290,6 +296,84 @@ class PoolWorkload:
         return 2 * self.num_kv_heads * self.head_dim * 2
 
 
+@dataclasses.dataclass(frozen=True)
+class PagerWorkload:
+    name: str
+    seed: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    block_size: int         # tokens per block
+    logical_blocks: int     # blocks of each sequence's history (all in host memory)
+    pool_slots: int         # device slots per sequence
+    rope_base: float
+    scale: float
+    decode_steps: int
+    prefill_blocks: int     # blocks per request while the history streams in
+    window_blocks: int      # the last blocks of the history, named by every step
+    focus_blocks: int       # consecutive blocks around a focus that drifts forward
+    focus_drift: int        # the focus moves U{0..focus_drift} blocks per step
+    revisits: int           # uniformly drawn earlier blocks per step
+
+    kind = "pager"
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def context(self) -> int:
+        return self.logical_blocks * self.block_size
+
+    def prefill_requests(self) -> list:
+        """Requests of the history streaming in: consecutive chunks of
+        prefill_blocks blocks, the same for every sequence."""
+        n, k = self.logical_blocks, self.prefill_blocks
+        return [list(range(c, min(c + k, n))) for c in range(0, n, k)]
+
+    @functools.cached_property
+    def _focus(self) -> np.ndarray:
+        """int64 [B, steps]: first block of each step's focus region."""
+        g = _rng(self.seed, _S_FOCUS)
+        hi = self.logical_blocks - self.window_blocks - self.focus_blocks
+        start = g.integers(0, max(1, hi // 2), size=self.batch)
+        drift = g.integers(0, self.focus_drift + 1, size=(self.batch, self.decode_steps))
+        drift[:, 0] = 0
+        return np.minimum(start[:, None] + np.cumsum(drift, axis=1), hi)
+
+    @functools.cached_property
+    def _revisits(self) -> np.ndarray:
+        g = _rng(self.seed, _S_REVISIT)
+        hi = self.logical_blocks - self.window_blocks
+        return g.integers(0, hi, size=(self.batch, self.decode_steps, self.revisits))
+
+    def step_request(self, b: int, step: int) -> list:
+        """Blocks decode step `step` of sequence b asks for: the window's
+        blocks, then the focus region, then the revisits (duplicates kept
+        once, at their first place)."""
+        n = self.logical_blocks
+        window = range(n - self.window_blocks, n)
+        f = int(self._focus[b, step])
+        focus = range(f, f + self.focus_blocks)
+        req = list(window) + list(focus) + [int(x) for x in self._revisits[b, step]]
+        return list(dict.fromkeys(req))
+
+    def rows(self, tensor: int, b: int, positions) -> np.ndarray:
+        return draw_rows(self.seed, tensor, b, positions, self.num_kv_heads, self.head_dim,
+                         self.scale, self.dtype)
+
+    def query(self, b: int, step: int) -> np.ndarray:
+        """Query of decode step `step`, taken as already rotated (an isotropic
+        draw is rotation invariant)."""
+        return draw_rows(self.seed, TENSOR_Q, b, [step], self.num_q_heads, self.head_dim,
+                         self.scale, self.dtype)[0]
+
+    def kv_bytes_per_token(self) -> int:
+        return 2 * self.num_kv_heads * self.head_dim * 2
+
+
 WORKLOADS = {
     "tiny-ring": RingWorkload(
         name="tiny-ring", seed=1, batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64,
@@ -325,6 +409,13 @@ WORKLOADS = {
         name="long-pool-b16", seed=5, batch=16, num_q_heads=24, num_kv_heads=4, head_dim=128,
         dtype="bf16", block_size=64, logical_blocks=4096, pool_slots=1152,
         rope_base=10000.0, scale=0.5, decode_steps=128),
+    # The long-pool-b1 context held whole in host memory: 1152 device slots
+    # filled on demand (LRU), a 4096-token window named by every step.
+    "long-pool-swap": PagerWorkload(
+        name="long-pool-swap", seed=6, batch=1, num_q_heads=24, num_kv_heads=4, head_dim=128,
+        dtype="bf16", block_size=64, logical_blocks=4096, pool_slots=1152,
+        rope_base=10000.0, scale=0.5, decode_steps=128, prefill_blocks=64, window_blocks=64,
+        focus_blocks=32, focus_drift=3, revisits=4),
 }
 
 
@@ -332,5 +423,5 @@ def workload(name: str):
     return WORKLOADS[name]
 
 
-__all__ = ["RingWorkload", "PagedWorkload", "PoolWorkload", "WORKLOADS", "workload", "CHUNK",
+__all__ = ["RingWorkload", "PagedWorkload", "PoolWorkload", "PagerWorkload", "WORKLOADS", "workload", "CHUNK",
            "TENSOR_K", "TENSOR_V", "TENSOR_Q"]
