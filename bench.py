@@ -34,6 +34,13 @@ TFLOP/s of useful attention arithmetic (4 x d flops per visible (query head,
 key) pair: S = Q K^T and O = P V) against the 2.5 PFLOP/s dense bf16 / fp16
 MFMA peak; `roofline` times the whole call (its three launches).
 
+Host-pool paging workload (long-pool-swap): a step is swa_pager_advance for
+the next step's block request (LRU decisions on the host, a validity launch
+on the attention stream, the block copies from pinned host memory on a copy
+stream, overlapping the attention) and the decode over the pool; `value`
+counts the blocks each decode actually saw.  `swap` reports the blocks and
+bytes copied per step, and the same steps without paging on the same pool.
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
@@ -75,6 +82,13 @@ def describe(w) -> dict:
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.block_size}-token blocks, lengths "
                 f"{w.len_range[0]}..{w.len_range[1]}, shared prefix {w.shared_prefix}")
+    elif w.kind == "pager":
+        text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
+                f"d={w.head_dim}, {w.dtype}, {w.logical_blocks} x {w.block_size}-token "
+                f"logical blocks in pinned host memory, {w.pool_slots} device slots per "
+                f"sequence filled on demand (LRU); per step: {w.window_blocks} window blocks, "
+                f"{w.focus_blocks} focus blocks drifting up to {w.focus_drift} per step, "
+                f"{w.revisits} random revisits")
     else:
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.logical_blocks} x {w.block_size}-token "
@@ -145,7 +159,7 @@ def decode_source_sha() -> str:
 # GPU side
 # ---------------------------------------------------------------------------
 
-def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
+def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True) -> dict:
     import numpy as np
     import torch
 
@@ -212,6 +226,40 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
             def decode(i):
                 B.decode_step_ring(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i],
                                    q_all[i][:, 0], st.out, st.workspace, st.lse)
+    elif w.kind == "pager":
+        import dataclasses
+
+        from decode_attention_fixed_amd.workloads import PagerState
+        wl = dataclasses.replace(w, decode_steps=total + 1)
+        st = PagerState(wl)
+        st.fill_host()
+        st.reset()
+        copy_stream = torch.cuda.Stream()
+        st.warm(copy_stream)
+        torch.cuda.synchronize()
+        qs = torch.stack([st.step_query(i) for i in range(min(total, w.decode_steps))])
+        reqs = [B.pack_requests(st.step_requests(i + 1)) for i in range(total)]
+        filled = sum(1 for b in range(w.batch) for x in st.slot_blocks(b) if x >= 0)
+        seen_blocks = {}   # step -> blocks the decode of that step sees
+        loaded = {}
+
+        host_us = {"advance": 0.0, "decode": 0.0}
+        calls = [B.prepare_decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
+                                             st.seq_lens, st.block_valid, st.out, st.workspace,
+                                             st.lse) for j in range(qs.shape[0])]
+        copy_stream = None if same_stream else copy_stream
+
+        def pre(i):
+            t = time.perf_counter()
+            n = st.advance(reqs[i], copy_stream)
+            host_us["advance"] += (time.perf_counter() - t) * 1e6
+            loaded[i] = n
+            seen_blocks[i] = filled - n
+
+        def decode(i):
+            t = time.perf_counter()
+            calls[i % len(calls)]()
+            host_us["decode"] += (time.perf_counter() - t) * 1e6
     else:
         st = PagedState(w, out_dtype=torch.float32)
         st.fill()
@@ -267,6 +315,45 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False) -> dict:
     torch.cuda.synchronize()
     dec_ms = begin.elapsed_time(end) / steps
     res = {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
+    if w.kind == "pager":
+        res["host_us_per_step"] = {k: round(v / (warmup + steps), 1) for k, v in host_us.items()}
+        timed = range(warmup, warmup + steps)
+        res["kv_bytes_region1"] = sum(seen_blocks[i] for i in timed) * w.block_size * \
+            w.kv_bytes_per_token()
+        res["blocks_loaded_region1"] = sum(loaded[i] for i in timed)
+        res["block_bytes"] = 2 * w.num_kv_heads * w.block_size * w.head_dim * 2
+        st.commit()
+        torch.cuda.synchronize()
+        # Region 2 for the pager: the decode alone, back to back, over cycled
+        # copies of the pool (>= 600 MB together, so none is served from the
+        # last-level cache): the attention kernel's own rate.
+        pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
+        copies = max(1, math.ceil(600e6 / pool_bytes))
+        pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
+                                            for _ in range(copies - 1)]
+        visible = int(st.block_valid.sum().item())
+        cyc = [B.prepare_decode_attn_paged(st.desc, qs[j % qs.shape[0]], k, v, st.block_table,
+                                           st.seq_lens, st.block_valid, st.out, st.workspace,
+                                           st.lse) for j, (k, v) in enumerate(pools)]
+        for i in range(warmup):
+            cyc[i % copies]()
+        torch.cuda.synchronize()
+        begin.record()
+        for s in range(steps):
+            cyc[s % copies]()
+        end.record()
+        torch.cuda.synchronize()
+        res["decode_ms_mean"] = begin.elapsed_time(end) / steps
+        res["kv_bytes_region2"] = visible * w.block_size * w.kv_bytes_per_token()
+        # Region 3: the same steps without paging, on the one live pool (the
+        # cache conditions of region 1): what the paging adds to a step.
+        begin.record()
+        for s in range(steps):
+            calls[s % len(calls)]()
+        end.record()
+        torch.cuda.synchronize()
+        res["no_swap_ms"] = begin.elapsed_time(end) / steps
+        st.close()
     if w.kind == "ring" and w.chunk:
         first = w.decode_start[None, :] + w.chunk * np.arange(total)[:, None]
         res["flops_region1"] = sum(prefill_flops(w, first[warmup + s]) for s in range(steps))
@@ -302,8 +389,16 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         if w.kind == "paged":
             pos = np.arange(int(w.lengths[b]))
             return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
+        if w.kind == "pager":
+            blocks = np.asarray(pager_sets[b][step], dtype=np.int64)
+            pos = (blocks[:, None] * w.block_size + np.arange(w.block_size)[None, :]).reshape(-1)
+            return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
         pos = w.resident_positions(b)
         return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
+
+    if w.kind == "pager":
+        from oracle.decode import pager_schedule
+        pager_sets = [pager_schedule(w, b)[0] for b in range(w.batch)]
 
     def oracle_step(pos, t, k_raw, v, q_raw):
         if w.kind == "ring":
@@ -344,7 +439,9 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
                            f"host memory; float64 NumPy, {timed:.1f} s timed; BLAS threads "
                            f"{threads}, elementwise ops on one thread; useful flops of the "
                            f"sampled rows / time")}
-    return {"value": round(steps_per_s * kv_bytes_per_step(w) / 1e9, 4), "unit": "GB/s",
+    step_bytes = (len(pager_sets[0][0]) * w.block_size * w.kv_bytes_per_token() * w.batch
+                  if w.kind == "pager" else kv_bytes_per_step(w))
+    return {"value": round(steps_per_s * step_bytes / 1e9, 4), "unit": "GB/s",
             "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
             "sample": (f"{n} (sequence, decode step) samples of {w.name} (sequences in order, "
                        f"steps from 0; all heads), inputs pre-drawn in host memory; float64 "
@@ -409,6 +506,9 @@ def main() -> int:
     ap.add_argument("--unfused", action="store_true",
                     help="ring caches: kv_append_rope + decode_attn_ring per step instead of "
                          "decode_step_ring")
+    ap.add_argument("--copy-stream", action="store_true",
+                    help="long-pool-swap: run the block copies on a stream of their own, "
+                         "overlapping the attention (default: on the attention stream)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -423,16 +523,21 @@ def main() -> int:
 
     from synth import WORKLOADS
     w = WORKLOADS[args.workload]
-    res = run_gpu(w, args.steps, args.warmup, args.unfused)
+    res = run_gpu(w, args.steps, args.warmup, args.unfused, not args.copy_stream)
     if w.kind == "ring" and w.chunk:
         out = prefill_line(w, args, res)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(w)
         print(json.dumps(out), flush=True)
         return 0
-    kv_bytes = kv_bytes_per_step(w)
-    ms_per_step = res["total_ms"] / args.steps
-    value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9
+    if w.kind == "pager":
+        kv_bytes = res["kv_bytes_region2"]
+        ms_per_step = res["total_ms"] / args.steps
+        value_gbs = res["kv_bytes_region1"] / (res["total_ms"] / 1e3) / 1e9
+    else:
+        kv_bytes = kv_bytes_per_step(w)
+        ms_per_step = res["total_ms"] / args.steps
+        value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9
     achieved = kv_bytes / (res["decode_ms_mean"] / 1e3) / 1e9
     traffic = traffic_record(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -454,6 +559,20 @@ def main() -> int:
         "hbm_frac_of_peak": round(value_gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline,
     }
+    if w.kind == "pager":
+        per_step = res["blocks_loaded_region1"] / args.steps
+        out["swap"] = {
+            "blocks_per_step": round(per_step, 3),
+            "bytes_per_step": int(per_step * res["block_bytes"]),
+            "host_to_device_gbs": round(per_step * res["block_bytes"] / ms_per_step / 1e6, 2),
+            "no_swap_ms_per_step": round(res["no_swap_ms"], 5),
+            "host_us_per_step": res["host_us_per_step"],
+            "wall_ms_per_step": round(res["wall_s"] * 1e3 / args.steps, 5),
+            "copies_on": "a stream of their own" if args.copy_stream else "the attention stream",
+            "note": ("copies from pinned host memory by one kernel launch per step; "
+                     "no_swap_ms_per_step is the same decode on the same pool without "
+                     "paging"),
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -47,6 +47,13 @@ class SwaPagedDesc(ctypes.Structure):
                 ("num_phys_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class SwaPagerConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("logical_blocks", ctypes.c_int32), ("slots_per_seq", ctypes.c_int32),
+                ("num_phys_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _PROTOS = {
@@ -73,6 +80,13 @@ _PROTOS = {
                                          ctypes.c_size_t, _vp]),
     "kv_write_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i32, ctypes.c_float, _i32, _vp]),
+    "swa_pager_create": (ctypes.c_int, [ctypes.POINTER(SwaPagerConfig), _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, ctypes.POINTER(_vp)]),
+    "swa_pager_reset": (ctypes.c_int, [_vp, _vp]),
+    "swa_pager_advance": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i32)]),
+    "swa_pager_commit": (ctypes.c_int, [_vp, _vp]),
+    "swa_pager_slot_blocks": (ctypes.c_int, [_vp, _i32, _vp]),
+    "swa_pager_destroy": (None, [_vp]),
     "swa_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_PROTOS)
@@ -274,6 +288,30 @@ def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def prepare_decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
+                              v_pool: torch.Tensor, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, block_valid: torch.Tensor | None,
+                              out: torch.Tensor, workspace: torch.Tensor,
+                              lse: torch.Tensor | None = None, scale: float = 0.0, stream=None):
+    """decode_attn_paged's arguments marshalled once (stream included);
+    returns a function of no arguments that makes the call, for a loop that
+    repeats one call on the same buffers."""
+    args = (ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+            _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
+            _ptr(block_valid, "block_valid", torch.uint8), scale, _ptr(out, "out"),
+            _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    fn = LIB.decode_attn_paged
+    keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, workspace, lse)
+
+    def call() -> None:
+        code = fn(*args)
+        if code != SWA_OK:
+            raise SwaError("decode_attn_paged", code)
+    call.keep = keep  # the tensors stay alive as long as the call
+    return call
+
+
 def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tensor,
                    k_src: torch.Tensor, v_src: torch.Tensor, dst_rows: torch.Tensor,
                    pos: torch.Tensor | None = None, rope_base: float = 10000.0,
@@ -284,6 +322,83 @@ def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tenso
                               _ptr(k_src, "k_src"), _ptr(v_src, "v_src"),
                               _ptr(dst_rows, "dst_rows", torch.int32), _ptr(pos, "pos", torch.int32),
                               k_src.shape[0], rope_base, _STYLE_CODE[rope_style], _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# host-pool pager
+# ---------------------------------------------------------------------------
+
+def make_pager_config(batch: int, num_kv_heads: int, head_dim: int, block_size: int,
+                      logical_blocks: int, slots_per_seq: int, num_phys_blocks: int,
+                      dtype: str = "bf16") -> SwaPagerConfig:
+    return SwaPagerConfig(batch, num_kv_heads, head_dim, block_size, logical_blocks,
+                          slots_per_seq, num_phys_blocks, _DTYPE_NAME[dtype])
+
+
+def _host_ptr(t: torch.Tensor, name: str) -> int:
+    if t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous host tensor")
+    return t.data_ptr()
+
+
+def swa_pager_create(cfg: SwaPagerConfig, host_k: torch.Tensor, host_v: torch.Tensor,
+                     k_pool: torch.Tensor, v_pool: torch.Tensor, slot_phys,
+                     block_table: torch.Tensor, block_valid: torch.Tensor) -> int:
+    """host_k, host_v: pinned host [B, L, Hkv, bs, d]; k_pool, v_pool: device
+    [Nphys, Hkv, bs, d]; slot_phys: [B, C] int32 host array (copied);
+    block_table [B, C] int32 and block_valid [B, C] uint8 on the device."""
+    flat = [int(x) for row in slot_phys for x in row]
+    sp = (_i32 * len(flat))(*flat)
+    handle = _vp()
+    _check("swa_pager_create",
+           LIB.swa_pager_create(ctypes.byref(cfg), _host_ptr(host_k, "host_k"),
+                                _host_ptr(host_v, "host_v"), _ptr(k_pool, "k_pool"),
+                                _ptr(v_pool, "v_pool"), ctypes.cast(sp, _vp),
+                                _ptr(block_table, "block_table", torch.int32),
+                                _ptr(block_valid, "block_valid", torch.uint8),
+                                ctypes.byref(handle)))
+    return handle.value
+
+
+def swa_pager_reset(handle: int, stream=None) -> None:
+    _check("swa_pager_reset", LIB.swa_pager_reset(handle, _stream(stream)))
+
+
+def pack_requests(requests) -> tuple:
+    """(offsets, blocks) C arrays of one request per sequence, for
+    swa_pager_advance (packing ahead of time keeps it off a timed loop)."""
+    flat = [int(b) for r in requests for b in r]
+    offsets = [0]
+    for r in requests:
+        offsets.append(offsets[-1] + len(r))
+    return (_i32 * len(offsets))(*offsets), (_i32 * max(1, len(flat)))(*flat)
+
+
+def swa_pager_advance(handle: int, requests, stream=None, copy_stream=None) -> int:
+    """requests: one list of logical blocks per sequence, or what
+    pack_requests returned.  Returns the number of blocks whose copies this
+    call starts."""
+    off, blocks = requests if isinstance(requests, tuple) else pack_requests(requests)
+    n = _i32()
+    cs = _stream(copy_stream) if copy_stream is not None else _stream(stream)
+    _check("swa_pager_advance",
+           LIB.swa_pager_advance(handle, ctypes.cast(off, _vp), ctypes.cast(blocks, _vp),
+                                 _stream(stream), cs, ctypes.byref(n)))
+    return n.value
+
+
+def swa_pager_commit(handle: int, stream=None) -> None:
+    _check("swa_pager_commit", LIB.swa_pager_commit(handle, _stream(stream)))
+
+
+def swa_pager_slot_blocks(handle: int, seq: int, slots_per_seq: int) -> list:
+    out = (_i32 * slots_per_seq)()
+    _check("swa_pager_slot_blocks", LIB.swa_pager_slot_blocks(handle, seq, ctypes.cast(out, _vp)))
+    return list(out)
+
+
+def swa_pager_destroy(handle: int | None) -> None:
+    LIB.swa_pager_destroy(handle)
 
 
 # ---------------------------------------------------------------------------

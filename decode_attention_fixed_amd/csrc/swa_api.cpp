@@ -136,6 +136,15 @@ int log2_exact(int32_t x) {
 
 }  // namespace
 
+// Error text shared with the other C-ABI sources (pager_api.cpp).
+namespace swa {
+int record_error(int code, const char* text) {
+  g_last_error = text;
+  return code;
+}
+void clear_error() { g_last_error.clear(); }
+}  // namespace swa
+
 extern "C" {
 
 swa_status swa_cache_required_bytes(const swa_cache_config* cfg, size_t* kv_bytes_each,

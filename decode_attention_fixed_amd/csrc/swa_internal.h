@@ -180,4 +180,34 @@ int prefill_tokens_per_block(int group);
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// Host-pool pager: block copies from pinned host memory, validity updates.
+// The lists travel by value in the kernel arguments, so nothing is staged in
+// memory that a later call could overwrite before the kernel runs.
+constexpr int kPagerMaxCopies = 224;  // blocks per copy launch
+constexpr int kPagerMaxValid = 448;   // validity updates per launch
+struct PagerCopyParams {
+  const void* host_k;   // device view of the pinned host store [B * L blocks]
+  const void* host_v;
+  void* k_pool;         // [num_phys_blocks blocks]
+  void* v_pool;
+  int32_t block_u4;     // 16-byte units per block of K (or V)
+  int32_t piece_u4;     // 16-byte units per workgroup
+  int32_t pieces;       // workgroups per block and tensor
+  int32_t n;            // blocks in this launch
+  int32_t src_block[kPagerMaxCopies];  // b * L + logical block
+  int32_t dst_block[kPagerMaxCopies];  // physical pool block
+};
+struct PagerValidParams {
+  uint8_t* valid;       // [B * C]
+  int32_t n;
+  int32_t entries[kPagerMaxValid];  // e >= 0: valid[e] = 1; e < 0: valid[-1 - e] = 0
+};
+hipError_t launch_pager_copy(const PagerCopyParams& p, hipStream_t stream);
+hipError_t launch_pager_valid(const PagerValidParams& p, hipStream_t stream);
+hipError_t launch_fill_u8(uint8_t* dst, size_t n, uint8_t value, hipStream_t stream);
+
+// The calling thread's error text (swa_last_error), set by every C-ABI source.
+int record_error(int code, const char* text);
+void clear_error();
+
 }  // namespace swa

@@ -11,7 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from synth import TENSOR_K, TENSOR_Q, TENSOR_V, PagedWorkload, PoolWorkload, RingWorkload
+from synth import (TENSOR_K, TENSOR_Q, TENSOR_V, PagedWorkload, PagerWorkload, PoolWorkload,
+                   RingWorkload)
 from synth.draws import SHARED_SEQUENCE, draw_rows_parallel
 
 from . import binding as B
@@ -212,3 +213,98 @@ class PagedState:
         B.decode_attn_paged(self.desc, q, self.k_pool, self.v_pool, self.block_table,
                             self.seq_lens, self.block_valid, self.out, self.workspace, self.lse,
                             scale)
+
+
+class PagerState:
+    """A PagerWorkload: the whole history in pinned host memory, a device pool
+    of slots filled on demand by the library's pager, and decode buffers.
+
+    The host store is built with the library's own write path: raw K rows are
+    rotated into a device staging pool by kv_write_paged (one block per
+    logical block, in order), then copied to the pinned host store."""
+
+    def __init__(self, w: PagerWorkload, device="cuda", out_dtype=torch.float32):
+        self.w = w
+        self.device = device
+        dt = _TORCH_DTYPE[w.dtype]
+        B_, L, C = w.batch, w.logical_blocks, w.pool_slots
+        blk = (w.num_kv_heads, w.block_size, w.head_dim)
+        self.host_k = torch.empty((B_, L) + blk, dtype=dt, pin_memory=True)
+        self.host_v = torch.empty((B_, L) + blk, dtype=dt, pin_memory=True)
+        self.num_phys = B_ * C
+        self.k_pool = torch.zeros((self.num_phys,) + blk, dtype=dt, device=device)
+        self.v_pool = torch.zeros((self.num_phys,) + blk, dtype=dt, device=device)
+        self.block_table = torch.empty((B_, C), dtype=torch.int32, device=device)
+        self.block_valid = torch.empty((B_, C), dtype=torch.uint8, device=device)
+        self.seq_lens = torch.full((B_,), C * w.block_size, dtype=torch.int32, device=device)
+        self.desc = B.make_paged_desc(B_, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                      w.block_size, C, self.num_phys, w.dtype)
+        self.workspace = B.new_workspace(B_, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         C * w.block_size, device)
+        self.out = torch.empty((B_, w.num_q_heads, w.head_dim), dtype=out_dtype, device=device)
+        self.lse = torch.empty((B_, w.num_q_heads), dtype=torch.float32, device=device)
+        self.cfg = B.make_pager_config(B_, w.num_kv_heads, w.head_dim, w.block_size, L, C,
+                                       self.num_phys, w.dtype)
+        self.handle = B.swa_pager_create(self.cfg, self.host_k, self.host_v, self.k_pool,
+                                         self.v_pool, w.slot_phys.tolist(), self.block_table,
+                                         self.block_valid)
+
+    def fill_host(self) -> None:
+        w = self.w
+        bs, L = w.block_size, w.logical_blocks
+        n = L * bs
+        desc = B.make_paged_desc(1, w.num_kv_heads, w.num_kv_heads, w.head_dim, bs, L, L, w.dtype)
+        stage_k = torch.empty((L, w.num_kv_heads, bs, w.head_dim), dtype=self.host_k.dtype,
+                              device=self.device)
+        stage_v = torch.empty_like(stage_k)
+        pos = torch.arange(n, dtype=torch.int32, device=self.device)
+        for b in range(w.batch):
+            k = draw_rows_parallel(w.seed, TENSOR_K, b, 0, n, w.num_kv_heads, w.head_dim,
+                                   w.scale, w.dtype)
+            v = draw_rows_parallel(w.seed, TENSOR_V, b, 0, n, w.num_kv_heads, w.head_dim,
+                                   w.scale, w.dtype)
+            B.kv_write_paged(desc, stage_k, stage_v, to_device(k, w.dtype, self.device),
+                             to_device(v, w.dtype, self.device), pos, pos, w.rope_base)
+            self.host_k[b].copy_(stage_k.cpu())
+            self.host_v[b].copy_(stage_v.cpu())
+        torch.cuda.synchronize()
+
+    def reset(self) -> None:
+        B.swa_pager_reset(self.handle)
+
+    def advance(self, requests, copy_stream=None) -> int:
+        return B.swa_pager_advance(self.handle, requests, None, copy_stream)
+
+    def commit(self) -> None:
+        B.swa_pager_commit(self.handle)
+
+    def warm(self, copy_stream=None) -> int:
+        """The history streams in, then step 0's request is met in full."""
+        w = self.w
+        n = 0
+        for r in w.prefill_requests():
+            n += self.advance([r] * w.batch, copy_stream)
+        n += self.advance([w.step_request(b, 0) for b in range(w.batch)], copy_stream)
+        self.commit()
+        return n
+
+    def step_requests(self, step: int) -> list:
+        return [self.w.step_request(b, step) for b in range(self.w.batch)]
+
+    def step_query(self, step: int) -> torch.Tensor:
+        q = np.stack([self.w.query(b, step) for b in range(self.w.batch)])
+        return to_device(q, self.w.dtype, self.device)
+
+    def decode(self, q: torch.Tensor, scale: float = 0.0) -> None:
+        B.decode_attn_paged(self.desc, q, self.k_pool, self.v_pool, self.block_table,
+                            self.seq_lens, self.block_valid, self.out, self.workspace, self.lse,
+                            scale)
+
+    def slot_blocks(self, b: int) -> list:
+        return B.swa_pager_slot_blocks(self.handle, b, self.w.pool_slots)
+
+    def close(self) -> None:
+        if self.handle:
+            torch.cuda.synchronize()
+            B.swa_pager_destroy(self.handle)
+            self.handle = 0

@@ -19,8 +19,8 @@
  *   - Plain C linkage; no exception crosses this boundary.
  *   - Every buffer is owned by the caller.  Device buffers are device
  *     pointers (hipMalloc'ed or equivalent); the library never allocates or
- *     frees device memory.  The only host-side allocation is the opaque
- *     swa_cache descriptor.
+ *     frees device memory.  The only allocations are the opaque host objects
+ *     (swa_cache, and swa_pager with its two HIP events).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
  *     are asynchronous on it; work on one stream runs in call order, so an
  *     append followed by a decode on the same stream reads the new token.
@@ -270,6 +270,103 @@ swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool
                           const void* k_src, const void* v_src, const int32_t* dst_rows,
                           const int32_t* pos, int32_t n_tokens, float rope_base,
                           swa_rope_style rope_style, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Host-pool pager: a sequence's history in host memory, a fixed pool of     */
+/* device slots filled on demand ([pool] "paging").                          */
+/* ------------------------------------------------------------------------- */
+
+typedef struct swa_pager_config {
+  int32_t batch;           /* B sequences, each with its own slots */
+  int32_t num_kv_heads;    /* Hkv */
+  int32_t head_dim;        /* d: 64 or 128 */
+  int32_t block_size;      /* tokens per block: a power of two, 16..1024 (64 on [pool]) */
+  int32_t logical_blocks;  /* L: blocks of each sequence's history in the host store */
+  int32_t slots_per_seq;   /* C: device slots of each sequence (columns of block_table) */
+  int32_t num_phys_blocks; /* blocks in the device pool */
+  swa_dtype dtype;         /* K / V element type */
+} swa_pager_config;
+
+/* Opaque host object: the LRU state of every slot, the caller's pointers and
+ * two HIP events that order the copies against the attention. */
+typedef struct swa_pager swa_pager;
+
+/* A pager over caller-owned memory.
+ *
+ *   host_k, host_v  [B, L, Hkv, block_size, d] in cfg->dtype: every block of
+ *                   every sequence's history, K already rotated by RoPE at
+ *                   its absolute position ([pool] "bake RoPE into K": a block
+ *                   is self-contained, so it can sit in any slot).  Pinned
+ *                   host memory that the device can read (hipHostMalloc, or
+ *                   torch's pin_memory); otherwise SWA_ERR_INVALID_ARG.
+ *   k_pool, v_pool  [num_phys_blocks, Hkv, block_size, d], device: the
+ *                   layout decode_attn_paged reads.
+ *   slot_phys       [B, C] int32, host, copied: the pool block behind slot j
+ *                   of sequence b; all distinct, in [0, num_phys_blocks).
+ *   block_table     [B, C] int32, device: written by swa_pager_reset
+ *                   (slot_phys), then left alone.
+ *   block_valid     [B, C] uint8, device: 1 where a slot's block may be read.
+ *
+ * decode_attn_paged with (block_table, block_valid, seq_lens = C * block_size,
+ * max_blocks_per_seq = C) then attends exactly the blocks the pager has made
+ * visible.  The pager never allocates device memory; it creates two HIP
+ * events (so this call needs a device).  Call swa_pager_reset before the
+ * first request.  Not thread-safe: one thread drives a pager. */
+swa_status swa_pager_create(const swa_pager_config* cfg, const void* host_k, const void* host_v,
+                            void* k_pool, void* v_pool, const int32_t* slot_phys,
+                            int32_t* block_table, uint8_t* block_valid, swa_pager** out);
+
+/* Every slot empty: block_table := slot_phys, block_valid := 0, no block
+ * resident, LRU history cleared.  Waits for copies in flight and returns when
+ * the stream has done it (a set-up call). */
+swa_status swa_pager_reset(swa_pager* pager, void* stream);
+
+/* Serves one request per sequence ([pool] "residency policy": LRU).
+ *
+ *   req_offsets  [B + 1] int32, host: sequence b names req_blocks[
+ *                req_offsets[b] .. req_offsets[b+1]) (offsets[0] = 0,
+ *                non-decreasing; a sequence may name nothing).
+ *   req_blocks   int32, host: logical blocks in [0, L); repeats count once.
+ *   stream       the stream the attention runs on.
+ *   copy_stream  the stream the copies run on.  It may equal `stream`: then
+ *                stream order alone orders everything and the copies do not
+ *                overlap the attention, but no event is waited on across
+ *                streams (on this platform such a wait costs the host more
+ *                than a short attention step).
+ *   n_loaded     host, or NULL: blocks this call starts copying.
+ *
+ * Every named block that is not resident gets a slot: the lowest empty one,
+ * else the slot of the least recently named block (ties: lower slot), never
+ * one named by this request or by the previous call (the attention step that
+ * call prepared is enqueued after this one and still needs them).  Blocks of a sliding window stay
+ * resident by being named in every request ([pool]: SWA layers keep their
+ * window blocks, only the others are paged).  If a sequence misses more
+ * blocks than it has empty plus evictable slots the call fails with
+ * SWA_ERR_INVALID_ARG and changes nothing.
+ *
+ * Order on the streams: work enqueued on `stream` after this call sees the
+ * blocks copied by the previous call (they become valid first) and no longer
+ * sees the slots this call overwrites (cleared); the new copies start on
+ * copy_stream once the work enqueued on `stream` before this call is done,
+ * and become visible at the next swa_pager_advance or swa_pager_commit.  So
+ *   advance(N_{t+1}); decode(t); advance(N_{t+2}); decode(t+1); ...
+ * overlaps the copies for step t+1 with the attention of step t.  After
+ * SWA_ERR_HIP the pager must be reset. */
+swa_status swa_pager_advance(swa_pager* pager, const int32_t* req_offsets,
+                             const int32_t* req_blocks, void* stream, void* copy_stream,
+                             int32_t* n_loaded);
+
+/* Makes the copies of the last advance visible to work enqueued on `stream`
+ * after this call (it waits for them on the device, not on the host). */
+swa_status swa_pager_commit(swa_pager* pager, void* stream);
+
+/* Logical block held by each slot of sequence seq (-1 = empty), as the host
+ * state stands (copies in flight included): out [C] int32, host. */
+swa_status swa_pager_slot_blocks(const swa_pager* pager, int32_t seq, int32_t* out);
+
+/* Frees the host object and its events (not the caller's memory).  Does not
+ * wait for copies in flight.  NULL is a no-op. */
+void swa_pager_destroy(swa_pager* pager);
 
 /* Text of the last failure on the calling thread ("" if none). */
 const char* swa_last_error(void);

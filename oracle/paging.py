@@ -19,10 +19,11 @@ Readings where the page is silent (each is stated in the functions below):
   takes the slot of the resident block with the oldest last use, ties going
   to the lower slot number.
 * Blocks named by the request being served and by the one before it are
-  never evicted: the previous request's blocks may still be under attention
-  while the next ones are copied in (the page overlaps the copies with the
-  attention kernel).  A request that cannot be met that way is refused and
-  leaves the pool as it was.
+  never evicted: the decode step that the previous request prepared runs
+  while the next request's blocks are copied in (the page overlaps the
+  copies with the attention kernel), and it must find every block it named.
+  A request that cannot be met that way is refused and leaves the pool as
+  it was.
 * Blocks are brought in for the next decode step while the current one runs:
   between `advance(N)` and the following advance (or `commit`) the blocks
   being copied are not yet visible and the slots they overwrite are already

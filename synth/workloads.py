@@ -327,6 +327,13 @@ class PagerWorkload:
     def context(self) -> int:
         return self.logical_blocks * self.block_size
 
+    @functools.cached_property
+    def slot_phys(self) -> np.ndarray:
+        """int32 [B, pool_slots]: device pool block behind each slot (a seeded
+        permutation of the B * pool_slots pool blocks)."""
+        perm = _rng(self.seed, _S_PERM).permutation(self.batch * self.pool_slots)
+        return perm.reshape(self.batch, self.pool_slots).astype(np.int32)
+
     def prefill_requests(self) -> list:
         """Requests of the history streaming in: consecutive chunks of
         prefill_blocks blocks, the same for every sequence."""

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 19, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -285,3 +285,67 @@ def test_product_path_has_no_fallback():
     for f in os.listdir(os.path.join(ROOT, "decode_attention_fixed_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "decode_attention_fixed_amd", "csrc",
                                                  f)).read()
+
+
+def _pcfg(**kw):
+    base = dict(batch=1, num_kv_heads=4, head_dim=128, block_size=64, logical_blocks=4096,
+                slots_per_seq=1152, num_phys_blocks=1152, dtype="bf16")
+    base.update(kw)
+    return B.make_pager_config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), B.SWA_ERR_INVALID_ARG),
+    (dict(logical_blocks=0), B.SWA_ERR_INVALID_ARG),
+    (dict(slots_per_seq=0), B.SWA_ERR_INVALID_ARG),
+    (dict(num_phys_blocks=0), B.SWA_ERR_INVALID_ARG),
+    (dict(head_dim=96), B.SWA_ERR_UNSUPPORTED),
+    (dict(block_size=48), B.SWA_ERR_UNSUPPORTED),
+    (dict(block_size=2048), B.SWA_ERR_UNSUPPORTED),
+    (dict(batch=1 << 20, logical_blocks=1 << 12), B.SWA_ERR_INVALID_ARG),
+])
+def test_pager_config_validation(kw, code):
+    L = B.LIB
+    cfg = _pcfg(**kw)
+    out = ctypes.c_void_p()
+    slots = (ctypes.c_int32 * 4)(0, 1, 2, 3)
+    assert L.swa_pager_create(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, ctypes.cast(slots,
+                              ctypes.c_void_p), FAKE, FAKE, ctypes.byref(out)) == code
+    assert out.value is None
+    assert B.swa_last_error()
+
+
+def test_pager_pointer_and_table_validation():
+    L = B.LIB
+    cfg = _pcfg(slots_per_seq=4, num_phys_blocks=8)
+    out = ctypes.c_void_p()
+    ok_slots = (ctypes.c_int32 * 4)(7, 0, 3, 5)
+
+    def create(hk=FAKE, hv=FAKE, kp=FAKE, vp=FAKE, slots=ok_slots, bt=FAKE, bv=FAKE, o=out):
+        sp = ctypes.cast(slots, ctypes.c_void_p) if slots is not None else None
+        return L.swa_pager_create(ctypes.byref(cfg), hk, hv, kp, vp, sp, bt, bv,
+                                  ctypes.byref(o) if o is not None else None)
+
+    assert create(hk=None) == B.SWA_ERR_INVALID_ARG
+    assert create(slots=None) == B.SWA_ERR_INVALID_ARG
+    assert create(bv=None) == B.SWA_ERR_INVALID_ARG
+    assert create(o=None) == B.SWA_ERR_INVALID_ARG
+    assert create(kp=FAKE + 8) == B.SWA_ERR_INVALID_ARG
+    assert create(slots=(ctypes.c_int32 * 4)(0, 1, 2, 8)) == B.SWA_ERR_INVALID_ARG  # out of range
+    assert "outside" in B.swa_last_error()
+    assert create(slots=(ctypes.c_int32 * 4)(0, 1, 1, 2)) == B.SWA_ERR_INVALID_ARG  # shared
+    assert "two slots" in B.swa_last_error()
+    # valid arguments, but the host store is not pinned memory the device can read
+    assert create() == B.SWA_ERR_INVALID_ARG
+    assert out.value is None
+
+
+def test_pager_null_handle():
+    L = B.LIB
+    off = (ctypes.c_int32 * 2)(0, 0)
+    assert L.swa_pager_reset(None, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_pager_advance(None, ctypes.cast(off, ctypes.c_void_p), None, None, None,
+                               None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_pager_commit(None, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_pager_slot_blocks(None, 0, FAKE) == B.SWA_ERR_INVALID_ARG
+    L.swa_pager_destroy(None)
