@@ -41,6 +41,11 @@ stream, overlapping the attention) and the decode over the pool; `value`
 counts the blocks each decode actually saw.  `swap` reports the blocks and
 bytes copied per step, and the same steps without paging on the same pool.
 
+Paged pool grown by appends (paged-append): a step is kv_append_paged of one
+token per sequence through the block manager (table and length updates, the
+token rows) and the decode over all tokens; KV bytes count each step's
+lengths after its append.
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
@@ -78,10 +83,13 @@ def describe(w) -> dict:
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, W={w.window} + {w.sinks} sinks, "
                 f"history {w.history}, {what}")
-    elif w.kind == "paged":
+    elif w.kind in ("paged", "paged-append"):
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.block_size}-token blocks, lengths "
                 f"{w.len_range[0]}..{w.len_range[1]}, shared prefix {w.shared_prefix}")
+        if w.kind == "paged-append":
+            text += (" shared by reference through the block manager; per step: append one "
+                     "token per sequence (kv_append_paged), then decode")
     elif w.kind == "pager":
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.logical_blocks} x {w.block_size}-token "
@@ -226,6 +234,36 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
             def decode(i):
                 B.decode_step_ring(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i],
                                    q_all[i][:, 0], st.out, st.workspace, st.lse)
+    elif w.kind == "paged-append":
+        import ctypes
+
+        from decode_attention_fixed_amd.workloads import build_paged_append
+        st = build_paged_append(w, extra_steps=total)
+
+        def staged(tensor):
+            arr = np.empty((w.batch, total, w.num_kv_heads, w.head_dim), dtype=np.float32)
+            for b in range(w.batch):
+                draw_rows_parallel(w.seed, tensor, b, int(w.lengths[b]), total, w.num_kv_heads,
+                                   w.head_dim, w.scale, w.dtype, out=arr[b])
+            t = to_device(arr, w.dtype)                               # [B, total, Hkv, d]
+            return t.permute(1, 0, 2, 3).contiguous().unsqueeze(2)    # [total, B, 1, Hkv, d]
+
+        k_all, v_all = staged(TENSOR_K), staged(TENSOR_V)
+        nq = min(total, w.decode_steps)
+        zero = np.zeros((1, w.num_q_heads, w.head_dim), np.float32)
+        qs = torch.stack([to_device(np.concatenate([np.stack([w.query(b, i)
+                                                              for b in range(w.batch)]), zero]),
+                                    w.dtype) for i in range(nq)])
+        seqs = (ctypes.c_int32 * w.batch)(*range(w.batch))
+        calls = [B.prepare_decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
+                                             st.seq_lens, None, st.out, st.workspace, st.lse)
+                 for j in range(nq)]
+
+        def pre(i):
+            st.append(seqs, k_all[i], v_all[i])
+
+        def decode(i):
+            calls[i % nq]()
     elif w.kind == "pager":
         import dataclasses
 
@@ -315,6 +353,14 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
     torch.cuda.synchronize()
     dec_ms = begin.elapsed_time(end) / steps
     res = {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
+    if w.kind == "paged-append":
+        # tokens each timed step attends: every sequence's length after its append
+        base = int(w.lengths.sum())
+        res["kv_bytes_region1"] = sum(base + w.batch * (warmup + s + 1) for s in range(steps)) * \
+            w.kv_bytes_per_token()
+        # region 2 repeats the decode on the state region 1 left (no appends)
+        res["kv_bytes_region2"] = (base + w.batch * (warmup + steps)) * w.kv_bytes_per_token()
+        st.close()
     if w.kind == "pager":
         res["host_us_per_step"] = {k: round(v / (warmup + steps), 1) for k, v in host_us.items()}
         timed = range(warmup, warmup + steps)
@@ -389,6 +435,9 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         if w.kind == "paged":
             pos = np.arange(int(w.lengths[b]))
             return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
+        if w.kind == "paged-append":
+            pos = np.arange(int(w.lengths[b]) + step + 1)
+            return pos, None, w.rows(TENSOR_K, b, pos), w.rows(TENSOR_V, b, pos), w.query(b, step)
         if w.kind == "pager":
             blocks = np.asarray(pager_sets[b][step], dtype=np.int64)
             pos = (blocks[:, None] * w.block_size + np.arange(w.block_size)[None, :]).reshape(-1)
@@ -404,7 +453,7 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         if w.kind == "ring":
             k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
             q = round_store(rope(q_raw, t, w.rope_base), w.dtype)
-        elif w.kind == "paged":
+        elif w.kind in ("paged", "paged-append"):
             k, q = k_raw.astype(np.float64), q_raw.astype(np.float64)
         else:
             k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
@@ -439,8 +488,12 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
                            f"host memory; float64 NumPy, {timed:.1f} s timed; BLAS threads "
                            f"{threads}, elementwise ops on one thread; useful flops of the "
                            f"sampled rows / time")}
-    step_bytes = (len(pager_sets[0][0]) * w.block_size * w.kv_bytes_per_token() * w.batch
-                  if w.kind == "pager" else kv_bytes_per_step(w))
+    if w.kind == "pager":
+        step_bytes = len(pager_sets[0][0]) * w.block_size * w.kv_bytes_per_token() * w.batch
+    elif w.kind == "paged-append":
+        step_bytes = (int(w.lengths.sum()) + w.batch) * w.kv_bytes_per_token()
+    else:
+        step_bytes = kv_bytes_per_step(w)
     return {"value": round(steps_per_s * step_bytes / 1e9, 4), "unit": "GB/s",
             "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
             "sample": (f"{n} (sequence, decode step) samples of {w.name} (sequences in order, "
@@ -530,7 +583,7 @@ def main() -> int:
             out["cpu_baseline"] = cpu_baseline(w)
         print(json.dumps(out), flush=True)
         return 0
-    if w.kind == "pager":
+    if w.kind in ("pager", "paged-append"):
         kv_bytes = res["kv_bytes_region2"]
         ms_per_step = res["total_ms"] / args.steps
         value_gbs = res["kv_bytes_region1"] / (res["total_ms"] / 1e3) / 1e9

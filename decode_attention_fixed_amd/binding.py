@@ -80,6 +80,15 @@ _PROTOS = {
                                          ctypes.c_size_t, _vp]),
     "kv_write_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i32, ctypes.c_float, _i32, _vp]),
+    "swa_blocks_create": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
+    "swa_blocks_destroy": (None, [_vp]),
+    "swa_blocks_reset": (ctypes.c_int, [_vp]),
+    "swa_blocks_sync": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "swa_blocks_share_prefix": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "swa_blocks_free": (ctypes.c_int, [_vp, _i32, _vp, _vp]),
+    "swa_blocks_state": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.POINTER(_i32)]),
+    "kv_append_paged": (ctypes.c_int, [_vp, ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
+                                       _i32, _i32, _vp, _vp, _i32, ctypes.c_float, _i32, _vp]),
     "swa_pager_create": (ctypes.c_int, [ctypes.POINTER(SwaPagerConfig), _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, ctypes.POINTER(_vp)]),
     "swa_pager_reset": (ctypes.c_int, [_vp, _vp]),
@@ -322,6 +331,83 @@ def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tenso
                               _ptr(k_src, "k_src"), _ptr(v_src, "v_src"),
                               _ptr(dst_rows, "dst_rows", torch.int32), _ptr(pos, "pos", torch.int32),
                               k_src.shape[0], rope_base, _STYLE_CODE[rope_style], _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# block manager (refcounted blocks, prefix sharing, copy-on-write)
+# ---------------------------------------------------------------------------
+
+def swa_blocks_create(num_blocks: int, block_size: int, max_seqs: int,
+                      max_blocks_per_seq: int) -> int:
+    handle = _vp()
+    _check("swa_blocks_create", LIB.swa_blocks_create(num_blocks, block_size, max_seqs,
+                                                      max_blocks_per_seq, ctypes.byref(handle)))
+    return handle.value
+
+
+def swa_blocks_destroy(handle: int | None) -> None:
+    LIB.swa_blocks_destroy(handle)
+
+
+def swa_blocks_reset(handle: int) -> None:
+    _check("swa_blocks_reset", LIB.swa_blocks_reset(handle))
+
+
+def swa_blocks_sync(handle: int, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    stream=None) -> None:
+    _check("swa_blocks_sync",
+           LIB.swa_blocks_sync(handle, _ptr(block_table, "block_table", torch.int32),
+                               _ptr(seq_lens, "seq_lens", torch.int32), _stream(stream)))
+
+
+def swa_blocks_share_prefix(handle: int, src: int, dst: int, prefix_len: int,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor,
+                            stream=None) -> None:
+    _check("swa_blocks_share_prefix",
+           LIB.swa_blocks_share_prefix(handle, src, dst, prefix_len,
+                                       _ptr(block_table, "block_table", torch.int32),
+                                       _ptr(seq_lens, "seq_lens", torch.int32), _stream(stream)))
+
+
+def swa_blocks_free(handle: int, seq: int, seq_lens: torch.Tensor, stream=None) -> None:
+    _check("swa_blocks_free",
+           LIB.swa_blocks_free(handle, seq, _ptr(seq_lens, "seq_lens", torch.int32),
+                               _stream(stream)))
+
+
+def swa_blocks_state(handle: int, max_seqs: int, max_blocks: int, num_blocks: int) -> dict:
+    table = (_i32 * (max_seqs * max_blocks))()
+    lens = (_i32 * max_seqs)()
+    refs = (_i32 * num_blocks)()
+    free = _i32()
+    _check("swa_blocks_state",
+           LIB.swa_blocks_state(handle, ctypes.cast(table, _vp), ctypes.cast(lens, _vp),
+                                ctypes.cast(refs, _vp), ctypes.byref(free)))
+    t = list(table)
+    return {"table": [t[i * max_blocks:(i + 1) * max_blocks] for i in range(max_seqs)],
+            "lens": list(lens), "refs": list(refs), "free": free.value}
+
+
+def kv_append_paged(handle: int, desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    block_table: torch.Tensor, seq_lens: torch.Tensor, seqs,
+                    k_new: torch.Tensor, v_new: torch.Tensor, rotate: bool = False,
+                    rope_base: float = 10000.0, rope_style: str = "interleaved",
+                    stream=None) -> None:
+    """k_new, v_new [n_seqs, n_tokens, Hkv, d]; seqs: the n_seqs sequences
+    (a list, or a C int32 array made once for a loop)."""
+    if isinstance(seqs, ctypes.Array):
+        arr, n = seqs, len(seqs)
+    else:
+        n = len(seqs)
+        arr = (_i32 * max(1, n))(*[int(x) for x in seqs])
+    _check("kv_append_paged",
+           LIB.kv_append_paged(handle, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
+                               _ptr(v_pool, "v_pool"),
+                               _ptr(block_table, "block_table", torch.int32),
+                               _ptr(seq_lens, "seq_lens", torch.int32), ctypes.cast(arr, _vp), n,
+                               k_new.shape[1], _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                               1 if rotate else 0, rope_base, _STYLE_CODE[rope_style],
+                               _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -158,9 +158,38 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
     p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
 }
 
+// One token's Hkv rows of K (rotated at pos when `rotate`) and V into pool
+// row r of block blk ([Nphys, Hkv, bs, d]).  Run by a whole workgroup; the
+// caller has checked blk and r.
+template <bool BF16>
+__device__ void write_token_rows(const void* k_src_all, const void* v_src_all, size_t src_token,
+                                 void* k_pool, void* v_pool, int64_t blk, int r, int num_kv_heads,
+                                 int block_size, int d, bool rotate, int32_t pos,
+                                 const RopeFreq& freq, int rope_half, double* s_cos,
+                                 double* s_sin) {
+  using T = typename Elem<BF16>::T;
+  if (rotate) {
+    rope_angles(static_cast<double>(pos), freq, d, s_cos, s_sin);
+    __syncthreads();
+  }
+  const size_t src_row = src_token * num_kv_heads * d;
+  const T* k_src = static_cast<const T*>(k_src_all) + src_row;
+  const T* v_src = static_cast<const T*>(v_src_all) + src_row;
+  // head h of the token goes to row (blk, h, r) of the pool
+  const size_t dst = (static_cast<size_t>(blk) * num_kv_heads * block_size + r) * d;
+  const size_t head_stride = static_cast<size_t>(block_size) * d;
+  T* k_dst = static_cast<T*>(k_pool) + dst;
+  if (rotate)
+    rotate_rows<BF16>(k_src, d, k_dst, head_stride, num_kv_heads, d, rope_half, s_cos, s_sin);
+  else
+    copy_rows16(k_src, d * sizeof(T), k_dst, head_stride * sizeof(T), num_kv_heads,
+                d * sizeof(T));
+  copy_rows16(v_src, d * sizeof(T), static_cast<T*>(v_pool) + dst, head_stride * sizeof(T),
+              num_kv_heads, d * sizeof(T));
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kAppendThreads) void write_paged_kernel(PagedWriteParams p) {
-  using T = typename Elem<BF16>::T;
   __shared__ double s_cos[kMaxHalfDim];
   __shared__ double s_sin[kMaxHalfDim];
 
@@ -171,27 +200,57 @@ __global__ __launch_bounds__(kAppendThreads) void write_paged_kernel(PagedWriteP
   const bool rotate = p.pos != nullptr;
   const int32_t pos = rotate ? p.pos[n] : 0;
   if (pos < 0) return;
-  if (rotate) {
-    rope_angles(static_cast<double>(pos), p.freq, p.head_dim, s_cos, s_sin);
-    __syncthreads();
-  }
-  const int d = p.head_dim;
   const int64_t blk = row / p.block_size;
   const int r = static_cast<int>(row - blk * p.block_size);
-  const size_t src_row = static_cast<size_t>(n) * p.num_kv_heads * d;
-  const T* k_src = static_cast<const T*>(p.k_src) + src_row;
-  const T* v_src = static_cast<const T*>(p.v_src) + src_row;
-  // head h of the token goes to row (blk, h, r) of the pool
-  const size_t dst = (static_cast<size_t>(blk) * p.num_kv_heads * p.block_size + r) * d;
-  const size_t head_stride = static_cast<size_t>(p.block_size) * d;
-  T* k_dst = static_cast<T*>(p.k_pool) + dst;
-  if (rotate)
-    rotate_rows<BF16>(k_src, d, k_dst, head_stride, p.num_kv_heads, d, p.rope_half, s_cos, s_sin);
-  else
-    copy_rows16(k_src, d * sizeof(T), k_dst, head_stride * sizeof(T), p.num_kv_heads,
-                d * sizeof(T));
-  copy_rows16(v_src, d * sizeof(T), static_cast<T*>(p.v_pool) + dst, head_stride * sizeof(T),
-              p.num_kv_heads, d * sizeof(T));
+  write_token_rows<BF16>(p.k_src, p.v_src, static_cast<size_t>(n), p.k_pool, p.v_pool, blk, r,
+                         p.num_kv_heads, p.block_size, p.head_dim, rotate, pos, p.freq,
+                         p.rope_half, s_cos, s_sin);
+}
+
+// Paged append: token j of listed sequence i (workgroup i * n_tokens + j) is
+// at position first_pos[i] + j of sequence seqs[i]; its row is found through
+// the device block table, which the update launch before this one has
+// already extended.
+template <bool BF16>
+__global__ __launch_bounds__(kAppendThreads) void append_paged_kernel(AppendPagedParams p) {
+  __shared__ double s_cos[kMaxHalfDim];
+  __shared__ double s_sin[kMaxHalfDim];
+  const int i = static_cast<int>(blockIdx.x) / p.n_tokens;
+  const int j = static_cast<int>(blockIdx.x) - i * p.n_tokens;
+  if (i >= p.n_seqs) return;
+  const int64_t pos = static_cast<int64_t>(p.first_pos[i]) + j;
+  const int64_t q = pos >> p.block_shift;
+  if (pos < 0 || q >= p.max_blocks) return;
+  const int32_t blk = p.block_table[static_cast<size_t>(p.seqs[i]) * p.max_blocks + q];
+  if (blk < 0 || blk >= p.num_phys_blocks) return;
+  const int r = static_cast<int>(pos & ((int64_t{1} << p.block_shift) - 1));
+  write_token_rows<BF16>(p.k_src, p.v_src, static_cast<size_t>(p.src_first + i) * p.n_tokens + j,
+                         p.k_pool, p.v_pool, blk, r, p.num_kv_heads, 1 << p.block_shift,
+                         p.head_dim, p.rotate != 0, static_cast<int32_t>(pos), p.freq,
+                         p.rope_half, s_cos, s_sin);
+}
+
+// Block-manager updates by value: block-table entries, sequence lengths, and
+// copy-on-write copies of the first `rows` rows of a block (all heads, K and
+// V).  Workgroup 0 writes the entries; workgroup 1 + 2c + t copies tensor t of
+// copy c.
+__global__ __launch_bounds__(kAppendThreads) void blocks_update_kernel(BlocksUpdateParams p) {
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < p.n_table; e += blockDim.x) p.block_table[p.table_idx[e]] = p.table_val[e];
+    for (int e = threadIdx.x; e < p.n_lens; e += blockDim.x) p.seq_lens[p.lens_idx[e]] = p.lens_val[e];
+    return;
+  }
+  const int c = (static_cast<int>(blockIdx.x) - 1) / 2;
+  const int t = (static_cast<int>(blockIdx.x) - 1) % 2;
+  if (c >= p.n_cow) return;
+  const size_t row_bytes = static_cast<size_t>(p.head_dim) * p.elem_bytes;
+  const size_t head_bytes = row_bytes * p.block_size;
+  const size_t block_bytes = head_bytes * p.num_kv_heads;
+  char* base = static_cast<char*>(t == 0 ? p.k_pool : p.v_pool);
+  const char* src = base + static_cast<size_t>(p.cow_src[c]) * block_bytes;
+  char* dst = base + static_cast<size_t>(p.cow_dst[c]) * block_bytes;
+  // rows 0 .. rows-1 of every head: Hkv runs of rows * row_bytes contiguous bytes
+  copy_rows16(src, head_bytes, dst, head_bytes, p.num_kv_heads, row_bytes * p.cow_rows[c]);
 }
 
 __global__ void fill_i32_kernel(int32_t* dst, size_t n, int32_t value) {
@@ -224,6 +283,23 @@ hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
     append_rope_kernel<true><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
   else
     append_rope_kernel<false><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_paged(const AppendPagedParams& p, hipStream_t stream) {
+  if (p.n_seqs <= 0 || p.n_tokens <= 0) return hipSuccess;
+  const size_t grid = static_cast<size_t>(p.n_seqs) * p.n_tokens;
+  if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+  if (p.bf16)
+    append_paged_kernel<true><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p);
+  else
+    append_paged_kernel<false><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks_update(const BlocksUpdateParams& p, hipStream_t stream) {
+  if (p.n_table <= 0 && p.n_lens <= 0 && p.n_cow <= 0) return hipSuccess;
+  blocks_update_kernel<<<1 + 2 * p.n_cow, kAppendThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -180,6 +180,45 @@ int prefill_tokens_per_block(int group);
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// Block manager (refcounted blocks, prefix sharing, copy-on-write): updates
+// of the device block table and lengths and copy-on-write block copies, by
+// value; then the new tokens' rows, found through the updated table.
+constexpr int kBlocksMaxTable = 160;  // block-table entries per update launch
+constexpr int kBlocksMaxLens = 32;    // length entries per update launch
+constexpr int kBlocksMaxCow = 16;     // copy-on-write copies per update launch
+struct BlocksUpdateParams {
+  int32_t* block_table;   // [max_seqs, max_blocks]
+  int32_t* seq_lens;      // [max_seqs]
+  void* k_pool;           // [Nphys, Hkv, bs, d]
+  void* v_pool;
+  int32_t num_kv_heads, block_size, head_dim, elem_bytes;
+  int32_t n_table, n_lens, n_cow;
+  int32_t table_idx[kBlocksMaxTable];
+  int32_t table_val[kBlocksMaxTable];
+  int32_t lens_idx[kBlocksMaxLens];
+  int32_t lens_val[kBlocksMaxLens];
+  int32_t cow_src[kBlocksMaxCow];   // physical block copied from
+  int32_t cow_dst[kBlocksMaxCow];   // physical block copied to
+  int32_t cow_rows[kBlocksMaxCow];  // rows 0 .. rows-1 of every head
+};
+constexpr int kAppendMaxSeqs = 128;  // sequences per paged-append launch
+struct AppendPagedParams {
+  const void* k_src;          // [n_all, n_tokens, Hkv, d]: rows of every listed sequence
+  const void* v_src;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table; // [max_seqs, max_blocks], device
+  int32_t src_first;          // index of this launch's first sequence in k_src / v_src
+  int32_t n_seqs, n_tokens;
+  int32_t num_kv_heads, head_dim, block_shift, max_blocks, num_phys_blocks;
+  int32_t rotate, rope_half, bf16;
+  int32_t seqs[kAppendMaxSeqs];       // sequence of each listed row group
+  int32_t first_pos[kAppendMaxSeqs];  // its length before the call
+  RopeFreq freq;
+};
+hipError_t launch_blocks_update(const BlocksUpdateParams& p, hipStream_t stream);
+hipError_t launch_append_paged(const AppendPagedParams& p, hipStream_t stream);
+
 // Host-pool pager: block copies from pinned host memory, validity updates.
 // The lists travel by value in the kernel arguments, so nothing is staged in
 // memory that a later call could overwrite before the kernel runs.

@@ -11,8 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from synth import (TENSOR_K, TENSOR_Q, TENSOR_V, PagedWorkload, PagerWorkload, PoolWorkload,
-                   RingWorkload)
+from synth import (TENSOR_K, TENSOR_Q, TENSOR_V, PagedAppendWorkload, PagedWorkload,
+                   PagerWorkload, PoolWorkload, RingWorkload)
 from synth.draws import SHARED_SEQUENCE, draw_rows_parallel
 
 from . import binding as B
@@ -308,3 +308,91 @@ class PagerState:
             torch.cuda.synchronize()
             B.swa_pager_destroy(self.handle)
             self.handle = 0
+
+
+class BlockPoolState:
+    """A paged pool driven by the library's block manager (refcounted blocks,
+    prefix sharing, copy-on-write), with the device block table and lengths
+    the decode reads, plus decode buffers."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, max_blocks: int,
+                 num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 device="cuda", out_dtype=torch.float32):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_seqs, self.max_blocks = max_seqs, max_blocks
+        self.dtype = dtype
+        dt = _TORCH_DTYPE[dtype]
+        self.handle = B.swa_blocks_create(num_blocks, block_size, max_seqs, max_blocks)
+        self.desc = B.make_paged_desc(max_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks, num_blocks, dtype)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.k_pool = torch.empty(shape, dtype=dt, device=device)
+        self.v_pool = torch.empty(shape, dtype=dt, device=device)
+        self.block_table = torch.empty((max_seqs, max_blocks), dtype=torch.int32, device=device)
+        self.seq_lens = torch.empty((max_seqs,), dtype=torch.int32, device=device)
+        B.swa_blocks_sync(self.handle, self.block_table, self.seq_lens)
+        self.workspace = B.new_workspace(max_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_blocks * block_size, device)
+        self.out = torch.empty((max_seqs, num_q_heads, head_dim), dtype=out_dtype, device=device)
+        self.lse = torch.empty((max_seqs, num_q_heads), dtype=torch.float32, device=device)
+
+    def append(self, seqs, k: torch.Tensor, v: torch.Tensor, rotate: bool = False,
+               rope_base: float = 10000.0) -> None:
+        B.kv_append_paged(self.handle, self.desc, self.k_pool, self.v_pool, self.block_table,
+                          self.seq_lens, seqs, k, v, rotate, rope_base)
+
+    def share(self, src: int, dst: int, n: int) -> None:
+        B.swa_blocks_share_prefix(self.handle, src, dst, n, self.block_table, self.seq_lens)
+
+    def free(self, seq: int) -> None:
+        B.swa_blocks_free(self.handle, seq, self.seq_lens)
+
+    def state(self) -> dict:
+        return B.swa_blocks_state(self.handle, self.max_seqs, self.max_blocks, self.num_blocks)
+
+    def decode(self, q: torch.Tensor, scale: float = 0.0) -> None:
+        B.decode_attn_paged(self.desc, q, self.k_pool, self.v_pool, self.block_table,
+                            self.seq_lens, None, self.out, self.workspace, self.lse, scale)
+
+    def close(self) -> None:
+        if self.handle:
+            B.swa_blocks_destroy(self.handle)
+            self.handle = 0
+
+
+def build_paged_append(w: PagedAppendWorkload, extra_steps: int = 0,
+                       device="cuda") -> BlockPoolState:
+    """The paged workload built through the block manager: the shared prefix
+    is appended once to a holder sequence (index B), shared by reference into
+    every sequence, the holder is freed (its blocks live on through the
+    references), then each sequence's own tokens are appended.  Room is left
+    for decode_steps + extra_steps appended tokens per sequence."""
+    bs = w.block_size
+    steps = w.decode_steps + extra_steps
+    lens = [int(x) for x in w.lengths]
+    max_blocks = -(-(w.len_range[1] + steps) // bs)
+    own = sum(-(-(n + steps) // bs) - min(-(-n // bs), w.shared_blocks) for n in lens)
+    num_blocks = w.shared_blocks + own + w.batch
+    st = BlockPoolState(num_blocks, bs, w.batch + 1, max_blocks, w.num_q_heads, w.num_kv_heads,
+                        w.head_dim, w.dtype, device)
+    holder = w.batch
+    pre = w.shared_prefix
+
+    def rows(seq, first, n):
+        k = draw_rows_parallel(w.seed, TENSOR_K, seq, first, n, w.num_kv_heads, w.head_dim,
+                               w.scale, w.dtype)
+        v = draw_rows_parallel(w.seed, TENSOR_V, seq, first, n, w.num_kv_heads, w.head_dim,
+                               w.scale, w.dtype)
+        return (to_device(k, w.dtype, device).unsqueeze(0), to_device(v, w.dtype, device).unsqueeze(0))
+
+    k, v = rows(SHARED_SEQUENCE, 0, pre)
+    st.append([holder], k, v)
+    for b in range(w.batch):
+        st.share(holder, b, min(lens[b], pre))
+    st.free(holder)
+    for b in range(w.batch):
+        if lens[b] > pre:
+            k, v = rows(b, pre, lens[b] - pre)
+            st.append([b], k, v)
+    torch.cuda.synchronize()
+    return st

@@ -20,7 +20,7 @@
  *   - Every buffer is owned by the caller.  Device buffers are device
  *     pointers (hipMalloc'ed or equivalent); the library never allocates or
  *     frees device memory.  The only allocations are the opaque host objects
- *     (swa_cache, and swa_pager with its two HIP events).
+ *     (swa_cache, swa_blocks, and swa_pager with its two HIP events).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
  *     are asynchronous on it; work on one stream runs in call order, so an
  *     append followed by a decode on the same stream reads the new token.
@@ -270,6 +270,81 @@ swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool
                           const void* k_src, const void* v_src, const int32_t* dst_rows,
                           const int32_t* pos, int32_t n_tokens, float rope_base,
                           swa_rope_style rope_style, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Block manager: refcounted pool blocks, prefix sharing, copy-on-write      */
+/* ([share] §3.2 prefix sharing, §5.1 allocate / share_prefix / append_token, */
+/* §6.1 release by reference count on every path).                           */
+/* ------------------------------------------------------------------------- */
+
+/* Opaque host object: per-block reference counts, per-sequence block lists
+ * and lengths, and the free list.  Not thread-safe: one thread drives it. */
+typedef struct swa_blocks swa_blocks;
+
+/* A manager of num_blocks pool blocks of block_size tokens (a power of two,
+ * 16..1024) for sequences 0 .. max_seqs-1 of up to max_blocks_per_seq blocks
+ * each.  All blocks start free and every sequence empty.  Host only. */
+swa_status swa_blocks_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                             int32_t max_blocks_per_seq, swa_blocks** out);
+
+/* Frees the host object.  NULL is a no-op. */
+void swa_blocks_destroy(swa_blocks* mgr);
+
+/* Every block free, every sequence empty (host state only; follow with
+ * swa_blocks_sync before the device mirrors are read). */
+swa_status swa_blocks_reset(swa_blocks* mgr);
+
+/* Writes the whole host state into the device mirrors the paged decode reads:
+ *   block_table  [max_seqs, max_blocks_per_seq] int32 (-1 = no block),
+ *   seq_lens     [max_seqs] int32.
+ * Returns when `stream` has done it (a set-up call). */
+swa_status swa_blocks_sync(swa_blocks* mgr, int32_t* block_table, int32_t* seq_lens,
+                           void* stream);
+
+/* The first prefix_len tokens of the empty sequence dst point at src's blocks
+ * (ceil(prefix_len / block_size) of them, each gaining a reference); dst's
+ * length becomes prefix_len.  The device mirrors are updated on `stream`. */
+swa_status swa_blocks_share_prefix(swa_blocks* mgr, int32_t src, int32_t dst, int32_t prefix_len,
+                                   int32_t* block_table, int32_t* seq_lens, void* stream);
+
+/* Ends sequence seq: each of its blocks loses a reference and returns to the
+ * free list when no sequence references it any more; its length becomes 0
+ * (device mirror updated on `stream`). */
+swa_status swa_blocks_free(swa_blocks* mgr, int32_t seq, int32_t* seq_lens, void* stream);
+
+/* Host copies of the state; each output may be NULL:
+ *   table [max_seqs * max_blocks_per_seq], lens [max_seqs],
+ *   refs [num_blocks] reference counts, *free_blocks = free blocks. */
+swa_status swa_blocks_state(const swa_blocks* mgr, int32_t* table, int32_t* lens, int32_t* refs,
+                            int32_t* free_blocks);
+
+/* Appends n_tokens tokens to each listed sequence ([share] §5.1
+ * append_token, blocks allocated on demand).
+ *
+ *   desc          the pool: batch = max_seqs, max_blocks_per_seq, block_size
+ *                 and num_phys_blocks as the manager's; num_kv_heads,
+ *                 head_dim (64 or 128), dtype of the rows.
+ *   k_pool, v_pool, block_table, seq_lens  device, as decode_attn_paged reads
+ *                 them; the table and lengths are updated by this call.
+ *   seqs          [n_seqs] int32, host: distinct sequences.
+ *   k_new, v_new  [n_seqs, n_tokens, Hkv, d], device: row (i, t) is token
+ *                 seq_lens[seqs[i]] + t of sequence seqs[i].
+ *   rotate        nonzero: K is rotated by RoPE at the token's position in
+ *                 its sequence before it is stored (rope_base, rope_style);
+ *                 0: K is stored as given.
+ *
+ * Equivalent to appending the tokens one at a time, sequence by sequence in
+ * the listed order: a token that starts a block takes the lowest-numbered
+ * free block; a token written into a block that another sequence also
+ * references first gets a private copy of that block's used rows
+ * (copy-on-write: a shared block is never written in place).  If the blocks
+ * would not suffice, or a table would overflow, SWA_ERR_INVALID_ARG is
+ * returned and nothing changes.  Two launches or more on `stream`. */
+swa_status kv_append_paged(swa_blocks* mgr, const swa_paged_desc* desc, void* k_pool, void* v_pool,
+                           int32_t* block_table, int32_t* seq_lens, const int32_t* seqs,
+                           int32_t n_seqs, int32_t n_tokens, const void* k_new, const void* v_new,
+                           int32_t rotate, float rope_base, swa_rope_style rope_style,
+                           void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host-pool pager: a sequence's history in host memory, a fixed pool of     */

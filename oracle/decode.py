@@ -17,7 +17,8 @@ Chunked prefill on a ring ([pool] "paging", chunks of 128-256 tokens): a
   steps' outputs.
 Paged workloads (block table with a shared prefix, [share] §3.1-§3.2):
   plain causal attention over all len_b tokens of sequence b; K rows are used
-  as given (no RoPE on this workload).
+  as given (no RoPE on this workload).  Grown by appends ([share] §5.1), step
+  s first appends the token at position len_b + s, then attends.
 Pool workloads (fixed pool + validity mask, [pool] "paging" and "mask"):
   attention over exactly the tokens of the resident blocks; absent blocks
   are as if they did not exist.  Resident K rows carry RoPE at their
@@ -94,6 +95,17 @@ def ring_slot_table(w, b: int, through_step: int | None = None) -> np.ndarray:
 
 def paged_expected(w, b: int, step: int, scale=None):
     n = int(w.lengths[b])
+    pos = np.arange(n, dtype=np.int64)
+    k = w.rows(TENSOR_K, b, pos).astype(np.float64)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)
+
+
+def paged_append_expected(w, b: int, step: int, scale=None):
+    """Paged workload grown by appends: decode step `step` first appends the
+    token at position lengths[b] + step, then attends positions
+    0 .. lengths[b] + step (K as given, no RoPE on this workload)."""
+    n = int(w.lengths[b]) + step + 1
     pos = np.arange(n, dtype=np.int64)
     k = w.rows(TENSOR_K, b, pos).astype(np.float64)
     v = w.rows(TENSOR_V, b, pos).astype(np.float64)

@@ -21,6 +21,7 @@ from .draws import (  # noqa: F401
 )
 from .workloads import (  # noqa: F401
     WORKLOADS,
+    PagedAppendWorkload,
     PagedWorkload,
     PagerWorkload,
     PoolWorkload,

@@ -7,7 +7,8 @@ Three kinds of workload:
   new token and attends).
 * PagedWorkload  - a block-table KV pool (16-token blocks) with ragged lengths
   and a common prompt prefix shared through identical block ids; read-only
-  decode steps with a fresh query per step.
+  decode steps with a fresh query per step.  PagedAppendWorkload: the same
+  contents grown through a block manager, one new token per sequence and step.
 * PoolWorkload   - one long logical context split in 64-token blocks, of which
   only a fixed-size pool of slots is resident; a per-slot validity mask marks
   the filled slots; read-only decode steps.
@@ -220,6 +221,25 @@ class PagedWorkload:
 
 
 @dataclasses.dataclass(frozen=True)
+class PagedAppendWorkload(PagedWorkload):
+    """The paged workload built and grown through a block manager: the shared
+    prefix is written once and shared by reference, every sequence's own
+    tokens are appended, and each decode step first appends one new token per
+    sequence (at position lengths[b] + step, drawn from the sequence's own
+    stream) and then attends over all of them."""
+
+    kind = "paged-append"
+
+    def row_source(self, b: int, positions) -> tuple:
+        """Rows of sequence b: the shared stream for the part of the prefix it
+        shares when built (its first min(lengths[b], shared_prefix) tokens),
+        its own stream for everything after, appended tokens included."""
+        pos = np.asarray(positions, dtype=np.int64)
+        shared = min(int(self.lengths[b]), self.shared_prefix)
+        return np.where(pos < shared, SHARED_SEQUENCE, b), pos
+
+
+@dataclasses.dataclass(frozen=True)
 class PoolWorkload:
     name: str
     seed: int
@@ -408,6 +428,10 @@ WORKLOADS = {
         name="paged", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
         dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
         decode_steps=128),
+    "paged-append": PagedAppendWorkload(
+        name="paged-append", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
+        decode_steps=128),
     "long-pool-b1": PoolWorkload(
         name="long-pool-b1", seed=5, batch=1, num_q_heads=24, num_kv_heads=4, head_dim=128,
         dtype="bf16", block_size=64, logical_blocks=4096, pool_slots=1152,
@@ -430,5 +454,6 @@ def workload(name: str):
     return WORKLOADS[name]
 
 
-__all__ = ["RingWorkload", "PagedWorkload", "PoolWorkload", "PagerWorkload", "WORKLOADS", "workload", "CHUNK",
+__all__ = ["RingWorkload", "PagedWorkload", "PagedAppendWorkload", "PoolWorkload", "PagerWorkload",
+           "WORKLOADS", "workload", "CHUNK",
            "TENSOR_K", "TENSOR_V", "TENSOR_Q"]
