@@ -101,6 +101,8 @@ def describe(w) -> dict:
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.logical_blocks} x {w.block_size}-token "
                 f"logical blocks, pool of {w.pool_slots} slots per sequence")
+    if getattr(w, "cache", "") == "i8":
+        text += "; int8 cache rows (codes + one float32 scale per row, quantised when written)"
     return {"workload": text, "batch": w.batch, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim}
 
@@ -421,6 +423,7 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     import threadpoolctl
 
     from oracle.attention import attend_heads
+    from oracle.decode import stored_rows
     from oracle.ring import resident_positions
     from oracle.rope import rope
     from oracle.rounding import round_store
@@ -451,14 +454,15 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
 
     def oracle_step(pos, t, k_raw, v, q_raw):
         if w.kind == "ring":
-            k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
+            k, v = stored_rows(w, rope(k_raw, pos[:, None], w.rope_base), v)
             q = round_store(rope(q_raw, t, w.rope_base), w.dtype)
         elif w.kind in ("paged", "paged-append"):
-            k, q = k_raw.astype(np.float64), q_raw.astype(np.float64)
-        else:
-            k = round_store(rope(k_raw, pos[:, None], w.rope_base), w.dtype)
+            k, v = stored_rows(w, k_raw.astype(np.float64), v)
             q = q_raw.astype(np.float64)
-        return attend_heads(q, k, v.astype(np.float64))
+        else:
+            k, v = stored_rows(w, rope(k_raw, pos[:, None], w.rope_base), v)
+            q = q_raw.astype(np.float64)
+        return attend_heads(q, k, v)
 
     oracle_step(*inputs(0, 0))  # untimed: first-touch of the arrays and BLAS start-up
     timed, n, step, done, flops = 0.0, 0, 0, False, 0
@@ -606,7 +610,8 @@ def main() -> int:
         "metric": "decode-attention KV-read GB/s", "value": round(value_gbs, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "vs_baseline": None,
+        "dtype": "i8" if getattr(w, "cache", "") == "i8" else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic", "config": describe(w),
         "steps_per_s": round(1e3 / ms_per_step, 1),
         "hbm_frac_of_peak": round(value_gbs / HBM_PEAK_GBS, 4),

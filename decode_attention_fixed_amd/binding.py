@@ -25,11 +25,14 @@ SWA_ERR_HIP = -4
 
 SWA_F32 = 0
 SWA_BF16 = 1
+SWA_I8 = 2
 SWA_ROPE_INTERLEAVED = 0
 SWA_ROPE_HALF = 1
 
 _DTYPE_CODE = {torch.float32: SWA_F32, torch.bfloat16: SWA_BF16}
-_DTYPE_NAME = {"f32": SWA_F32, "bf16": SWA_BF16}
+_DTYPE_NAME = {"f32": SWA_F32, "bf16": SWA_BF16, "i8": SWA_I8}
+# torch dtype of the cache buffers: int8 caches are raw bytes (codes, then scales)
+_BUFFER_DTYPE = {SWA_F32: torch.float32, SWA_BF16: torch.bfloat16, SWA_I8: torch.uint8}
 _STYLE_CODE = {"interleaved": SWA_ROPE_INTERLEAVED, "half": SWA_ROPE_HALF}
 
 
@@ -75,6 +78,8 @@ _PROTOS = {
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "prefill_attn_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          _i32, _vp, _vp, ctypes.c_size_t, _vp]),
+    "swa_pool_required_bytes": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc),
+                                               ctypes.POINTER(ctypes.c_size_t)]),
     "decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
@@ -172,7 +177,7 @@ def swa_cache_required_bytes(cfg: SwaCacheConfig) -> tuple:
 def swa_cache_create(cfg: SwaCacheConfig, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      slot_pos: torch.Tensor) -> int:
     handle = _vp()
-    dt = torch.bfloat16 if cfg.dtype == SWA_BF16 else torch.float32
+    dt = _BUFFER_DTYPE[cfg.dtype]
     _check("swa_cache_create",
            LIB.swa_cache_create(ctypes.byref(cfg), _ptr(k_cache, "k_cache", dt),
                                 _ptr(v_cache, "v_cache", dt), _ptr(slot_pos, "slot_pos", torch.int32),
@@ -279,6 +284,24 @@ def make_paged_desc(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: i
                     dtype: str = "bf16") -> SwaPagedDesc:
     return SwaPagedDesc(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                         max_blocks_per_seq, num_phys_blocks, _DTYPE_NAME[dtype])
+
+
+def swa_pool_required_bytes(desc: SwaPagedDesc) -> int:
+    n = ctypes.c_size_t()
+    _check("swa_pool_required_bytes", LIB.swa_pool_required_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def new_pool(desc: SwaPagedDesc, device="cuda") -> tuple:
+    """(k_pool, v_pool) device buffers for `desc`: [Nphys, Hkv, bs, d] tensors
+    of the element type, or flat byte buffers for int8 pools."""
+    if desc.dtype == SWA_I8:
+        n = swa_pool_required_bytes(desc)
+        return (torch.empty(n, dtype=torch.uint8, device=device),
+                torch.empty(n, dtype=torch.uint8, device=device))
+    shape = (desc.num_phys_blocks, desc.num_kv_heads, desc.block_size, desc.head_dim)
+    dt = _BUFFER_DTYPE[desc.dtype]
+    return torch.empty(shape, dtype=dt, device=device), torch.empty(shape, dtype=dt, device=device)
 
 
 def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
@@ -506,9 +529,13 @@ class RingCache:
                  rope_style: str = "interleaved", device="cuda", stream=None) -> "RingCache":
         cfg = make_config(batch, num_kv_heads, head_dim, window, num_sinks, dtype, rope_base,
                           rope_style)
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         slots = num_sinks + window
-        k = torch.empty((batch, num_kv_heads, slots, head_dim), dtype=tdt, device=device)
+        if cfg.dtype == SWA_I8:  # raw bytes: codes, then one float32 scale per row
+            kv_bytes, _ = swa_cache_required_bytes(cfg)
+            k = torch.empty(kv_bytes, dtype=torch.uint8, device=device)
+        else:
+            k = torch.empty((batch, num_kv_heads, slots, head_dim), dtype=_BUFFER_DTYPE[cfg.dtype],
+                            device=device)
         v = torch.empty_like(k)
         slot_pos = torch.empty((batch, slots), dtype=torch.int32, device=device)
         handle = swa_cache_create(cfg, k, v, slot_pos)

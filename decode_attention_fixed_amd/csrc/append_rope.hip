@@ -253,6 +253,133 @@ __global__ __launch_bounds__(kAppendThreads) void blocks_update_kernel(BlocksUpd
   copy_rows16(src, head_bytes, dst, head_bytes, p.num_kv_heads, row_bytes * p.cow_rows[c]);
 }
 
+// int8 rows ([kvc] §5.1: INT8 cache).  A wave quantises one row of d values:
+// lane l < d/2 holds the row's elements e0 and e1 (a RoPE pair) as float64.
+//   a = max |x|,  s = float32(a / 127),  c = clamp(rint(x / s), -127, 127)
+// (s = 0 gives codes 0).  The scale is stored next to the codes' row.
+__device__ void quantize_row_store(double x0, double x1, bool active, int e0, int e1,
+                                   int8_t* codes, float* scale) {
+  double a = active ? fmax(fabs(x0), fabs(x1)) : 0.0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = fmax(a, __shfl_xor(a, o));
+  const float s = static_cast<float>(a / 127.0);
+  const double sd = static_cast<double>(s);
+  if (active) {
+    double c0 = 0.0, c1 = 0.0;
+    if (sd > 0.0) {
+      c0 = fmin(fmax(rint(x0 / sd), -127.0), 127.0);
+      c1 = fmin(fmax(rint(x1 / sd), -127.0), 127.0);
+    }
+    codes[e0] = static_cast<int8_t>(c0);
+    codes[e1] = static_cast<int8_t>(c1);
+  }
+  if ((threadIdx.x & 63) == 0) *scale = s;
+}
+
+// Elements of RoPE pair i of a row: (2i, 2i+1) or (i, i + d/2).
+__device__ __forceinline__ void pair_elems(int i, int half, int rope_half, int* e0, int* e1) {
+  *e0 = rope_half ? i : 2 * i;
+  *e1 = rope_half ? i + half : 2 * i + 1;
+}
+
+// Ring append into an int8 cache: one workgroup per token, one wave per row
+// (its Hkv K rows, Hkv V rows, and Hq query rows when q_inout is given).  K
+// is rotated at the token's position in float64 and quantised from there; V
+// is quantised from its bf16 values; the query stays bf16, rotated and
+// rounded exactly as the bf16 append does it.  Slot rule, skipping of a
+// token whose slot a later token of the call takes, and slot_pos as in
+// append_rope_kernel.
+__global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams p) {
+  const int token = blockIdx.x;
+  const int b = token / p.n_tokens;
+  const int j = token - b * p.n_tokens;
+  const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
+  if (pos < 0 || pos > INT32_MAX) return;
+  const int d = p.head_dim;
+  const int half = d / 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slots = p.sinks + p.window;
+  const bool overwritten = pos >= p.sinks && j + p.window <= p.n_tokens - 1;
+  const int slot = pos < p.sinks ? static_cast<int>(pos) : p.sinks + static_cast<int>(pos % p.window);
+  const bool active = lane < half;
+  double sn = 0.0, cs = 1.0;
+  if (active) rope_sincos(static_cast<double>(pos), p.freq.theta[lane], &sn, &cs);
+  int e0 = 0, e1 = 0;
+  pair_elems(active ? lane : 0, half, p.rope_half, &e0, &e1);
+  const int q_rows = p.q_inout != nullptr ? p.num_q_heads : 0;
+  const int rows = 2 * p.num_kv_heads + q_rows;
+  for (int r = wave; r < rows; r += kAppendThreads / 64) {
+    if (r < 2 * p.num_kv_heads) {
+      if (overwritten) continue;
+      const bool is_v = r >= p.num_kv_heads;
+      const int h = is_v ? r - p.num_kv_heads : r;
+      const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) +
+                            ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_kv_heads + h) * d;
+      double x0 = 0.0, x1 = 0.0;
+      if (active) {
+        x0 = static_cast<double>(bf16_to_f32(src[e0]));
+        x1 = static_cast<double>(bf16_to_f32(src[e1]));
+        if (!is_v) rope_rotate_pair(x0, x1, cs, sn, &x0, &x1);
+      }
+      const size_t row = (static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot;
+      quantize_row_store(x0, x1, active, e0, e1,
+                         static_cast<int8_t*>(is_v ? p.v_cache : p.k_cache) + row * d,
+                         (is_v ? p.v_scale : p.k_scale) + row);
+      if (!is_v && h == 0 && lane == 0)
+        p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
+    } else if (active) {
+      const int h = r - 2 * p.num_kv_heads;
+      uint16_t* q = static_cast<uint16_t*>(p.q_inout) +
+                    ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
+      double o0, o1;
+      rope_rotate_pair(static_cast<double>(bf16_to_f32(q[e0])),
+                       static_cast<double>(bf16_to_f32(q[e1])), cs, sn, &o0, &o1);
+      q[e0] = f64_to_bf16_rne(o0);
+      q[e1] = f64_to_bf16_rne(o1);
+    }
+  }
+}
+
+// Pool write into int8 pools: one workgroup per token, one wave per K or V
+// row; K rotated at pos[n] first when positions are given.
+__global__ __launch_bounds__(kAppendThreads) void write_paged_i8_kernel(PagedWriteParams p) {
+  const int n = blockIdx.x;
+  const int64_t row = p.dst_rows[n];
+  const int64_t rows_total = static_cast<int64_t>(p.num_phys_blocks) * p.block_size;
+  if (row < 0 || row >= rows_total) return;
+  const bool rotate = p.pos != nullptr;
+  const int32_t pos = rotate ? p.pos[n] : 0;
+  if (pos < 0) return;
+  const int d = p.head_dim;
+  const int half = d / 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const bool active = lane < half;
+  double sn = 0.0, cs = 1.0;
+  if (rotate && active) rope_sincos(static_cast<double>(pos), p.freq.theta[lane], &sn, &cs);
+  int e0 = 0, e1 = 0;
+  pair_elems(active ? lane : 0, half, p.rope_half, &e0, &e1);
+  const int64_t blk = row / p.block_size;
+  const int rr = static_cast<int>(row - blk * p.block_size);
+  for (int r = wave; r < 2 * p.num_kv_heads; r += kAppendThreads / 64) {
+    const bool is_v = r >= p.num_kv_heads;
+    const int h = is_v ? r - p.num_kv_heads : r;
+    const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_src : p.k_src) +
+                          (static_cast<size_t>(n) * p.num_kv_heads + h) * d;
+    double x0 = 0.0, x1 = 0.0;
+    if (active) {
+      x0 = static_cast<double>(bf16_to_f32(src[e0]));
+      x1 = static_cast<double>(bf16_to_f32(src[e1]));
+      if (!is_v && rotate) rope_rotate_pair(x0, x1, cs, sn, &x0, &x1);
+    }
+    const size_t out_row = (static_cast<size_t>(blk) * p.num_kv_heads + h) * p.block_size + rr;
+    quantize_row_store(x0, x1, active, e0, e1,
+                       static_cast<int8_t*>(is_v ? p.v_pool : p.k_pool) + out_row * d,
+                       (is_v ? p.v_scale : p.k_scale) + out_row);
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* dst, size_t n, int32_t value) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -283,6 +410,20 @@ hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
     append_rope_kernel<true><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
   else
     append_rope_kernel<false><<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, items, wgs);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream) {
+  const size_t grid = static_cast<size_t>(p.batch) * p.n_tokens;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+  append_i8_kernel<<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_paged_i8(const PagedWriteParams& p, hipStream_t stream) {
+  if (p.n_tokens <= 0) return hipSuccess;
+  write_paged_i8_kernel<<<static_cast<unsigned>(p.n_tokens), kAppendThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

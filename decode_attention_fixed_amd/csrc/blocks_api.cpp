@@ -239,6 +239,8 @@ swa_status kv_append_paged(swa_blocks* m, const swa_paged_desc* desc, void* k_po
       desc->num_phys_blocks != m->num_blocks || desc->block_size != m->block_size)
     return fail(SWA_ERR_INVALID_ARG, "desc (batch, max_blocks_per_seq, num_phys_blocks, "
                                      "block_size) must match the manager");
+  if (desc->dtype == SWA_I8)
+    return fail(SWA_ERR_UNSUPPORTED, "kv_append_paged: int8 pools are not supported");
   if (desc->num_kv_heads < 1 || (desc->head_dim != 64 && desc->head_dim != 128) ||
       (desc->dtype != SWA_F32 && desc->dtype != SWA_BF16))
     return fail(SWA_ERR_INVALID_ARG, "desc: num_kv_heads >= 1, head_dim 64 or 128, f32 or bf16");

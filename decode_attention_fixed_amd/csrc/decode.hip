@@ -37,19 +37,25 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr int kNumSteps = 8;  // load instructions per tensor per tile
 
-template <bool BF16, int D>
+// Stored element kinds: float32, bf16, int8 codes with one float32 scale per
+// row (queries are bf16 for int8 caches).
+enum Kind { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+template <int KIND, int D>
 struct Geo {
-  static constexpr int kElemBytes = BF16 ? 2 : 4;
-  static constexpr int kEPL = 16 / kElemBytes;  // elements per lane per row
+  static constexpr int kElemBytes = KIND == kF32 ? 4 : (KIND == kBF16 ? 2 : 1);
+  // elements per lane per row: one 16-byte load (8-byte loads for int8, which
+  // keeps the per-lane query and accumulator slices at 8 elements)
+  static constexpr int kEPL = KIND == kI8 ? 8 : 16 / kElemBytes;
   static constexpr int kLPR = D / kEPL;         // lanes per row
   static constexpr int kRPI = 64 / kLPR;        // rows per wave load instruction
   static_assert(kLPR >= 1 && kLPR <= 64 && 64 % kLPR == 0, "row must split evenly over a wave");
 };
 
-template <bool BF16>
+template <int KIND>
 struct Unpack;
 template <>
-struct Unpack<true> {
+struct Unpack<kBF16> {
   __device__ static void run(const Vec16& v, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -59,12 +65,50 @@ struct Unpack<true> {
   }
 };
 template <>
-struct Unpack<false> {
+struct Unpack<kF32> {
   __device__ static void run(const Vec16& v, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v.w[i]);
   }
 };
+template <>
+struct Unpack<kI8> {  // 8 signed bytes in w[0], w[1]; exact in float
+  __device__ static void run(const Vec16& v, float* x) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[4 * i + k] = static_cast<float>(static_cast<int8_t>((v.w[i] >> (8 * k)) & 0xffu));
+  }
+};
+
+// One lane's slice of a row: 16 bytes, or 8 for int8.
+template <int KIND>
+__device__ __forceinline__ Vec16 load_slice(const void* p) {
+  if constexpr (KIND == kI8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    Vec16 r;
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+    r.w[2] = 0u;
+    r.w[3] = 0u;
+    return r;
+  } else {
+    return load16(p);
+  }
+}
+
+// The EPL query elements of one lane: bf16 for bf16 and int8 caches.
+template <int KIND, int EPL>
+__device__ void load_q(const void* q, size_t elem, float* x) {
+  if constexpr (KIND == kF32) {
+    Unpack<kF32>::run(load16(static_cast<const float*>(q) + elem), x);
+  } else {
+#pragma unroll
+    for (int c = 0; c < EPL; c += 8)
+      Unpack<kBF16>::run(load16(static_cast<const uint16_t*>(q) + elem + c), x + c);
+  }
+}
 
 // Ring cache: token index = slot; resident iff the slot holds a position.
 struct RingAddr {
@@ -97,10 +141,12 @@ struct PoolAddr {
   }
 };
 
-template <bool BF16, int D, int G, class Addr>
+template <int KIND, int D, int G, class Addr>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
-  using Gm = Geo<BF16, D>;
-  using T = std::conditional_t<BF16, uint16_t, float>;
+  using Gm = Geo<KIND, D>;
+  using T = std::conditional_t<KIND == kF32, float, std::conditional_t<KIND == kBF16, uint16_t, int8_t>>;
+  constexpr bool I8 = KIND == kI8;
+  constexpr int kShiftD = D == 64 ? 6 : 7;  // row index = element offset >> kShiftD
   constexpr int EPL = Gm::kEPL, LPR = Gm::kLPR, RPI = Gm::kRPI;
   constexpr int TILE = RPI * kNumSteps;
 
@@ -126,8 +172,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 
   float q[G][EPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-    Unpack<BF16>::run(load16(static_cast<const T*>(p.q) + (head0 + g) * D + cl * EPL), q[g]);
+  for (int g = 0; g < G; ++g) load_q<KIND, EPL>(p.q, (head0 + g) * D + cl * EPL, q[g]);
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -144,21 +189,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   for (int ts = t0; ts < t1; ts += TILE) {
     Vec16 kr[kNumSteps], vr[kNumSteps];
     bool ok[kNumSteps];
+    float ksc[kNumSteps], vsc[kNumSteps];  // int8: the rows' scales
 #pragma unroll
     for (int i = 0; i < kNumSteps; ++i) {
       const int t = ts + i * RPI + rl;
       const bool in = t < t1;
       size_t off;
       ok[i] = Addr::template row<D>(p, b, kvh, in ? t : t0, off) && in;
-      kr[i] = load16(kbase + off);
-      vr[i] = load16(vbase + off);
+      kr[i] = load_slice<KIND>(kbase + off);
+      vr[i] = load_slice<KIND>(vbase + off);
+      if constexpr (I8) {
+        ksc[i] = p.k_scale[off >> kShiftD];
+        vsc[i] = p.v_scale[off >> kShiftD];
+      }
     }
 
     float s[G][kNumSteps];
 #pragma unroll
     for (int i = 0; i < kNumSteps; ++i) {
       float kx[EPL];
-      Unpack<BF16>::run(kr[i], kx);
+      Unpack<KIND>::run(kr[i], kx);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float a = 0.f;
@@ -166,6 +216,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
         for (int e = 0; e < EPL; ++e) a = fmaf(q[g][e], kx[e], a);
 #pragma unroll
         for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o);
+        if constexpr (I8) a *= ksc[i];  // <q, c * s> = s <q, c>
         s[g][i] = ok[i] ? a : kNegInf;
       }
     }
@@ -199,13 +250,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kNumSteps; ++i) {
       float vx[EPL];
-      Unpack<BF16>::run(vr[i], vx);
+      Unpack<KIND>::run(vr[i], vx);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) vx[e] = ok[i] ? vx[e] : 0.f;
+      // int8: the row's V scale joins the weight (selected, so that the
+      // scale of an absent row, whatever it holds, never reaches arithmetic)
+      const float vs = I8 ? (ok[i] ? vsc[i] : 0.f) : 1.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        const float w = I8 ? pr[g][i] * vs : pr[g][i];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[g][i], vx[e], acc[g][e]);
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(w, vx[e], acc[g][e]);
+      }
     }
   }
 
@@ -284,14 +340,14 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeParams p) {
   if (p.lse != nullptr && lane == 0) p.lse[bh] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
 }
 
-template <bool BF16, int D, class Addr>
+template <int KIND, int D, class Addr>
 hipError_t launch_split(const DecodeParams& p, int g, hipStream_t stream) {
   const unsigned grid =
       static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
   switch (g) {
 #define SWA_CASE(G)                                                             \
   case G:                                                                       \
-    decode_split_kernel<BF16, D, G, Addr><<<grid, 64, 0, stream>>>(p);          \
+    decode_split_kernel<KIND, D, G, Addr><<<grid, 64, 0, stream>>>(p);          \
     break;
     SWA_CASE(1)
     SWA_CASE(2)
@@ -310,12 +366,15 @@ template <class Addr>
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int g = p.num_q_heads / p.num_kv_heads;
   hipError_t err;
-  if (p.bf16)
-    err = p.head_dim == 64 ? launch_split<true, 64, Addr>(p, g, stream)
-                           : launch_split<true, 128, Addr>(p, g, stream);
+  if (p.i8)
+    err = p.head_dim == 64 ? launch_split<kI8, 64, Addr>(p, g, stream)
+                           : launch_split<kI8, 128, Addr>(p, g, stream);
+  else if (p.bf16)
+    err = p.head_dim == 64 ? launch_split<kBF16, 64, Addr>(p, g, stream)
+                           : launch_split<kBF16, 128, Addr>(p, g, stream);
   else
-    err = p.head_dim == 64 ? launch_split<false, 64, Addr>(p, g, stream)
-                           : launch_split<false, 128, Addr>(p, g, stream);
+    err = p.head_dim == 64 ? launch_split<kF32, 64, Addr>(p, g, stream)
+                           : launch_split<kF32, 128, Addr>(p, g, stream);
   if (err != hipSuccess) return err;
   const unsigned grid = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   if (p.head_dim == 64)

@@ -81,6 +81,7 @@ swa_status check_config(const swa_pager_config* c) {
       c->num_phys_blocks < 1)
     return fail(SWA_ERR_INVALID_ARG, "batch, num_kv_heads, logical_blocks, slots_per_seq and "
                                      "num_phys_blocks must be >= 1");
+  if (c->dtype == SWA_I8) return fail(SWA_ERR_UNSUPPORTED, "the pager moves f32 or bf16 blocks");
   if (c->dtype != SWA_F32 && c->dtype != SWA_BF16)
     return fail(SWA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
   if (c->head_dim != 64 && c->head_dim != 128)

@@ -20,6 +20,10 @@ struct swa_cache {
   void* k;
   void* v;
   int32_t* slot_pos;
+  size_t rows() const {
+    return static_cast<size_t>(cfg.batch) * cfg.num_kv_heads *
+           (static_cast<size_t>(cfg.num_sinks) + cfg.window);
+  }
 };
 
 namespace {
@@ -48,9 +52,22 @@ swa_status from_hip(hipError_t err, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t elem_bytes(swa_dtype t) { return t == SWA_BF16 ? 2 : 4; }
+size_t elem_bytes(swa_dtype t) { return t == SWA_F32 ? 4 : 2; }  // rows given / queries
 
-bool dtype_valid(swa_dtype t) { return t == SWA_F32 || t == SWA_BF16; }
+bool dtype_valid(swa_dtype t) { return t == SWA_F32 || t == SWA_BF16 || t == SWA_I8; }
+
+bool out_dtype_valid(swa_dtype t) { return t == SWA_F32 || t == SWA_BF16; }
+
+// Bytes of one K (or V) buffer of `rows` rows of d elements of `t`.
+size_t rows_bytes(swa_dtype t, size_t rows, int32_t d) {
+  if (t == SWA_I8) return swa::i8_codes_bytes(rows, d) + rows * sizeof(float);
+  return rows * static_cast<size_t>(d) * (t == SWA_BF16 ? 2 : 4);
+}
+
+// Scales of an int8 buffer of `rows` rows: after the padded codes.
+float* i8_scales(void* buf, size_t rows, int32_t d) {
+  return reinterpret_cast<float*>(static_cast<char*>(buf) + swa::i8_codes_bytes(rows, d));
+}
 
 bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
 
@@ -89,7 +106,7 @@ swa_status check_decode_common(const void* q, void* out, swa_dtype out_dtype, fl
                                void* workspace, size_t workspace_bytes, size_t need) {
   if (q == nullptr) return fail(SWA_ERR_INVALID_ARG, "q is NULL");
   if (out == nullptr) return fail(SWA_ERR_INVALID_ARG, "out is NULL");
-  if (!dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!out_dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(SWA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(SWA_ERR_INVALID_ARG, "lse misaligned");
@@ -154,8 +171,8 @@ swa_status swa_cache_required_bytes(const swa_cache_config* cfg, size_t* kv_byte
   if (kv_bytes_each == nullptr || slot_pos_bytes == nullptr)
     return fail(SWA_ERR_INVALID_ARG, "output pointer is NULL");
   const size_t slots = static_cast<size_t>(cfg->num_sinks) + cfg->window;
-  *kv_bytes_each = static_cast<size_t>(cfg->batch) * cfg->num_kv_heads * slots * cfg->head_dim *
-                   elem_bytes(cfg->dtype);
+  *kv_bytes_each = rows_bytes(cfg->dtype, static_cast<size_t>(cfg->batch) * cfg->num_kv_heads * slots,
+                              cfg->head_dim);
   *slot_pos_bytes = static_cast<size_t>(cfg->batch) * slots * sizeof(int32_t);
   return ok();
 }
@@ -222,7 +239,13 @@ swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new
   p.sinks = cache->cfg.num_sinks;
   p.freq = swa::make_rope_freq(cache->cfg.rope_base, cache->cfg.head_dim);
   p.rope_half = cache->cfg.rope_style == SWA_ROPE_HALF;
-  p.bf16 = cache->cfg.dtype == SWA_BF16;
+  p.bf16 = cache->cfg.dtype != SWA_F32;
+  if (cache->cfg.dtype == SWA_I8) {
+    p.i8 = 1;
+    p.k_scale = i8_scales(cache->k, cache->rows(), cache->cfg.head_dim);
+    p.v_scale = i8_scales(cache->v, cache->rows(), cache->cfg.head_dim);
+    return from_hip(swa::launch_append_i8(p, static_cast<hipStream_t>(stream)), "kv_append_rope");
+  }
   return from_hip(swa::launch_append_rope(p, static_cast<hipStream_t>(stream)), "kv_append_rope");
 }
 
@@ -276,6 +299,11 @@ static swa_status ring_decode_params(const swa_cache* cache, const void* q, int3
   p.lse = lse;
   p.out_bf16 = out_dtype == SWA_BF16;
   p.bf16 = cfg.dtype == SWA_BF16;
+  if (cfg.dtype == SWA_I8) {
+    p.i8 = 1;
+    p.k_scale = i8_scales(cache->k, cache->rows(), cfg.head_dim);
+    p.v_scale = i8_scales(cache->v, cache->rows(), cfg.head_dim);
+  }
   p.sinks = cfg.num_sinks;
   p.window = cfg.window;
   p.rope_half = cfg.rope_style == SWA_ROPE_HALF;
@@ -320,7 +348,7 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
   // then the decode over that copy.
   void* q_copy = static_cast<char*>(workspace) + lay.q_offset;
   const size_t q_bytes = static_cast<size_t>(p.batch) * num_q_heads * p.head_dim *
-                         (p.bf16 ? sizeof(uint16_t) : sizeof(float));
+                         (p.bf16 || p.i8 ? sizeof(uint16_t) : sizeof(float));
   hipError_t err = hipMemcpyAsync(q_copy, q, q_bytes, hipMemcpyDeviceToDevice, s);
   if (err != hipSuccess) return from_hip(err, "decode_step_ring");
   swa::AppendParams a{};
@@ -340,8 +368,15 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
   a.sinks = p.sinks;
   a.freq = p.freq;
   a.rope_half = p.rope_half;
-  a.bf16 = p.bf16;
-  err = swa::launch_append_rope(a, s);
+  a.bf16 = p.bf16 || p.i8;
+  if (p.i8) {
+    a.i8 = 1;
+    a.k_scale = const_cast<float*>(p.k_scale);
+    a.v_scale = const_cast<float*>(p.v_scale);
+    err = swa::launch_append_i8(a, s);
+  } else {
+    err = swa::launch_append_rope(a, s);
+  }
   if (err != hipSuccess) return from_hip(err, "decode_step_ring");
   p.q = q_copy;
   return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
@@ -474,6 +509,17 @@ static swa_status check_paged_desc(const swa_paged_desc* d) {
   return SWA_OK;
 }
 
+swa_status swa_pool_required_bytes(const swa_paged_desc* desc, size_t* kv_bytes_each) {
+  swa_status st = check_paged_desc(desc);
+  if (st != SWA_OK) return st;
+  if (kv_bytes_each == nullptr) return fail(SWA_ERR_INVALID_ARG, "kv_bytes_each is NULL");
+  *kv_bytes_each = rows_bytes(desc->dtype,
+                              static_cast<size_t>(desc->num_phys_blocks) * desc->num_kv_heads *
+                                  desc->block_size,
+                              desc->head_dim);
+  return ok();
+}
+
 swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table,
                              const int32_t* seq_lens, const uint8_t* block_valid, float scale,
@@ -521,6 +567,13 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
   p.lse = lse;
   p.out_bf16 = out_dtype == SWA_BF16;
   p.bf16 = desc->dtype == SWA_BF16;
+  if (desc->dtype == SWA_I8) {
+    const size_t rows = static_cast<size_t>(desc->num_phys_blocks) * desc->num_kv_heads *
+                        desc->block_size;
+    p.i8 = 1;
+    p.k_scale = i8_scales(const_cast<void*>(k_pool), rows, desc->head_dim);
+    p.v_scale = i8_scales(const_cast<void*>(v_pool), rows, desc->head_dim);
+  }
   fill_workspace_ptrs(p, workspace, lay);
   return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream)),
                   "decode_attn_paged");
@@ -558,7 +611,16 @@ swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool
   p.num_phys_blocks = desc->num_phys_blocks;
   p.freq = swa::make_rope_freq(rope_base, desc->head_dim);
   p.rope_half = rope_style == SWA_ROPE_HALF;
-  p.bf16 = desc->dtype == SWA_BF16;
+  p.bf16 = desc->dtype != SWA_F32;
+  if (desc->dtype == SWA_I8) {
+    const size_t rows = static_cast<size_t>(desc->num_phys_blocks) * desc->num_kv_heads *
+                        desc->block_size;
+    p.i8 = 1;
+    p.k_scale = i8_scales(k_pool, rows, desc->head_dim);
+    p.v_scale = i8_scales(v_pool, rows, desc->head_dim);
+    return from_hip(swa::launch_write_paged_i8(p, static_cast<hipStream_t>(stream)),
+                    "kv_write_paged");
+  }
   return from_hip(swa::launch_write_paged(p, static_cast<hipStream_t>(stream)), "kv_write_paged");
 }
 

@@ -54,7 +54,10 @@ struct AppendParams {
   int32_t batch, n_tokens, num_kv_heads, num_q_heads, head_dim, window, sinks;
   RopeFreq freq;
   int rope_half;          // 0: pairs (2i, 2i+1); 1: pairs (i, i + d/2)
-  int bf16;               // storage dtype
+  int bf16;               // storage dtype (inputs and queries: bf16 also when i8)
+  int i8;                 // int8 rows: codes in k_cache / v_cache, scales below
+  float* k_scale;         // [B, Hkv, S+W] (i8)
+  float* v_scale;
 };
 
 struct PagedWriteParams {
@@ -68,7 +71,19 @@ struct PagedWriteParams {
   RopeFreq freq;
   int rope_half;
   int bf16;
+  int i8;                 // int8 rows (sources bf16): codes in the pools, scales below
+  float* k_scale;         // [Nphys, Hkv, bs] (i8)
+  float* v_scale;
 };
+
+// int8 row storage: codes of all rows first, padded to 256 bytes, then one
+// float32 scale per row.
+inline size_t i8_codes_bytes(size_t rows, int head_dim) {
+  return (rows * static_cast<size_t>(head_dim) + 255) / 256 * 256;
+}
+inline size_t i8_buffer_bytes(size_t rows, int head_dim) {
+  return i8_codes_bytes(rows, head_dim) + rows * sizeof(float);
+}
 
 // One decode step, both addressing modes.  The split kernel writes one
 // partial (normalised output, base-2 log-sum-exp) per (sequence, query head,
@@ -93,6 +108,9 @@ struct DecodeParams {
   float* lse;                 // [B, Hq] or null
   int out_bf16;
   int bf16;
+  int i8;                     // int8 rows with per-row scales (queries bf16)
+  const float* k_scale;       // scale of each row, in the row order of k / v
+  const float* v_scale;
   // Fused decode step (ring): the new token of each sequence is appended by
   // the decode launch itself.  new_pos null: plain decode.
   const void* k_new;          // [B, Hkv, d], not rotated
@@ -131,6 +149,8 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
 
 hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream);
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream);
+hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream);
+hipError_t launch_write_paged_i8(const PagedWriteParams& p, hipStream_t stream);
 hipError_t launch_write_paged(const PagedWriteParams& p, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);

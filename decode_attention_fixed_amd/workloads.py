@@ -36,7 +36,7 @@ class RingState:
         self.w = w
         self.device = device
         self.cache = B.RingCache.allocate(w.batch, w.num_kv_heads, w.head_dim, w.window, w.sinks,
-                                          w.dtype, w.rope_base, rope_style, device)
+                                          w.cache or w.dtype, w.rope_base, rope_style, device)
         self.workspace = self.cache.workspace(w.num_q_heads)
         self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=out_dtype,
                                device=device)
@@ -128,7 +128,6 @@ class PagedState:
     def __init__(self, w, device="cuda", out_dtype=torch.float32, rope_style="interleaved"):
         self.w = w
         self.device = device
-        dt = _TORCH_DTYPE[w.dtype]
         if isinstance(w, PagedWorkload):
             table = w.block_table
             self.num_phys = w.num_unique_blocks
@@ -142,10 +141,9 @@ class PagedState:
         else:
             raise TypeError(type(w))
         self.desc = B.make_paged_desc(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                      w.block_size, table.shape[1], self.num_phys, w.dtype)
-        shape = (self.num_phys, w.num_kv_heads, w.block_size, w.head_dim)
-        self.k_pool = torch.empty(shape, dtype=dt, device=device)
-        self.v_pool = torch.empty(shape, dtype=dt, device=device)
+                                      w.block_size, table.shape[1], self.num_phys,
+                                      w.cache or w.dtype)
+        self.k_pool, self.v_pool = B.new_pool(self.desc, device)
         self.block_table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(device)
         self.seq_lens = torch.from_numpy(lens.astype(np.int32)).to(device)
         self.block_valid = (torch.from_numpy(np.ascontiguousarray(valid)).to(device)

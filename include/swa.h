@@ -52,7 +52,15 @@ typedef enum swa_status {
   SWA_ERR_HIP = -4          /* the HIP runtime reported an error           */
 } swa_status;
 
-typedef enum swa_dtype { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+/* Element types of cached K / V rows.  SWA_I8 ([kvc] §5.1: quantise the
+ * cache to INT8, half the bytes of 16-bit rows): every stored row (one head
+ * of one token, d values) is int8 codes c with one float32 scale s,
+ * s = float32(max|x| / 127), c = clamp(rint(x / s), -127, 127), value c * s.
+ * A K / V buffer of SWA_I8 holds all rows' codes first (their total padded
+ * to a multiple of 256 bytes), then all rows' scales in the same row order.
+ * With SWA_I8 caches the queries and the new rows handed to appends and
+ * writes are bf16; the rows are quantised when they are stored. */
+typedef enum swa_dtype { SWA_F32 = 0, SWA_BF16 = 1, SWA_I8 = 2 } swa_dtype;
 
 /* RoPE pairing: coordinates (2i, 2i+1) or (i, i + d/2) rotate together by
  * angle pos * base^(-2i/d).  The pages name RoPE without fixing a pairing. */
@@ -68,7 +76,7 @@ typedef struct swa_cache_config {
   int32_t head_dim;       /* d: 64 or 128 */
   int32_t window;         /* W >= 1: last W positions kept ([ring] §2.2) */
   int32_t num_sinks;      /* S >= 0: first S positions kept forever ([sink], S = 4) */
-  swa_dtype dtype;        /* storage dtype of K, V and of queries */
+  swa_dtype dtype;        /* storage dtype of K, V (and of queries, bf16 for SWA_I8) */
   float rope_base;        /* > 0, e.g. 10000 */
   swa_rope_style rope_style;
 } swa_cache_config;
@@ -78,7 +86,8 @@ typedef struct swa_cache swa_cache;
 
 /* Bytes the caller must allocate for the cache of `cfg`:
  *   K and V, each  [B, Hkv, S+W, d]  elements of cfg->dtype (head-major, so
- *                   one head's slots are contiguous rows of d elements);
+ *                   one head's slots are contiguous rows of d elements; for
+ *                   SWA_I8 the codes, then [B, Hkv, S+W] float32 scales);
  *   slot_pos       [B, S+W] int32, the absolute position held by each slot,
  *                   -1 when empty ([ring] §3.2: a cache slot must remember its
  *                   true position, the slot index is not the position). */
@@ -230,6 +239,12 @@ typedef struct swa_paged_desc {
   swa_dtype dtype;            /* pool and query dtype */
 } swa_paged_desc;
 
+/* Bytes of each of the K and V pools of `desc`: [num_phys_blocks, Hkv,
+ * block_size, d] elements of desc->dtype; for SWA_I8 the codes, padded to a
+ * multiple of 256 bytes, then [num_phys_blocks, Hkv, block_size] float32
+ * scales. */
+swa_status swa_pool_required_bytes(const swa_paged_desc* desc, size_t* kv_bytes_each);
+
 /* One decode step over a paged pool ([share] §3.1 block table; [pool]
  * "paging" and "the kernel forgets absent blocks").
  *
@@ -242,6 +257,8 @@ typedef struct swa_paged_desc {
  *                   [0, max_blocks_per_seq * block_size]).
  *   block_valid     [B, max_blocks_per_seq] uint8, device, or NULL (all
  *                   valid): 0 marks a slot whose block is absent.
+ *   (for SWA_I8 pools the query is bf16 and each pool holds codes then
+ *   scales, swa_pool_required_bytes.)
  *
  * Resident rows of sequence b: tokens i < seq_lens[b] whose entry
  * j = i / block_size is valid and names a block in [0, num_phys_blocks);
@@ -339,7 +356,8 @@ swa_status swa_blocks_state(const swa_blocks* mgr, int32_t* table, int32_t* lens
  * references first gets a private copy of that block's used rows
  * (copy-on-write: a shared block is never written in place).  If the blocks
  * would not suffice, or a table would overflow, SWA_ERR_INVALID_ARG is
- * returned and nothing changes.  Two launches or more on `stream`. */
+ * returned and nothing changes.  Two launches or more on `stream`.  SWA_I8
+ * pools are not supported here (SWA_ERR_UNSUPPORTED). */
 swa_status kv_append_paged(swa_blocks* mgr, const swa_paged_desc* desc, void* k_pool, void* v_pool,
                            int32_t* block_table, int32_t* seq_lens, const int32_t* seqs,
                            int32_t n_seqs, int32_t n_tokens, const void* k_new, const void* v_new,
@@ -359,7 +377,7 @@ typedef struct swa_pager_config {
   int32_t logical_blocks;  /* L: blocks of each sequence's history in the host store */
   int32_t slots_per_seq;   /* C: device slots of each sequence (columns of block_table) */
   int32_t num_phys_blocks; /* blocks in the device pool */
-  swa_dtype dtype;         /* K / V element type */
+  swa_dtype dtype;         /* K / V element type: SWA_F32 or SWA_BF16 */
 } swa_pager_config;
 
 /* Opaque host object: the LRU state of every slot, the caller's pointers and

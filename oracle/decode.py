@@ -19,6 +19,8 @@ Paged workloads (block table with a shared prefix, [share] §3.1-§3.2):
   plain causal attention over all len_b tokens of sequence b; K rows are used
   as given (no RoPE on this workload).  Grown by appends ([share] §5.1), step
   s first appends the token at position len_b + s, then attends.
+int8 caches ([kvc] §5.1, oracle/quant.py): every stored row is quantised
+  on its own (absmax scale); attention reads code * scale.
 Pool workloads (fixed pool + validity mask, [pool] "paging" and "mask"):
   attention over exactly the tokens of the resident blocks; absent blocks
   are as if they did not exist.  Resident K rows carry RoPE at their
@@ -37,18 +39,29 @@ from synth import TENSOR_K, TENSOR_Q, TENSOR_V
 
 from .attention import attend_heads
 from .paging import LruPool
+from .quant import quantize_dequantize
 from .ring import resident_positions, simulate_appends
 from .rope import rope
 from .rounding import round_store
 
 
+def stored_rows(w, k_rot, v):
+    """What the cache holds, as float64: int8 caches hold every row quantised
+    with its own scale (oracle/quant.py; K from its float64 rotation, V from
+    its given values); other caches hold K rounded to the storage dtype and
+    V as given."""
+    if getattr(w, "cache", "") == "i8":
+        return quantize_dequantize(k_rot), quantize_dequantize(np.asarray(v, dtype=np.float64))
+    return round_store(k_rot, w.dtype), np.asarray(v, dtype=np.float64)
+
+
 def ring_rows(w, b: int, positions, style: str = "interleaved"):
-    """Cached (K, V) rows of sequence b at absolute positions: K rotated + rounded."""
+    """Cached (K, V) rows of sequence b at absolute positions: K rotated, then
+    stored (rounded, or quantised for int8 caches)."""
     pos = np.asarray(positions, dtype=np.int64)
     k_raw = w.rows(TENSOR_K, b, pos)
-    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
-    k = round_store(rope(k_raw, pos[:, None], w.rope_base, style), w.dtype)
-    return k, v
+    v = w.rows(TENSOR_V, b, pos)
+    return stored_rows(w, rope(k_raw, pos[:, None], w.rope_base, style), v)
 
 
 def ring_query(w, b: int, t: int, style: str = "interleaved") -> np.ndarray:
@@ -96,8 +109,8 @@ def ring_slot_table(w, b: int, through_step: int | None = None) -> np.ndarray:
 def paged_expected(w, b: int, step: int, scale=None):
     n = int(w.lengths[b])
     pos = np.arange(n, dtype=np.int64)
-    k = w.rows(TENSOR_K, b, pos).astype(np.float64)
-    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    k, v = stored_rows(w, w.rows(TENSOR_K, b, pos).astype(np.float64),
+                       w.rows(TENSOR_V, b, pos))
     return attend_heads(w.query(b, step).astype(np.float64), k, v, scale)
 
 
@@ -116,8 +129,7 @@ def pool_rows(w, b: int, style: str = "interleaved"):
     """(positions, K rotated + rounded, V) of sequence b's resident tokens."""
     pos = w.resident_positions(b)
     k_raw = w.rows(TENSOR_K, b, pos)
-    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
-    k = round_store(rope(k_raw, pos[:, None], w.rope_base, style), w.dtype)
+    k, v = stored_rows(w, rope(k_raw, pos[:, None], w.rope_base, style), w.rows(TENSOR_V, b, pos))
     return pos, k, v
 
 

@@ -65,6 +65,7 @@ class RingWorkload:
     history: str            # "prefill:<T>" | "chunks:<T>:<N>" | "sinks+window"
     pos0_range: tuple = (0, 0)   # used by "sinks+window": decode start ~ U[lo, hi)
     chunk: int = 0          # prefill workloads: decode steps taken `chunk` tokens per call
+    cache: str = ""         # "i8": int8 cache rows (inputs stay `dtype`); "": same as dtype
 
     kind = "ring"
 
@@ -121,6 +122,8 @@ class RingWorkload:
                                   self.scale, self.dtype, out=out)
 
     def kv_bytes_per_token(self) -> int:
+        if self.cache == "i8":  # codes plus one float32 scale per row
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
         e = 4 if self.dtype == "f32" else 2
         return 2 * self.num_kv_heads * self.head_dim * e
 
@@ -139,6 +142,7 @@ class PagedWorkload:
     shared_prefix: int      # tokens shared by every sequence (multiple of block_size)
     scale: float
     decode_steps: int
+    cache: str = ""         # "i8": int8 pool rows (inputs stay `dtype`)
 
     kind = "paged"
 
@@ -217,6 +221,8 @@ class PagedWorkload:
                          self.scale, self.dtype)[0]
 
     def kv_bytes_per_token(self) -> int:
+        if getattr(self, "cache", "") == "i8":  # codes plus one float32 scale per row
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
         return 2 * self.num_kv_heads * self.head_dim * 2
 
 
@@ -254,6 +260,7 @@ class PoolWorkload:
     rope_base: float
     scale: float
     decode_steps: int
+    cache: str = ""         # "i8": int8 pool rows (inputs stay `dtype`)
 
     kind = "pool"
 
@@ -313,6 +320,8 @@ class PoolWorkload:
                          self.scale, self.dtype)[0]
 
     def kv_bytes_per_token(self) -> int:
+        if getattr(self, "cache", "") == "i8":  # codes plus one float32 scale per row
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
         return 2 * self.num_kv_heads * self.head_dim * 2
 
 
@@ -398,6 +407,8 @@ class PagerWorkload:
                          self.scale, self.dtype)[0]
 
     def kv_bytes_per_token(self) -> int:
+        if getattr(self, "cache", "") == "i8":  # codes plus one float32 scale per row
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
         return 2 * self.num_kv_heads * self.head_dim * 2
 
 
@@ -428,6 +439,24 @@ WORKLOADS = {
         name="paged", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
         dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
         decode_steps=128),
+    # The same workloads over int8 caches ([kvc] §5.1): codes plus one
+    # float32 scale per row, quantised when written.
+    "mha-ring-i8": RingWorkload(
+        name="mha-ring-i8", seed=2, batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128,
+        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=256,
+        history="chunks:256:32", cache="i8"),
+    "gqa-ring-i8": RingWorkload(
+        name="gqa-ring-i8", seed=3, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=128,
+        history="sinks+window", pos0_range=(4096, 65536), cache="i8"),
+    "paged-i8": PagedWorkload(
+        name="paged-i8", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
+        decode_steps=128, cache="i8"),
+    "long-pool-b16-i8": PoolWorkload(
+        name="long-pool-b16-i8", seed=5, batch=16, num_q_heads=24, num_kv_heads=4, head_dim=128,
+        dtype="bf16", block_size=64, logical_blocks=4096, pool_slots=1152,
+        rope_base=10000.0, scale=0.5, decode_steps=128, cache="i8"),
     "paged-append": PagedAppendWorkload(
         name="paged-append", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
         dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
