@@ -128,9 +128,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(AppendParam
       dst = static_cast<T*>(p.k_cache) +
             ((static_cast<size_t>(b) * p.num_kv_heads + h) * slots + slot) * d;
     } else {
-      dst = static_cast<T*>(p.q_inout) +
-            ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
-      src = dst;
+      const size_t qrow = ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
+      src = static_cast<const T*>(p.q_inout) + qrow;
+      dst = static_cast<T*>(p.q_out != nullptr ? p.q_out : p.q_inout) + qrow;
     }
     double o0, o1;
     rope_rotate_pair(E::load(src, i0), E::load(src, i1), cs, sn, &o0, &o1);
@@ -282,15 +282,17 @@ __device__ __forceinline__ void pair_elems(int i, int half, int rope_half, int* 
   *e1 = rope_half ? i + half : 2 * i + 1;
 }
 
-// Ring append into an int8 cache: one workgroup per token, one wave per row
-// (its Hkv K rows, Hkv V rows, and Hq query rows when q_inout is given).  K
+// Ring append into an int8 cache: one wave per row of a token (its Hkv K
+// rows, Hkv V rows, and Hq query rows when q_inout is given), four rows per
+// workgroup, so a decode step's few tokens still spread over many CUs.  K
 // is rotated at the token's position in float64 and quantised from there; V
 // is quantised from its bf16 values; the query stays bf16, rotated and
 // rounded exactly as the bf16 append does it.  Slot rule, skipping of a
 // token whose slot a later token of the call takes, and slot_pos as in
 // append_rope_kernel.
-__global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams p) {
-  const int token = blockIdx.x;
+__global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams p,
+                                                                   int wgs_per_token) {
+  const int token = blockIdx.x / wgs_per_token;
   const int b = token / p.n_tokens;
   const int j = token - b * p.n_tokens;
   const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams 
   const int d = p.head_dim;
   const int half = d / 2;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = (blockIdx.x - token * wgs_per_token) * (kAppendThreads / 64) + (threadIdx.x >> 6);
   const int slots = p.sinks + p.window;
   const bool overwritten = pos >= p.sinks && j + p.window <= p.n_tokens - 1;
   const int slot = pos < p.sinks ? static_cast<int>(pos) : p.sinks + static_cast<int>(pos % p.window);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams 
   pair_elems(active ? lane : 0, half, p.rope_half, &e0, &e1);
   const int q_rows = p.q_inout != nullptr ? p.num_q_heads : 0;
   const int rows = 2 * p.num_kv_heads + q_rows;
-  for (int r = wave; r < rows; r += kAppendThreads / 64) {
+  for (int r = wave; r < rows; r += wgs_per_token * (kAppendThreads / 64)) {
     if (r < 2 * p.num_kv_heads) {
       if (overwritten) continue;
       const bool is_v = r >= p.num_kv_heads;
@@ -330,13 +332,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_i8_kernel(AppendParams 
         p.slot_pos[static_cast<size_t>(b) * slots + slot] = static_cast<int32_t>(pos);
     } else if (active) {
       const int h = r - 2 * p.num_kv_heads;
-      uint16_t* q = static_cast<uint16_t*>(p.q_inout) +
-                    ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
+      const size_t qrow = ((static_cast<size_t>(b) * p.n_tokens + j) * p.num_q_heads + h) * d;
+      const uint16_t* q = static_cast<const uint16_t*>(p.q_inout) + qrow;
+      uint16_t* qo = static_cast<uint16_t*>(p.q_out != nullptr ? p.q_out : p.q_inout) + qrow;
       double o0, o1;
       rope_rotate_pair(static_cast<double>(bf16_to_f32(q[e0])),
                        static_cast<double>(bf16_to_f32(q[e1])), cs, sn, &o0, &o1);
-      q[e0] = f64_to_bf16_rne(o0);
-      q[e1] = f64_to_bf16_rne(o1);
+      qo[e0] = f64_to_bf16_rne(o0);
+      qo[e1] = f64_to_bf16_rne(o1);
     }
   }
 }
@@ -414,10 +417,12 @@ hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream) {
-  const size_t grid = static_cast<size_t>(p.batch) * p.n_tokens;
+  const int rows = 2 * p.num_kv_heads + (p.q_inout != nullptr ? p.num_q_heads : 0);
+  const int wgs = (rows + kAppendThreads / 64 - 1) / (kAppendThreads / 64);
+  const size_t grid = static_cast<size_t>(p.batch) * p.n_tokens * wgs;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidValue;
-  append_i8_kernel<<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p);
+  append_i8_kernel<<<static_cast<unsigned>(grid), kAppendThreads, 0, stream>>>(p, wgs);
   return hipGetLastError();
 }
 

@@ -390,7 +390,8 @@ bool group_supported(int g) {
   return g == 1 || g == 2 || g == 3 || g == 4 || g == 6 || g == 8;
 }
 
-bool use_mfma_path(int bf16, int32_t head_dim) { return bf16 && head_dim == 128; }
+// bf16 or int8 rows with head_dim 128 take the matrix-core kernel.
+bool use_mfma_path(int bf16_or_i8, int32_t head_dim) { return bf16_or_i8 && head_dim == 128; }
 
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_tokens) {
   // One wave per split: aim for about eight waves per CU over the 256 CUs,
@@ -447,12 +448,12 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
 }
 
 hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream) {
-  if (use_mfma_path(p.bf16, p.head_dim)) return launch_decode_mfma_ring(p, stream);
+  if (use_mfma_path(p.bf16 || p.i8, p.head_dim)) return launch_decode_mfma_ring(p, stream);
   return launch_decode<RingAddr>(p, stream);
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  if (use_mfma_path(p.bf16, p.head_dim)) return launch_decode_mfma_pool(p, stream);
+  if (use_mfma_path(p.bf16 || p.i8, p.head_dim)) return launch_decode_mfma_pool(p, stream);
   return launch_decode<PoolAddr>(p, stream);
 }
 

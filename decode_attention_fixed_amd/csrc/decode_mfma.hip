@@ -46,6 +46,17 @@
 // The MFMA products of bf16 values are exact and accumulate in fp32; the
 // bf16 inputs are the stored values, so no precision is lost before the fp32
 // accumulation.
+//
+// int8 caches (codes + one float32 scale per row): a 128-byte row is half a
+// bf16 row, so one 16-byte load instruction covers eight whole rows (lane l:
+// chunk l % 8 of row 8i + l / 8); the 16 codes of a chunk become 16 bf16
+// values (exact: |code| <= 127) written as the two bf16 chunks of the same
+// LDS layout, so the operand reads and the MFMA are the bf16 path's.  The
+// score of a row is its MFMA dot product times the row's K scale; V is read
+// as 8-byte pieces (8 codes of row 4lq + r, dims 8lc .. +7), and the row's V
+// scale joins its softmax weight before the weight is broadcast.  Lane l
+// loads the two scales of row 4lq + l % 4 of a subtile; a lane's rows 4lq + r
+// take theirs from lane 16lq + r by a DPP row broadcast.
 #include <type_traits>
 
 #include "device_common.h"
@@ -66,9 +77,32 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const Vec16& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Four int8 codes (one 32-bit word) as exact floats.
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float* x) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = static_cast<float>(static_cast<int8_t>((w >> (8 * k)) & 0xffu));
+}
+
+// bf16 bits of two small integers held exactly in floats (truncation is exact).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
+}
+
+// 16 int8 codes -> two chunks of 8 bf16 values (elements 0-7, 8-15).
+__device__ __forceinline__ void i8x16_to_bf16(const Vec16& v, Vec16& lo, Vec16& hi) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) i8x4_to_f32(v.w[i], x + 4 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo.w[i] = pack_bf16_exact(x[2 * i], x[2 * i + 1]);
+    hi.w[i] = pack_bf16_exact(x[8 + 2 * i], x[8 + 2 * i + 1]);
+  }
+}
+
 // K/V rows are read once per step and never again before the whole cache has
 // streamed past: non-temporal loads keep them from displacing reused lines.
-__device__ __forceinline__ Vec16 load16_stream(const uint16_t* p) {
+__device__ __forceinline__ Vec16 load16_stream(const void* p) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   Vec16 r;
@@ -77,6 +111,12 @@ __device__ __forceinline__ Vec16 load16_stream(const uint16_t* p) {
   r.w[2] = v[2];
   r.w[3] = v[3];
   return r;
+}
+
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
 }
 
 // Value of lane (16 * (l / 16) + SRC) for every lane l: broadcast inside each
@@ -332,10 +372,11 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
 // sequence, the normalised partial output and base-2 lse at partial slot
 // `slot` (layout [slot][head][d]).  Every thread of the workgroup must call it
 // with the same arguments; it returns with LDS free for reuse.
-template <int G, class Rows, int NW, bool FUSED = false, int NS_>
+template <int G, class Rows, int NW, bool FUSED = false, bool I8 = false, int NS_>
 __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b, int kvh, int t0,
                              int t1, bool direct, size_t slot, NewRow<G>* nr = nullptr,
                              NewToken nt = NewToken{}) {
+  static_assert(!(FUSED && I8), "the fused step appends bf16 rows");
   using Sm = Smem<G, NW, NS_>;
   constexpr int NS = Sm::NS;
   constexpr int TILE = Sm::TILE;
@@ -346,8 +387,11 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
   const int lc = lane & 15;
   const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
   Rows rows(p, b, kvh);
-  const uint16_t* kb = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vb = static_cast<const uint16_t*>(p.v);
+  // element offsets index bf16 rows, or bytes of int8 rows
+  using KT = std::conditional_t<I8, int8_t, uint16_t>;
+  const KT* kb = static_cast<const KT*>(p.k);
+  const KT* vb = static_cast<const KT*>(p.v);
+  constexpr int KL = I8 ? 2 : 4;  // K load instructions per 16-row subtile
 
   // B operand: the g query heads of this kv head, zero-padded to 16 (the
   // fused step rotates them into LDS first).
@@ -382,149 +426,213 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
   // operand-wise reads below touch 16 distinct bank groups per 16 lanes.
   uint4* s_k = reinterpret_cast<uint4*>(sm.raw) + wave * KBUF;
 
+  // One wave tile: NS subtiles of 16 rows.
+  struct Tile {
+    Vec16 kr[NS][KL];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
+                       // (int8: row 8i + l / 8, 16-byte chunk l % 8)
+    std::conditional_t<I8, uint2, Vec16> vr[NS][4];  // V: row 4lq + r of subtile u, dims 8lc..
+    float ksl[NS], vsl[NS];  // int8: K and V scales of row lc of subtile u
+    uint32_t vm[NS];         // bit i: row ts + 16u + i is resident
+    size_t base[NS];
+    bool live[NS];
+  };
+  // Issues the tile's loads (rows ts .. of the staged chunk [c0, c1)).
+  auto load_tile = [&](Tile& T, int ts, int c0, int c1) {
+    // Every load instruction reads four whole 256-byte rows; K first, so
+    // the score phase waits on K while the V loads are still in flight.
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int tu = ts + 16 * u;
+      T.vm[u] = 0;
+      T.base[u] = 0;
+      T.live[u] = tu < c1 && rows.subtile(p, sm.blk, c0, tu, T.base[u]);
+      if (T.live[u]) {
+        const int tk = tu + lc;
+        const bool okk = tk < c1 && rows.row_ok(tk);
+        T.vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
+        const KT* ks = kb + T.base[u];  // uniform: scalar base register
+        if constexpr (I8) {
+#pragma unroll
+          for (int i = 0; i < KL; ++i) {
+            const int rho = 8 * i + (lane >> 3);
+            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
+            T.kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 16 * (lane & 7)));
+          }
+          // lane l loads the scales of row 4lq + (l % 4); row 4lq + r is then
+          // lane 16lq + r's, one DPP broadcast away
+          const int sr = 4 * lq + (lc & 3);
+          const int rr = Rows::kWholeSubtiles || tu + sr < c1 ? sr : 0;
+          const size_t srow = (T.base[u] >> 7) + rr;  // kD = 128 codes per row
+          T.ksl[u] = p.k_scale[srow];
+          T.vsl[u] = p.v_scale[srow];
+        } else {
+#pragma unroll
+          for (int i = 0; i < KL; ++i) {
+            const int rho = 4 * i + lq;
+            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
+            T.kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 8 * lc));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) T.kr[u][i] = Vec16{};
+        T.ksl[u] = 0.f;
+        T.vsl[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int tu = ts + 16 * u;
+      if (T.live[u]) {
+        const KT* vs = vb + T.base[u];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * lq + r;
+          const int row = Rows::kWholeSubtiles || tu + i < c1 ? i : 0;
+          if constexpr (I8)
+            T.vr[u][r] = load8_stream(vs + static_cast<uint32_t>(row * kD + 8 * lc));
+          else
+            T.vr[u][r] = load16_stream(vs + static_cast<uint32_t>(row * kD + 8 * lc));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T.vr[u][r] = {};
+      }
+    }
+
+};
+  // Scores, online softmax and P*V of a loaded tile.
+  auto compute_tile = [&](Tile& T, int ts, int c1) {
+    // K chunks into the MFMA A-operand layout through LDS (DS instructions
+    // of one wave execute in order; the wave barriers only stop the compiler
+    // from moving LDS accesses across each other).
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        if constexpr (I8) {  // 16 codes -> bf16 chunks 2c and 2c + 1 of the row
+          const int rho = 8 * i + (lane >> 3);
+          const int c8 = lane & 7;
+          Vec16 lo, hi;
+          i8x16_to_bf16(T.kr[u][i], lo, hi);
+          s_k[(u * 16 + rho) * 16 + ((2 * c8) ^ rho)] = make_uint4(lo.w[0], lo.w[1], lo.w[2], lo.w[3]);
+          s_k[(u * 16 + rho) * 16 + ((2 * c8 + 1) ^ rho)] =
+              make_uint4(hi.w[0], hi.w[1], hi.w[2], hi.w[3]);
+        } else {
+          const int rho = 4 * i + lq;
+          s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
+              make_uint4(T.kr[u][i].w[0], T.kr[u][i].w[1], T.kr[u][i].w[2], T.kr[u][i].w[3]);
+        }
+      }
+    __builtin_amdgcn_wave_barrier();
+    Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
+        ka[u][s].w[0] = t.x;
+        ka[u][s].w[1] = t.y;
+        ka[u][s].w[2] = t.z;
+        ka[u][s].w[3] = t.w;
+      }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t all = 0xffffu;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) all &= T.vm[u];
+    const bool all_ok = all == 0xffffu;
+
+    // scores (log2 units) of rows 16u + 4lq + r for head lc
+    float x[NS][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
+        float dr = d[r];
+        if constexpr (I8) dr *= row_bcast_dyn(T.ksl[u], r);  // the row's K scale
+        x[u][r] = ok ? dr * c : kNegInf;
+        tmax = fmaxf(tmax, x[u][r]);
+      }
+    }
+    tmax = xor_max(tmax, 16);
+    tmax = xor_max(tmax, 32);
+    const float mn = fmaxf(m, tmax);
+    // mn == -inf: nothing resident so far for this head; keep everything at 0
+    const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
+    m = mn;
+    float pr[NS][4];
+    float tsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[u][r] = x[u][r] == kNegInf ? 0.f : exp2f(x[u][r] - mn);
+        tsum += pr[u][r];
+      }
+    lsum = lsum * alpha + tsum;
+    if constexpr (I8) {  // the row's V scale joins its weight (selected: an
+                         // absent row's scale may hold anything)
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
+          const float vsc = row_bcast_dyn(T.vsl[u], r);
+          pr[u][r] = ok ? pr[u][r] * vsc : 0.f;
+        }
+    }
+
+    // P * V
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = row_bcast_dyn(alpha, h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[8];
+        if constexpr (I8) {
+          i8x4_to_f32(T.vr[u][r].x, v);
+          i8x4_to_f32(T.vr[u][r].y, v + 4);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(T.vr[u][r].w[i]);
+            v[2 * i + 1] = bf16_hi(T.vr[u][r].w[i]);
+          }
+        }
+        if (!I8 && !all_ok) {
+          const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ph = row_bcast_dyn(pr[u][r], h);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+        }
+      }
+    };
+
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int c1 = min(c0 + kChunk, t1);
     rows.stage(p, c0, c1, sm.blk);
     __syncthreads();
     for (int ts = c0 + wave * TILE; ts < c1; ts += NW * TILE) {
-      Vec16 kr[NS][4];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
-      Vec16 vr[NS][4];  // V: row 4lq + r of subtile u, chunk lc
-      uint32_t vm[NS];  // bit i: row ts + 16u + i is resident
-      size_t base[NS];
-      bool live[NS];
-      // Every load instruction reads four whole 256-byte rows; K first, so
-      // the score phase waits on K while the V loads are still in flight.
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int tu = ts + 16 * u;
-        vm[u] = 0;
-        base[u] = 0;
-        live[u] = tu < c1 && rows.subtile(p, sm.blk, c0, tu, base[u]);
-        if (live[u]) {
-          const int tk = tu + lc;
-          const bool okk = tk < c1 && rows.row_ok(tk);
-          vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
-          const uint16_t* ks = kb + base[u];  // uniform: scalar base register
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rho = 4 * i + lq;
-            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
-            kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 8 * lc));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) kr[u][i] = Vec16{};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int tu = ts + 16 * u;
-        if (live[u]) {
-          const uint16_t* vs = vb + base[u];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * lq + r;
-            const int row = Rows::kWholeSubtiles || tu + i < c1 ? i : 0;
-            vr[u][r] = load16_stream(vs + static_cast<uint32_t>(row * kD + 8 * lc));
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vr[u][r] = Vec16{};
-        }
-      }
-
-      // K chunks into the MFMA A-operand layout through LDS (DS instructions
-      // of one wave execute in order; the wave barriers only stop the compiler
-      // from moving LDS accesses across each other).
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < NS; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rho = 4 * i + lq;
-          s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
-              make_uint4(kr[u][i].w[0], kr[u][i].w[1], kr[u][i].w[2], kr[u][i].w[3]);
-        }
-      __builtin_amdgcn_wave_barrier();
-      Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
-#pragma unroll
-      for (int u = 0; u < NS; ++u)
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-          const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
-          ka[u][s].w[0] = t.x;
-          ka[u][s].w[1] = t.y;
-          ka[u][s].w[2] = t.z;
-          ka[u][s].w[3] = t.w;
-        }
-      __builtin_amdgcn_wave_barrier();
-      uint32_t all = 0xffffu;
-#pragma unroll
-      for (int u = 0; u < NS; ++u) all &= vm[u];
-      const bool all_ok = all == 0xffffu;
-
-      // scores (log2 units) of rows 16u + 4lq + r for head lc
-      float x[NS][4];
-      float tmax = kNegInf;
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
-          x[u][r] = ok ? d[r] * c : kNegInf;
-          tmax = fmaxf(tmax, x[u][r]);
-        }
-      }
-      tmax = xor_max(tmax, 16);
-      tmax = xor_max(tmax, 32);
-      const float mn = fmaxf(m, tmax);
-      // mn == -inf: nothing resident so far for this head; keep everything at 0
-      const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
-      m = mn;
-      float pr[NS][4];
-      float tsum = 0.f;
-#pragma unroll
-      for (int u = 0; u < NS; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[u][r] = x[u][r] == kNegInf ? 0.f : exp2f(x[u][r] - mn);
-          tsum += pr[u][r];
-        }
-      lsum = lsum * alpha + tsum;
-
-      // P * V
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float a = row_bcast_dyn(alpha, h);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-      }
-#pragma unroll
-      for (int u = 0; u < NS; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_lo(vr[u][r].w[i]);
-            v[2 * i + 1] = bf16_hi(vr[u][r].w[i]);
-          }
-          if (!all_ok) {
-            const bool ok = (vm[u] >> (4 * lq + r)) & 1u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float ph = row_bcast_dyn(pr[u][r], h);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
-          }
-        }
+      Tile A;
+      load_tile(A, ts, c0, c1);
+      compute_tile(A, ts, c1);
     }
     __syncthreads();  // the next chunk restages the block ids
   }
@@ -600,7 +708,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 
 // Ring caches: grid of (b, kv head, split), one piece per workgroup; partial
 // slot (b * Hkv + kv head) * num_splits + split.
-template <int G, int NW, bool FUSED>
+template <int G, int NW, bool FUSED, bool I8>
 __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
   __shared__ Smem<G, NW, subtiles<G, false>()> sm;
   const int ns = p.num_splits;
@@ -624,7 +732,7 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
     }
     attend_piece<G, RingRows, NW, true>(p, sm, b, kvh, t0, t1, ns == 1, slot, &nr, nt);
   } else {
-    attend_piece<G, RingRows, NW>(p, sm, b, kvh, t0, t1, ns == 1, slot);
+    attend_piece<G, RingRows, NW, false, I8>(p, sm, b, kvh, t0, t1, ns == 1, slot);
   }
 }
 
@@ -810,7 +918,7 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 
 // 8 / NW workgroups per CU (two 4-wave or one 8-wave): two waves per SIMD, at
 // most 256 registers per lane.
-template <int G, int NW>
+template <int G, int NW, bool I8>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
   constexpr int NT = NW * 64;
   __shared__ Smem<G, NW, subtiles<G, true>()> sm;
@@ -854,7 +962,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
   __syncthreads();
   Piece pc;
   while (next_piece<NT>(p, sc, pc))
-    attend_piece<G, PoolRows, NW>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct, pc.slot);
+    attend_piece<G, PoolRows, NW, false, I8>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct, pc.slot);
 }
 
 // Combines the partials of one (sequence, query head) spread over several
@@ -1018,32 +1126,29 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   }
 }
 
-#define SWA_KERNEL_TABLE(NAME)                                                            \
-  template <int NW>                                                                       \
-  hipError_t NAME##_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {    \
-    switch (p.num_q_heads / p.num_kv_heads) {                                             \
-      case 1: NAME<1, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      case 2: NAME<2, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      case 3: NAME<3, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      case 4: NAME<4, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      case 6: NAME<6, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      case 8: NAME<8, NW><<<grid, NW * 64, 0, stream>>>(p); break;                        \
-      default: return hipErrorInvalidValue;                                               \
-    }                                                                                     \
-    return hipGetLastError();                                                             \
+template <int NW, bool I8>
+hipError_t decode_pool_kernel_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {
+  switch (p.num_q_heads / p.num_kv_heads) {
+    case 1: decode_pool_kernel<1, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 2: decode_pool_kernel<2, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 3: decode_pool_kernel<3, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 4: decode_pool_kernel<4, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 6: decode_pool_kernel<6, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 8: decode_pool_kernel<8, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
   }
-SWA_KERNEL_TABLE(decode_pool_kernel)
-#undef SWA_KERNEL_TABLE
+  return hipGetLastError();
+}
 
-template <int NW, bool FUSED>
+template <int NW, bool FUSED, bool I8>
 hipError_t decode_ring_kernel_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {
   switch (p.num_q_heads / p.num_kv_heads) {
-    case 1: decode_ring_kernel<1, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 2: decode_ring_kernel<2, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 3: decode_ring_kernel<3, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 4: decode_ring_kernel<4, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 6: decode_ring_kernel<6, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 8: decode_ring_kernel<8, NW, FUSED><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 1: decode_ring_kernel<1, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 2: decode_ring_kernel<2, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 3: decode_ring_kernel<3, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 4: decode_ring_kernel<4, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 6: decode_ring_kernel<6, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 8: decode_ring_kernel<8, NW, FUSED, I8><<<grid, NW * 64, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1055,9 +1160,11 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
   const unsigned grid =
       static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
   // p.new_pos set: the fused step (append of one token per sequence + decode)
+  if (p.i8 && p.new_pos != nullptr) return hipErrorInvalidValue;  // fused step: bf16 only
   hipError_t err = p.new_pos != nullptr
-                       ? decode_ring_kernel_launch<kRingWaves, true>(p, grid, stream)
-                       : decode_ring_kernel_launch<kRingWaves, false>(p, grid, stream);
+                       ? decode_ring_kernel_launch<kRingWaves, true, false>(p, grid, stream)
+                       : (p.i8 ? decode_ring_kernel_launch<kRingWaves, false, true>(p, grid, stream)
+                               : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream));
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);
@@ -1068,9 +1175,13 @@ hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream) {
   // p.num_splits carries the size of the balanced grid: kPoolGrid 4-wave
   // workgroups, or half as many 8-wave ones for small pools
   const unsigned grid = static_cast<unsigned>(p.num_splits);
-  hipError_t err = grid == static_cast<unsigned>(kPoolGrid)
-                       ? decode_pool_kernel_launch<4>(p, grid, stream)
-                       : decode_pool_kernel_launch<8>(p, grid, stream);
+  hipError_t err;
+  if (p.i8)
+    err = grid == static_cast<unsigned>(kPoolGrid) ? decode_pool_kernel_launch<4, true>(p, grid, stream)
+                                                   : decode_pool_kernel_launch<8, true>(p, grid, stream);
+  else
+    err = grid == static_cast<unsigned>(kPoolGrid) ? decode_pool_kernel_launch<4, false>(p, grid, stream)
+                                                   : decode_pool_kernel_launch<8, false>(p, grid, stream);
   if (err != hipSuccess) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   merge_kernel<8><<<heads, 256, 0, stream>>>(p, 1);

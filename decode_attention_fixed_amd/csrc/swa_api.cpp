@@ -273,11 +273,11 @@ static swa_status ring_decode_params(const swa_cache* cache, const void* q, int3
   swa_status st = check_group(num_q_heads, cfg.num_kv_heads);
   if (st != SWA_OK) return st;
   const int32_t slots = cfg.num_sinks + cfg.window;
-  if (swa::use_mfma_path(cfg.dtype == SWA_BF16, cfg.head_dim) && slots > swa::kMaxMfmaTokens)
+  if (swa::use_mfma_path(cfg.dtype != SWA_F32, cfg.head_dim) && slots > swa::kMaxMfmaTokens)
     return fail(SWA_ERR_UNSUPPORTED, "num_sinks + window above %lld rows per sequence",
                 static_cast<long long>(swa::kMaxMfmaTokens));
   const swa::SplitPlan plan =
-      plan_for(cfg.dtype == SWA_BF16, cfg.head_dim, cfg.batch, cfg.num_kv_heads, slots, false);
+      plan_for(cfg.dtype != SWA_F32, cfg.head_dim, cfg.batch, cfg.num_kv_heads, slots, false);
   lay = swa::workspace_layout(cfg.batch, num_q_heads, cfg.num_kv_heads, cfg.head_dim, slots);
   st = check_decode_common(q, out, out_dtype, lse, workspace, workspace_bytes, lay.total);
   if (st != SWA_OK) return st;
@@ -338,24 +338,22 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
     return fail(SWA_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swa::use_mfma_path(p.bf16, p.head_dim)) {  // one launch (plus the split merge)
+  if (swa::use_mfma_path(p.bf16, p.head_dim)) {  // bf16: one launch (plus the split merge)
     p.k_new = k_new;
     p.v_new = v_new;
     p.new_pos = pos;
     return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
   }
-  // Other shapes: the append (rotating a copy of q kept in the workspace),
-  // then the decode over that copy.
+  // Other shapes: the append (writing the rotated query into the workspace,
+  // q itself is only read), then the decode over that rotated copy.
   void* q_copy = static_cast<char*>(workspace) + lay.q_offset;
-  const size_t q_bytes = static_cast<size_t>(p.batch) * num_q_heads * p.head_dim *
-                         (p.bf16 || p.i8 ? sizeof(uint16_t) : sizeof(float));
-  hipError_t err = hipMemcpyAsync(q_copy, q, q_bytes, hipMemcpyDeviceToDevice, s);
-  if (err != hipSuccess) return from_hip(err, "decode_step_ring");
+  hipError_t err = hipSuccess;
   swa::AppendParams a{};
   a.k_new = k_new;
   a.v_new = v_new;
   a.pos = pos;
-  a.q_inout = q_copy;
+  a.q_inout = const_cast<void*>(q);  // read only: q_out is set
+  a.q_out = q_copy;
   a.k_cache = cache->k;
   a.v_cache = cache->v;
   a.slot_pos = cache->slot_pos;
@@ -535,11 +533,11 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
       !aligned(seq_lens, 4))
     return fail(SWA_ERR_INVALID_ARG, "pool buffers misaligned");
   const int32_t max_tokens = desc->max_blocks_per_seq * desc->block_size;
-  if (swa::use_mfma_path(desc->dtype == SWA_BF16, desc->head_dim) &&
+  if (swa::use_mfma_path(desc->dtype != SWA_F32, desc->head_dim) &&
       max_tokens > swa::kMaxMfmaTokens)
     return fail(SWA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size above %lld rows per sequence",
                 static_cast<long long>(swa::kMaxMfmaTokens));
-  const swa::SplitPlan plan = plan_for(desc->dtype == SWA_BF16, desc->head_dim, desc->batch,
+  const swa::SplitPlan plan = plan_for(desc->dtype != SWA_F32, desc->head_dim, desc->batch,
                                        desc->num_kv_heads, max_tokens, true);
   const swa::WorkspaceLayout lay = swa::workspace_layout(
       desc->batch, desc->num_q_heads, desc->num_kv_heads, desc->head_dim, max_tokens);

@@ -46,6 +46,7 @@ struct AppendParams {
   const void* v_new;      // [B, T, Hkv, d]
   const int32_t* pos;     // [B]
   void* q_inout;          // [B, T, Hq, d] or null
+  void* q_out;            // [B, T, Hq, d] or null: rotated queries go here, q_inout is only read
   const void* k_rotated;  // [B, T, Hkv, d] or null: K rows already rotated (and rounded) exactly
                           // as this kernel would, copied instead of k_new
   void* k_cache;          // [B, Hkv, S+W, d]
