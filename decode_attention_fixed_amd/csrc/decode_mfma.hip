@@ -161,6 +161,7 @@ constexpr int kChunk = 8192;  // rows whose block ids are staged in LDS at a tim
 constexpr int kMaxSplitBlocks = kChunk / 16 + 1;
 constexpr int kMaxSplits = 512;  // ring splits per sequence (the plan never exceeds it)
 
+
 // Ring: rows of head (b, h) are contiguous, slot t at row t; a row is
 // resident iff its slot holds a position.
 struct RingRows {
@@ -234,8 +235,14 @@ struct PoolRows {
 // SIMD cap a wave at 256 VGPRs).  Pools stream best with one subtile per tile
 // for g >= 3 (measured: 1-1.5% over two on the paged and pool workloads);
 // ring caches with two for g = 3..6.
-template <int G, bool POOL>
-constexpr int subtiles() { return G <= 2 ? 4 : (G < 8 && !POOL ? 2 : 1); }
+// int8 rows carry half the bytes of a bf16 subtile and half its registers:
+// twice the subtiles on rings with g >= 3 and four times on pools (measured:
+// paged-i8 319 -> 285 us, long-pool-b16-i8 337 -> 282 us, gqa-ring-i8 152 ->
+// 148 us); g <= 2 keeps four, all the LDS staging area allows.
+template <int G, bool POOL, bool I8 = false>
+constexpr int subtiles() {
+  return G <= 2 ? 4 : ((G < 8 && !POOL ? 2 : 1) * (I8 ? (POOL ? 4 : 2) : 1));
+}
 
 template <int G, int NW, int NS_>
 struct Smem {
@@ -710,7 +717,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 // slot (b * Hkv + kv head) * num_splits + split.
 template <int G, int NW, bool FUSED, bool I8>
 __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
-  __shared__ Smem<G, NW, subtiles<G, false>()> sm;
+  __shared__ Smem<G, NW, subtiles<G, false, I8>()> sm;
   const int ns = p.num_splits;
   const int split = blockIdx.x % ns;
   const int unit = blockIdx.x / ns;
@@ -921,7 +928,7 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 template <int G, int NW, bool I8>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
   constexpr int NT = NW * 64;
-  __shared__ Smem<G, NW, subtiles<G, true>()> sm;
+  __shared__ Smem<G, NW, subtiles<G, true, I8>()> sm;
   __shared__ SeqChunk<NT> sc;
   const int64_t hkv = p.num_kv_heads;
   const int64_t nwg = gridDim.x;
