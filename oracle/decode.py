@@ -10,6 +10,8 @@ Ring workloads (sink + sliding window, [sink] cache formula, [ring] §2.2):
   [ring] demo does, §4.3).  Cached K rows carry RoPE at their absolute
   position, rounded to the storage dtype ([pool] "bake RoPE into K"); V rows
   are stored as given; the query is rotated at t and stored the same way.
+Cache position shifting ([sink]): the same resident set, with each key and
+  the query rotated at their index in the cache instead of their position.
 Chunked prefill on a ring ([pool] "paging", chunks of 128-256 tokens): a
   chunk of T new tokens at positions p0 .. p0 + T - 1; query row j is exactly
   decode step j of the same workload (position p0 + j attends R(p0 + j) after
@@ -76,6 +78,31 @@ def ring_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
     pos = resident_positions(t, w.sinks, w.window)
     k, v = ring_rows(w, b, pos, style)
     return attend_heads(ring_query(w, b, t, style), k, v, scale)
+
+
+def ring_cache_positions(t: int, sinks: int, window: int) -> dict:
+    """Position in the cache of every position held after positions 0..t were
+    appended ([sink] "cache position shifting"): the cache is the sinks
+    followed by the recent window, in order, and a key's position is its
+    index in that sequence; the query, the newest key, has the last index."""
+    return {p: c for c, p in enumerate(resident_positions(t, sinks, window))}
+
+
+def ring_shifted_expected(w, b: int, step: int, scale=None, style: str = "interleaved"):
+    """(out [Hq, d], lse [Hq]) of decode step `step` with positions taken in
+    the cache ([sink]: the window's positions are moved left inside the
+    attention so that their distance to the sinks stays within the window):
+    every key is rotated at its cache position and the query at its own, at
+    read time, in float64 from the rows as given (keys are not stored
+    rotated in this variant)."""
+    t = int(w.decode_positions(step)[b])
+    cpos = ring_cache_positions(t, w.sinks, w.window)
+    pos = np.asarray(sorted(cpos), dtype=np.int64)
+    c = np.asarray([cpos[p] for p in pos], dtype=np.int64)
+    k = rope(w.rows(TENSOR_K, b, pos), c[:, None], w.rope_base, style)
+    v = w.rows(TENSOR_V, b, pos).astype(np.float64)
+    q = rope(w.rows(TENSOR_Q, b, [t])[0], cpos[t], w.rope_base, style)
+    return attend_heads(q, k, v, scale)
 
 
 def ring_prefill_expected(w, b: int, first_step: int, n_tokens: int, scale=None,
