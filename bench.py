@@ -83,6 +83,8 @@ def describe(w) -> dict:
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, W={w.window} + {w.sinks} sinks, "
                 f"history {w.history}, {what}")
+        if w.positions == "cache":
+            text += ", positions inside the cache (sink position shifting)"
     elif w.kind in ("paged", "paged-append"):
         text = (f"{w.name}: B={w.batch}, Hq={w.num_q_heads}, Hkv={w.num_kv_heads}, "
                 f"d={w.head_dim}, {w.dtype}, {w.block_size}-token blocks, lengths "
@@ -232,12 +234,15 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
             def decode(i):
                 B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse)
         else:  # one call per step: the decode launch appends the token itself
+            step_fn = (B.decode_step_ring_shifted if w.positions == "cache"
+                       else B.decode_step_ring)
+
             def pre(i):
                 pass
 
             def decode(i):
-                B.decode_step_ring(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i],
-                                   q_all[i][:, 0], st.out, st.workspace, st.lse)
+                step_fn(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i], q_all[i][:, 0],
+                        st.out, st.workspace, st.lse)
     elif w.kind == "paged-append":
         import ctypes
 
@@ -455,7 +460,12 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         pager_sets = [pager_schedule(w, b)[0] for b in range(w.batch)]
 
     def oracle_step(pos, t, k_raw, v, q_raw):
-        if w.kind == "ring":
+        if w.kind == "ring" and getattr(w, "positions", "") == "cache":
+            c = np.arange(len(pos))  # cache indices: the resident positions in order
+            k = rope(k_raw, c[:, None], w.rope_base)
+            q = rope(q_raw, len(pos) - 1, w.rope_base)
+            v = np.asarray(v, dtype=np.float64)
+        elif w.kind == "ring":
             k, v = stored_rows(w, rope(k_raw, pos[:, None], w.rope_base), v)
             q = round_store(rope(q_raw, t, w.rope_base), w.dtype)
         elif w.kind in ("paged", "paged-append"):

@@ -74,6 +74,8 @@ _PROTOS = {
                                         ctypes.c_size_t, _vp]),
     "decode_step_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _i32,
                                         _vp, _vp, ctypes.c_size_t, _vp]),
+    "decode_step_ring_shifted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp,
+                                                _i32, _vp, _vp, ctypes.c_size_t, _vp]),
     "prefill_attn_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "prefill_attn_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
@@ -244,6 +246,22 @@ def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos:
                                 _ptr(out, "out"), _DTYPE_CODE[out.dtype],
                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_step_ring_shifted(handle: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                             pos: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                             workspace: torch.Tensor, lse: torch.Tensor | None = None,
+                             scale: float = 0.0, stream=None) -> None:
+    """decode_step_ring with positions taken inside the cache (sinks scored
+    against the query rotated at its cache position)."""
+    _check("decode_step_ring_shifted",
+           LIB.decode_step_ring_shifted(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+                                        _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1],
+                                        scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+                                        _ptr(lse, "lse", torch.float32),
+                                        _ptr(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
 
 
 def prefill_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

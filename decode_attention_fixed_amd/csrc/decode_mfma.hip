@@ -272,12 +272,21 @@ struct NewToken {
   int slot = -1;
   int32_t pos = 0;
   double theta = 0.0;  // theta_(tid % 64), read first of all loads (they complete in order)
+  // Cache position shifting ([sink]): positions inside the attention are
+  // indices in the cache (sinks, then the window in order).  A window key
+  // keeps its distance to the query, so only the sinks change: they are
+  // scored against the query rotated at its cache position cpos.  `shift`:
+  // this workgroup holds sink rows and cpos differs from pos.
+  bool shift = false;
+  int32_t cpos = 0;
 };
 
 template <int G>
 struct NewRow {
   double cs[kD / 2], sn[kD / 2];  // the token's rotation angles
+  double cs2[kD / 2], sn2[kD / 2];  // the angles at its cache position (shifting)
   uint16_t q[G][kD];              // rotated query heads (bf16, as an append stores them)
+  uint16_t qs[G][kD];             // the query heads rotated at the cache position (shifting)
   float k[kD], v[kD];             // its rotated K row and its V row
   float x[G];                     // its score per head (log2 units)
 };
@@ -319,6 +328,11 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
     rope_sincos(static_cast<double>(nt.pos), nt.theta, &sn, &cs);
     nr.cs[tid] = cs;
     nr.sn[tid] = sn;
+    if (nt.shift) {
+      rope_sincos(static_cast<double>(nt.cpos), nt.theta, &sn, &cs);
+      nr.cs2[tid] = cs;
+      nr.sn2[tid] = sn;
+    }
   }
   __syncthreads();
   const size_t crow = ((static_cast<size_t>(b) * p.num_kv_heads + kvh) * p.slots + nt.slot) * kD;
@@ -341,6 +355,13 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
     if (h < G) {
       nr.q[h][i0] = o0;
       nr.q[h][i1] = o1;
+      if (nt.shift) {  // the same rotation and rounding at the cache position
+        double x0, x1;
+        rope_rotate_pair(static_cast<double>(bf16_to_f32(r0[j])),
+                         static_cast<double>(bf16_to_f32(r1[j])), nr.cs2[i], nr.sn2[i], &x0, &x1);
+        nr.qs[h][i0] = f64_to_bf16_rne(x0);
+        nr.qs[h][i1] = f64_to_bf16_rne(x1);
+      }
     } else {  // the K row, rotated, into the cache and LDS
       uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k)) + crow;
       kc[i0] = o0;
@@ -559,6 +580,22 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s)
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
+      if constexpr (FUSED) {
+        const int tu = ts + 16 * u;
+        if (nt.shift && tu < p.sinks) {  // sink rows: the query at its cache position
+          f32x4_t ds = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < kKSteps; ++s) {
+            Vec16 v{};
+            if (lc < G) v = load16(&nr->qs[lc][32 * s + 8 * lq]);
+            ds = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), as_bf16x8(v), ds, 0,
+                                                         0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tu + 4 * lq + r < p.sinks) d[r] = ds[r];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
@@ -736,6 +773,8 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
     if (nt.app) {
       nt.slot = nt.pos < p.sinks ? nt.pos : p.sinks + nt.pos % p.window;
       nt.mine = nt.slot >= t0 && nt.slot < t1;
+      nt.cpos = min(nt.pos, p.sinks + p.window - 1);
+      nt.shift = p.shift_sinks && nt.cpos != nt.pos && t0 < p.sinks;
     }
     attend_piece<G, RingRows, NW, true>(p, sm, b, kvh, t0, t1, ns == 1, slot, &nr, nt);
   } else {

@@ -324,15 +324,18 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
                   "decode_attn_ring");
 }
 
-swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_new,
+static swa_status step_ring(swa_cache* cache, const void* k_new, const void* v_new,
                             const int32_t* pos, const void* q, int32_t num_q_heads, float scale,
                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool shift_sinks) {
   swa::DecodeParams p;
   swa::WorkspaceLayout lay;
   swa_status st = ring_decode_params(cache, q, num_q_heads, scale, out, out_dtype, lse, workspace,
                                      workspace_bytes, p, lay);
   if (st != SWA_OK) return st;
+  if (shift_sinks && !swa::use_mfma_path(p.bf16, p.head_dim))
+    return fail(SWA_ERR_UNSUPPORTED, "cache position shifting needs a bf16 cache with head_dim 128");
+  p.shift_sinks = shift_sinks ? 1 : 0;
   if (k_new == nullptr || v_new == nullptr || pos == nullptr)
     return fail(SWA_ERR_INVALID_ARG, "k_new, v_new and pos must not be NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
@@ -378,6 +381,22 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
   if (err != hipSuccess) return from_hip(err, "decode_step_ring");
   p.q = q_copy;
   return from_hip(swa::launch_decode_ring(p, s), "decode_step_ring");
+}
+
+swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_new,
+                            const int32_t* pos, const void* q, int32_t num_q_heads, float scale,
+                            void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return step_ring(cache, k_new, v_new, pos, q, num_q_heads, scale, out, out_dtype, lse, workspace,
+                   workspace_bytes, stream, false);
+}
+
+swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const void* v_new,
+                                    const int32_t* pos, const void* q, int32_t num_q_heads,
+                                    float scale, void* out, swa_dtype out_dtype, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return step_ring(cache, k_new, v_new, pos, q, num_q_heads, scale, out, out_dtype, lse, workspace,
+                   workspace_bytes, stream, true);
 }
 
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

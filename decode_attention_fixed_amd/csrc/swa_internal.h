@@ -119,6 +119,8 @@ struct DecodeParams {
   const int32_t* new_pos;     // [B]
   int32_t sinks, window;
   int32_t rope_half;
+  int32_t shift_sinks;        // fused step: positions inside the cache (sinks scored
+                              // against the query rotated at its cache position)
   RopeFreq freq;
 };
 

@@ -88,9 +88,10 @@ class RingState:
         """One decode step.  fused: decode_step_ring (one call; q left as
         given); else kv_append_rope (rotating q in place), then decode_attn_ring."""
         if fused:
-            B.decode_step_ring(self.cache.handle, inputs["k"][:, 0], inputs["v"][:, 0],
-                               inputs["pos"], inputs["q"][:, 0], self.out, self.workspace,
-                               self.lse, scale)
+            step = (B.decode_step_ring_shifted if self.w.positions == "cache"
+                    else B.decode_step_ring)
+            step(self.cache.handle, inputs["k"][:, 0], inputs["v"][:, 0], inputs["pos"],
+                 inputs["q"][:, 0], self.out, self.workspace, self.lse, scale)
             return
         B.kv_append_rope(self.cache.handle, inputs["k"], inputs["v"], inputs["pos"], inputs["q"])
         B.decode_attn_ring(self.cache.handle, inputs["q"][:, 0], self.out, self.workspace,

@@ -184,6 +184,23 @@ swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_n
                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* decode_step_ring with positions taken inside the cache ([sink] "cache
+ * position shifting": the window's positions are moved left inside the
+ * attention so that their distance to the sinks stays within the window).
+ * The cache (sinks, then the window in order) gives every key its index
+ * there as its position, and the query the last index,
+ * c = min(pos[b], S + W - 1).  RoPE scores depend on distances only; a window
+ * key keeps its distance pos[b] - p to the query, so only the sinks change:
+ * they are scored against the query rotated at c (rounded to bf16 as an
+ * append rounds it), the window against the query rotated at pos[b].  The
+ * cache itself is the same as decode_step_ring's (K baked at absolute
+ * positions) and ends in the same state.  Arguments as decode_step_ring;
+ * bf16 caches with head_dim 128 only (SWA_ERR_UNSUPPORTED otherwise). */
+swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const void* v_new,
+                                    const int32_t* pos, const void* q, int32_t num_q_heads,
+                                    float scale, void* out, swa_dtype out_dtype, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace (device bytes) of a prefill_attn_ring call with n_tokens tokens
  * per sequence.  Needs no initialisation. */
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -66,6 +66,7 @@ class RingWorkload:
     pos0_range: tuple = (0, 0)   # used by "sinks+window": decode start ~ U[lo, hi)
     chunk: int = 0          # prefill workloads: decode steps taken `chunk` tokens per call
     cache: str = ""         # "i8": int8 cache rows (inputs stay `dtype`); "": same as dtype
+    positions: str = ""     # "cache": positions inside the attention are cache indices
 
     kind = "ring"
 
@@ -439,6 +440,11 @@ WORKLOADS = {
         name="paged", seed=4, batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
         dtype="bf16", block_size=16, len_range=(1024, 32768), shared_prefix=2000, scale=0.5,
         decode_steps=128),
+    # mha-ring with StreamingLLM cache position shifting ([sink]).
+    "mha-ring-shift": RingWorkload(
+        name="mha-ring-shift", seed=2, batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128,
+        dtype="bf16", window=4096, sinks=4, rope_base=10000.0, scale=0.5, decode_steps=256,
+        history="chunks:256:32", positions="cache"),
     # The same workloads over int8 caches ([kvc] §5.1): codes plus one
     # float32 scale per row, quantised when written.
     "mha-ring-i8": RingWorkload(
