@@ -132,51 +132,61 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
-// Rotation of the chunk: one thread per (token, pair i, group of
-// `group_heads` heads) forms the angle once and rotates pair i of those heads
-// (query heads first, then key heads; rounding as the append kernel: f64
-// rotation, one rounding to bf16).  Small chunks split the heads into more
-// groups so that enough threads are in flight.
-__global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p, int group_heads) {
+// Rotation of the chunk: one workgroup per token.  The token's d/2 angles are
+// formed once (one wave, into LDS); then each thread rotates four pairs of a
+// head at a time, query heads first, then key heads.  Rounding as the append
+// kernel: f64 rotation, one rounding to bf16.
+__global__ __launch_bounds__(256) void rotate_chunk_kernel(RotateChunkParams p) {
   constexpr int kHalf = kD / 2;
-  const int64_t token = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // b * T + j
-  if (token >= static_cast<int64_t>(p.batch) * p.n_tokens) return;
-  const int i = threadIdx.x & 63;
+  constexpr int kQuads = kHalf / 4;  // four pairs per thread and head
+  __shared__ double s_cos[kHalf], s_sin[kHalf];
+  const int64_t token = blockIdx.x;  // b * T + j
   const int b = static_cast<int>(token / p.n_tokens);
   const int j = static_cast<int>(token - static_cast<int64_t>(b) * p.n_tokens);
   const int64_t pos = static_cast<int64_t>(p.pos[b]) + j;
   const bool rot = pos >= 0 && pos <= INT32_MAX;  // a token at such a position is never attended
-  double sn = 0.0, cs = 1.0;
-  if (rot) rope_sincos(static_cast<double>(pos), p.freq.theta[i], &sn, &cs);
-  auto rotate = [&](uint16_t& a, uint16_t& c) {
+  if (threadIdx.x < kHalf) {
+    double sn = 0.0, cs = 1.0;
+    if (rot) rope_sincos(static_cast<double>(pos), p.freq.theta[threadIdx.x], &sn, &cs);
+    s_cos[threadIdx.x] = cs;
+    s_sin[threadIdx.x] = sn;
+  }
+  __syncthreads();
+  auto rotate = [&](uint16_t& a, uint16_t& c, int i) {
     if (!rot) return;
     double x0, x1;
-    rope_rotate_pair(static_cast<double>(bf16_to_f32(a)), static_cast<double>(bf16_to_f32(c)), cs,
-                     sn, &x0, &x1);
+    rope_rotate_pair(static_cast<double>(bf16_to_f32(a)), static_cast<double>(bf16_to_f32(c)),
+                     s_cos[i], s_sin[i], &x0, &x1);
     a = f64_to_bf16_rne(x0);
     c = f64_to_bf16_rne(x1);
   };
-  const int h0 = blockIdx.y * group_heads;  // first head of this thread's group
-  auto rows = [&](const void* src, void* dst, int heads, int first, int end) {
-    const size_t row0 = static_cast<size_t>(token) * heads;
-    for (int h = max(first, 0); h < min(end, heads); ++h) {
-      const uint16_t* sr = static_cast<const uint16_t*>(src) + (row0 + h) * kD;
-      uint16_t* dr = static_cast<uint16_t*>(dst) + (row0 + h) * kD;
-      if (p.rope_half) {  // pairs (i, i + d/2)
-        uint16_t a = sr[i], c = sr[i + kHalf];
-        rotate(a, c);
-        dr[i] = a;
-        dr[i + kHalf] = c;
-      } else {            // pairs (2i, 2i + 1), one 32-bit word
-        const uint32_t w = reinterpret_cast<const uint32_t*>(sr)[i];
-        uint16_t a = static_cast<uint16_t>(w), c = static_cast<uint16_t>(w >> 16);
-        rotate(a, c);
-        reinterpret_cast<uint32_t*>(dr)[i] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
-      }
+  const int heads = p.num_q_heads + p.num_kv_heads;
+  for (int w = threadIdx.x; w < heads * kQuads; w += blockDim.x) {
+    const int h = w / kQuads;
+    const int i0 = 4 * (w - h * kQuads);  // pairs i0 .. i0 + 3
+    const bool is_q = h < p.num_q_heads;
+    const int hh = is_q ? h : h - p.num_q_heads;
+    const int nh = is_q ? p.num_q_heads : p.num_kv_heads;
+    const size_t row = (static_cast<size_t>(token) * nh + hh) * kD;
+    const uint16_t* sr = static_cast<const uint16_t*>(is_q ? p.q : p.k) + row;
+    uint16_t* dr = static_cast<uint16_t*>(is_q ? p.q_rot : p.k_rot) + row;
+    if (p.rope_half) {  // pairs (i, i + d/2): four elements from each half
+      uint2 lo = *reinterpret_cast<const uint2*>(sr + i0);
+      uint2 hi = *reinterpret_cast<const uint2*>(sr + i0 + kHalf);
+      uint16_t* l = reinterpret_cast<uint16_t*>(&lo);
+      uint16_t* u = reinterpret_cast<uint16_t*>(&hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rotate(l[e], u[e], i0 + e);
+      *reinterpret_cast<uint2*>(dr + i0) = lo;
+      *reinterpret_cast<uint2*>(dr + i0 + kHalf) = hi;
+    } else {            // pairs (2i, 2i + 1): eight neighbouring elements
+      uint4 v = *reinterpret_cast<const uint4*>(sr + 2 * i0);
+      uint16_t* e16 = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rotate(e16[2 * e], e16[2 * e + 1], i0 + e);
+      *reinterpret_cast<uint4*>(dr + 2 * i0) = v;
     }
-  };
-  rows(p.q, p.q_rot, p.num_q_heads, h0, h0 + group_heads);
-  rows(p.k, p.k_rot, p.num_kv_heads, h0 - p.num_q_heads, h0 + group_heads - p.num_q_heads);
+  }
 }
 
 template <int G>
@@ -564,16 +574,9 @@ PrefillLayout prefill_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_
 
 hipError_t launch_rotate_chunk(const RotateChunkParams& p, hipStream_t stream) {
   const int64_t tokens = static_cast<int64_t>(p.batch) * p.n_tokens;
-  const int64_t grid = (tokens + 3) / 4;
-  // About 2M threads: head groups = 2^21 / (tokens * 64), at least 1.
-  const int heads = p.num_q_heads + p.num_kv_heads;
-  const int64_t want = ((int64_t{1} << 21) + tokens * 64 - 1) / (tokens * 64);
-  const int groups_wanted = static_cast<int>(std::min<int64_t>(std::max<int64_t>(want, 1), heads));
-  const int group_heads = (heads + groups_wanted - 1) / groups_wanted;
-  const int groups = (heads + group_heads - 1) / group_heads;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  rotate_chunk_kernel<<<dim3(static_cast<unsigned>(grid), static_cast<unsigned>(groups)), 256, 0,
-                        stream>>>(p, group_heads);
+  if (tokens == 0) return hipSuccess;
+  if (tokens > 0x7fffffff) return hipErrorInvalidValue;
+  rotate_chunk_kernel<<<static_cast<unsigned>(tokens), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
