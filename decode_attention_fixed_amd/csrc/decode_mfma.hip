@@ -66,6 +66,8 @@ namespace swa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
@@ -77,27 +79,36 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const Vec16& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+__device__ __forceinline__ f16x8_t as_f16x8(const Vec16& v) {
+  return __builtin_bit_cast(f16x8_t, v);
+}
+
+// Eight int8 codes (two 32-bit words) as fp16, exactly: a code c, its sign
+// bit flipped, is the byte c + 128; placed under the fp16 exponent of 1024
+// (0x64, unit spacing) it reads 1152 + c, and one packed subtraction of 1152
+// leaves c (all exact: |c| <= 127).  Two byte permutes and one packed add per
+// four codes.
+__device__ __forceinline__ Vec16 codes8_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
+  // v_perm_b32 byte selectors: 0..3 pick bytes of the second operand (the
+  // codes), 4 picks the first operand's 0x64
+  auto pair = [&](uint32_t x, uint32_t sel) {
+    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, x, sel);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, b) + off);
+  };
+  Vec16 r;
+  r.w[0] = pair(x0, 0x04010400u);
+  r.w[1] = pair(x0, 0x04030402u);
+  r.w[2] = pair(x1, 0x04010400u);
+  r.w[3] = pair(x1, 0x04030402u);
+  return r;
+}
+
 // Four int8 codes (one 32-bit word) as exact floats.
 __device__ __forceinline__ void i8x4_to_f32(uint32_t w, float* x) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) x[k] = static_cast<float>(static_cast<int8_t>((w >> (8 * k)) & 0xffu));
-}
-
-// bf16 bits of two small integers held exactly in floats (truncation is exact).
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
-  return (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
-}
-
-// 16 int8 codes -> two chunks of 8 bf16 values (elements 0-7, 8-15).
-__device__ __forceinline__ void i8x16_to_bf16(const Vec16& v, Vec16& lo, Vec16& hi) {
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) i8x4_to_f32(v.w[i], x + 4 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo.w[i] = pack_bf16_exact(x[2 * i], x[2 * i + 1]);
-    hi.w[i] = pack_bf16_exact(x[8 + 2 * i], x[8 + 2 * i + 1]);
-  }
 }
 
 // K/V rows are read once per step and never again before the whole cache has
@@ -244,11 +255,12 @@ constexpr int subtiles() {
   return G <= 2 ? 4 : ((G < 8 && !POOL ? 2 : 1) * (I8 ? (POOL ? 4 : 2) : 1));
 }
 
-template <int G, int NW, int NS_>
+// RC: 16-byte chunks per staged K row (16 for bf16 rows, 8 for int8 codes).
+template <int G, int NW, int NS_, int RC = 16>
 struct Smem {
   static constexpr int NS = NS_;
   static constexpr int TILE = 16 * NS;
-  static constexpr int KBUF = TILE * 16;  // 16-byte chunks per wave: TILE rows x 256 B
+  static constexpr int KBUF = TILE * RC;  // 16-byte chunks per wave: TILE staged rows
   static constexpr size_t KBYTES = static_cast<size_t>(NW) * KBUF * 16;
   static constexpr size_t ABYTES = static_cast<size_t>(NW) * G * kD * sizeof(float);
   // each wave's K tile while streaming; the same bytes then hold the waves'
@@ -401,11 +413,11 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
 // `slot` (layout [slot][head][d]).  Every thread of the workgroup must call it
 // with the same arguments; it returns with LDS free for reuse.
 template <int G, class Rows, int NW, bool FUSED = false, bool I8 = false, int NS_>
-__device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b, int kvh, int t0,
+__device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16>& sm, int b, int kvh, int t0,
                              int t1, bool direct, size_t slot, NewRow<G>* nr = nullptr,
                              NewToken nt = NewToken{}) {
   static_assert(!(FUSED && I8), "the fused step appends bf16 rows");
-  using Sm = Smem<G, NW, NS_>;
+  using Sm = Smem<G, NW, NS_, I8 ? 8 : 16>;
   constexpr int NS = Sm::NS;
   constexpr int TILE = Sm::TILE;
   constexpr int KBUF = Sm::KBUF;
@@ -422,25 +434,58 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
   constexpr int KL = I8 ? 2 : 4;  // K load instructions per 16-row subtile
 
   // B operand: the g query heads of this kv head, zero-padded to 16 (the
-  // fused step rotates them into LDS first).
+  // fused step rotates them into LDS first).  Lane (lc, lq) holds 8 dims of
+  // head lc per MFMA step s: dims 32s + 8lq .. for bf16 tiles; for int8
+  // tiles the dims in the order the lane reads its row's codes back from
+  // LDS, 64(s/2) + 16lq + 8(s%2) .. (the same permutation of the dims on
+  // both operands).
+  // int8 tiles multiply in fp16: the query is scaled per head by the power
+  // of two 2^k that brings its largest |element| into [2^14, 2^15), which is
+  // exact (a bf16 value has 8 significant bits), and the scores by 2^-k.
   if constexpr (FUSED) fused_step_prologue<G, NW>(p, *nr, nt, b, kvh, rows);
-  bf16x8_t qop[kKSteps];
+  Vec16 qop[kKSteps];
+  float qinv = 1.f;
   {
     const uint16_t* qb = static_cast<const uint16_t*>(p.q);
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) {
+      const int off = I8 ? 64 * (s >> 1) + 16 * lq + 8 * (s & 1) : 32 * s + 8 * lq;
       Vec16 v{};
       if (lc < G) {
         if constexpr (FUSED)
-          v = load16(&nr->q[lc][32 * s + 8 * lq]);
+          v = load16(&nr->q[lc][off]);
         else
-          v = load16(qb + (head0 + lc) * kD + 32 * s + 8 * lq);
+          v = load16(qb + (head0 + lc) * kD + off);
       }
-      qop[s] = as_bf16x8(v);
+      qop[s] = v;
+    }
+    if constexpr (I8) {
+      float amax = 0.f;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qop[s].w[i])), fabsf(bf16_hi(qop[s].w[i]))));
+      amax = xor_max(amax, 16);
+      amax = xor_max(amax, 32);
+      int k = 0;  // zero or non-finite heads keep their values
+      if (amax > 0.f && amax <= 3.4e38f) {
+        k = 15 - __builtin_amdgcn_frexp_expf(amax);  // amax = f 2^e, f in [1/2, 1)
+        k = k < -126 ? -126 : (k > 126 ? 126 : k);
+      }
+      qinv = ldexpf(1.f, -k);
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2_t h = {static_cast<_Float16>(ldexpf(bf16_lo(qop[s].w[i]), k)),
+                             static_cast<_Float16>(ldexpf(bf16_hi(qop[s].w[i]), k))};
+          qop[s].w[i] = __builtin_bit_cast(uint32_t, h);
+        }
     }
   }
 
-  const float c = p.score_scale_log2;
+  const float c = p.score_scale_log2 * qinv;
   float m = kNegInf;  // running max of head lc (log2 units)
   float lsum = 0.f;   // this lane's share of the running sum of head lc
   float acc[G][8];
@@ -465,7 +510,10 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
     bool live[NS];
   };
   // Issues the tile's loads (rows ts .. of the staged chunk [c0, c1)).
-  auto load_tile = [&](Tile& T, int ts, int c0, int c1) {
+  // `whole`: the tile lies inside [c0, c1), so no row needs clamping.
+  auto load_tile = [&](Tile& T, int ts, int c0, int c1, auto whole) {
+    constexpr bool kIn = decltype(whole)::value;
+    constexpr bool kNoClamp = kIn || Rows::kWholeSubtiles;
     // Every load instruction reads four whole 256-byte rows; K first, so
     // the score phase waits on K while the V loads are still in flight.
 #pragma unroll
@@ -473,23 +521,23 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
       const int tu = ts + 16 * u;
       T.vm[u] = 0;
       T.base[u] = 0;
-      T.live[u] = tu < c1 && rows.subtile(p, sm.blk, c0, tu, T.base[u]);
+      T.live[u] = (kIn || tu < c1) && rows.subtile(p, sm.blk, c0, tu, T.base[u]);
       if (T.live[u]) {
         const int tk = tu + lc;
-        const bool okk = tk < c1 && rows.row_ok(tk);
+        const bool okk = (kIn || tk < c1) && rows.row_ok(tk);
         T.vm[u] = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
         const KT* ks = kb + T.base[u];  // uniform: scalar base register
         if constexpr (I8) {
 #pragma unroll
           for (int i = 0; i < KL; ++i) {
             const int rho = 8 * i + (lane >> 3);
-            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
+            const int row = kNoClamp || tu + rho < c1 ? rho : 0;
             T.kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 16 * (lane & 7)));
           }
           // lane l loads the scales of row 4lq + (l % 4); row 4lq + r is then
           // lane 16lq + r's, one DPP broadcast away
           const int sr = 4 * lq + (lc & 3);
-          const int rr = Rows::kWholeSubtiles || tu + sr < c1 ? sr : 0;
+          const int rr = kNoClamp || tu + sr < c1 ? sr : 0;
           const size_t srow = (T.base[u] >> 7) + rr;  // kD = 128 codes per row
           T.ksl[u] = p.k_scale[srow];
           T.vsl[u] = p.v_scale[srow];
@@ -497,7 +545,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 #pragma unroll
           for (int i = 0; i < KL; ++i) {
             const int rho = 4 * i + lq;
-            const int row = Rows::kWholeSubtiles || tu + rho < c1 ? rho : 0;
+            const int row = kNoClamp || tu + rho < c1 ? rho : 0;
             T.kr[u][i] = load16_stream(ks + static_cast<uint32_t>(row * kD + 8 * lc));
           }
         }
@@ -516,7 +564,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * lq + r;
-          const int row = Rows::kWholeSubtiles || tu + i < c1 ? i : 0;
+          const int row = kNoClamp || tu + i < c1 ? i : 0;
           if constexpr (I8)
             T.vr[u][r] = load8_stream(vs + static_cast<uint32_t>(row * kD + 8 * lc));
           else
@@ -533,39 +581,58 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
   auto compute_tile = [&](Tile& T, int ts, int c1) {
     // K chunks into the MFMA A-operand layout through LDS (DS instructions
     // of one wave execute in order; the wave barriers only stop the compiler
-    // from moving LDS accesses across each other).
-    __builtin_amdgcn_wave_barrier();
+    // from moving LDS accesses across each other).  int8 rows are staged as
+    // codes, 8 chunks a row at chunk c ^ swz8(row), and read back as chunks
+    // lq and 4 + lq of row lc (16 codes = two MFMA steps each); the XOR puts
+    // every 8 and every 16 lanes of a read on distinct banks.
+    Vec16 ka[NS][I8 ? 2 : kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
+                                     // (int8: codes of chunks lq, 4 + lq)
+    if constexpr (I8) {
+      auto swz8 = [](int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; };
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < NS; ++u)
+      for (int u = 0; u < NS; ++u)
 #pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        if constexpr (I8) {  // 16 codes -> bf16 chunks 2c and 2c + 1 of the row
+        for (int i = 0; i < KL; ++i) {
           const int rho = 8 * i + (lane >> 3);
-          const int c8 = lane & 7;
-          Vec16 lo, hi;
-          i8x16_to_bf16(T.kr[u][i], lo, hi);
-          s_k[(u * 16 + rho) * 16 + ((2 * c8) ^ rho)] = make_uint4(lo.w[0], lo.w[1], lo.w[2], lo.w[3]);
-          s_k[(u * 16 + rho) * 16 + ((2 * c8 + 1) ^ rho)] =
-              make_uint4(hi.w[0], hi.w[1], hi.w[2], hi.w[3]);
-        } else {
+          s_k[(u * 16 + rho) * 8 + ((lane & 7) ^ swz8(rho))] =
+              make_uint4(T.kr[u][i].w[0], T.kr[u][i].w[1], T.kr[u][i].w[2], T.kr[u][i].w[3]);
+        }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 t = s_k[(u * 16 + lc) * 8 + ((4 * j + lq) ^ swz8(lc))];
+          ka[u][j].w[0] = t.x;
+          ka[u][j].w[1] = t.y;
+          ka[u][j].w[2] = t.z;
+          ka[u][j].w[3] = t.w;
+        }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
           const int rho = 4 * i + lq;
           s_k[(u * 16 + rho) * 16 + (lc ^ rho)] =
               make_uint4(T.kr[u][i].w[0], T.kr[u][i].w[1], T.kr[u][i].w[2], T.kr[u][i].w[3]);
         }
-      }
-    __builtin_amdgcn_wave_barrier();
-    Vec16 ka[NS][kKSteps];  // lane l: row lc, dims 32s + 8lq .. +7
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < NS; ++u)
+      for (int u = 0; u < NS; ++u)
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
-        ka[u][s].w[0] = t.x;
-        ka[u][s].w[1] = t.y;
-        ka[u][s].w[2] = t.z;
-        ka[u][s].w[3] = t.w;
-      }
-    __builtin_amdgcn_wave_barrier();
+        for (int s = 0; s < kKSteps; ++s) {
+          const uint4 t = s_k[(u * 16 + lc) * 16 + ((4 * s + lq) ^ lc)];
+          ka[u][s].w[0] = t.x;
+          ka[u][s].w[1] = t.y;
+          ka[u][s].w[2] = t.z;
+          ka[u][s].w[3] = t.w;
+        }
+      __builtin_amdgcn_wave_barrier();
+    }
     uint32_t all = 0xffffu;
 #pragma unroll
     for (int u = 0; u < NS; ++u) all &= T.vm[u];
@@ -578,8 +645,16 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
     for (int u = 0; u < NS; ++u) {
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), qop[s], d, 0, 0, 0);
+      for (int s = 0; s < kKSteps; ++s) {
+        if constexpr (I8) {  // 8 codes of row lc -> exact fp16 operand
+          const Vec16& w = ka[u][s >> 1];
+          const Vec16 a = codes8_to_f16(w.w[2 * (s & 1)], w.w[2 * (s & 1) + 1]);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(qop[s]), d, 0, 0, 0);
+        } else {
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), as_bf16x8(qop[s]), d, 0,
+                                                      0, 0);
+        }
+      }
       if constexpr (FUSED) {
         const int tu = ts + 16 * u;
         if (nt.shift && tu < p.sinks) {  // sink rows: the query at its cache position
@@ -609,15 +684,18 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
     tmax = xor_max(tmax, 32);
     const float mn = fmaxf(m, tmax);
     // mn == -inf: nothing resident so far for this head; keep everything at 0
-    const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
+    // (the hardware 2^x: exact 0 at -inf; arguments are <= 0 and results
+    // below 2^-126, far under anything a sum keeps, may flush to 0)
+    const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     m = mn;
+    const float mb = mn == kNegInf ? 0.f : mn;  // absent rows (x = -inf) give 0
     float pr[NS][4];
     float tsum = 0.f;
 #pragma unroll
     for (int u = 0; u < NS; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[u][r] = x[u][r] == kNegInf ? 0.f : exp2f(x[u][r] - mn);
+        pr[u][r] = __builtin_amdgcn_exp2f(x[u][r] - mb);
         tsum += pr[u][r];
       }
     lsum = lsum * alpha + tsum;
@@ -675,7 +753,10 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
     __syncthreads();
     for (int ts = c0 + wave * TILE; ts < c1; ts += NW * TILE) {
       Tile A;
-      load_tile(A, ts, c0, c1);
+      if (ts + TILE <= c1)
+        load_tile(A, ts, c0, c1, std::true_type{});
+      else
+        load_tile(A, ts, c0, c1, std::false_type{});
       compute_tile(A, ts, c1);
     }
     __syncthreads();  // the next chunk restages the block ids
@@ -754,7 +835,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_>& sm, int b,
 // slot (b * Hkv + kv head) * num_splits + split.
 template <int G, int NW, bool FUSED, bool I8>
 __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
-  __shared__ Smem<G, NW, subtiles<G, false, I8>()> sm;
+  __shared__ Smem<G, NW, subtiles<G, false, I8>(), I8 ? 8 : 16> sm;
   const int ns = p.num_splits;
   const int split = blockIdx.x % ns;
   const int unit = blockIdx.x / ns;
@@ -967,7 +1048,7 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 template <int G, int NW, bool I8>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
   constexpr int NT = NW * 64;
-  __shared__ Smem<G, NW, subtiles<G, true, I8>()> sm;
+  __shared__ Smem<G, NW, subtiles<G, true, I8>(), I8 ? 8 : 16> sm;
   __shared__ SeqChunk<NT> sc;
   const int64_t hkv = p.num_kv_heads;
   const int64_t nwg = gridDim.x;
