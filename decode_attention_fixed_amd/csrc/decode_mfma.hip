@@ -68,6 +68,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
@@ -432,6 +434,9 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
   const KT* kb = static_cast<const KT*>(p.k);
   const KT* vb = static_cast<const KT*>(p.v);
   constexpr int KL = I8 ? 2 : 4;  // K load instructions per 16-row subtile
+  // int8 tiles with g >= 3 multiply P*V on the matrix core: the VALU form
+  // costs g FMAs per (row, dim), the MFMA form a fixed repacking of V
+  constexpr bool kMfmaPV = I8 && G >= 3;
 
   // B operand: the g query heads of this kv head, zero-padded to 16 (the
   // fused step rotates them into LDS first).  Lane (lc, lq) holds 8 dims of
@@ -488,11 +493,17 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
   const float c = p.score_scale_log2 * qinv;
   float m = kNegInf;  // running max of head lc (log2 units)
   float lsum = 0.f;   // this lane's share of the running sum of head lc
-  float acc[G][8];
+  // P*V accumulators.  VALU form: acc[h][e] = head h, dim 8lc + e, over this
+  // lane's rows.  MFMA form (int8 tiles, g >= 3): accm[nb][j] = head 4lq + j,
+  // dim 8lc + nb, over all rows of the wave.
+  float acc[kMfmaPV ? 1 : G][8];
+  f32x4_t accm[kMfmaPV ? 8 : 1];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < (kMfmaPV ? 1 : G); ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < (kMfmaPV ? 8 : 1); ++nb) accm[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // This wave's K staging area: row rho of subtile u, 16-byte chunk c lives at
   // chunk (u * 16 + rho) * 16 + (c ^ rho), so both the row-wise writes and the
@@ -504,7 +515,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
     Vec16 kr[NS][KL];  // row-wise K chunks: row 4i + lq of subtile u, chunk lc
                        // (int8: row 8i + l / 8, 16-byte chunk l % 8)
     std::conditional_t<I8, uint2, Vec16> vr[NS][4];  // V: row 4lq + r of subtile u, dims 8lc..
-    float ksl[NS], vsl[NS];  // int8: K and V scales of row lc of subtile u
+    float ksl[NS], vsl[NS];  // int8: K and V scales of row 4lq + (lc & 3) of subtile u
     uint32_t vm[NS];         // bit i: row ts + 16u + i is resident
     size_t base[NS];
     bool live[NS];
@@ -712,40 +723,103 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
     }
 
     // P * V
+    if constexpr (kMfmaPV) {
+      // O[head][dim] += P[head][row] V[row][dim], v_mfma_f32_16x16x16_f16 per
+      // 16 rows and 16 dims: A = P (lane (lc, lq): head lc, rows 4lq + i,
+      // exactly pr[u][i]); B = V (lane (lc, lq): rows 4lq + i, dim 8lc + nb
+      // in block nb, byte nb of the lane's own codes of those rows, made
+      // fp16 as for K).  P carries the V scale; the tile's weights are scaled
+      // by 2^k, k from the largest V scale of its present rows, into fp16's
+      // range, and the tile's product by 2^-k on the way into accm.
+      float vmax = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = row_bcast_dyn(alpha, h);
+      for (int u = 0; u < NS; ++u) {
+        // vsl[u]: the scale of row 4lq + (lc & 3); absent rows' may hold anything
+        const bool okr = (T.vm[u] >> (4 * lq + (lc & 3))) & 1u;
+        vmax = fmaxf(vmax, okr ? T.vsl[u] : 0.f);
+      }
+      vmax = xor_max(vmax, 1);
+      vmax = xor_max(vmax, 2);
+      vmax = xor_max(vmax, 16);
+      vmax = xor_max(vmax, 32);
+      int k = 0;
+      if (vmax > 0.f && vmax <= 3.4e38f) {
+        k = 15 - __builtin_amdgcn_frexp_expf(vmax);
+        k = k < -126 ? -126 : (k > 126 ? 126 : k);
+      }
+      const float up = ldexpf(1.f, k), down = ldexpf(1.f, -k);
+      f32x4_t t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-    }
+      for (int nb = 0; nb < 8; ++nb) t[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
 #pragma unroll
-    for (int u = 0; u < NS; ++u)
+      for (int u = 0; u < NS; ++u) {
+        const f16x2_t a01 = __builtin_convertvector(f32x2_t{pr[u][0] * up, pr[u][1] * up}, f16x2_t);
+        const f16x2_t a23 = __builtin_convertvector(f32x2_t{pr[u][2] * up, pr[u][3] * up}, f16x2_t);
+        const f16x4_t a = {a01[0], a01[1], a23[0], a23[1]};
+        uint32_t x[4][2];  // codes of rows 4lq + i, sign bits flipped
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v[8];
-        if constexpr (I8) {
-          i8x4_to_f32(T.vr[u][r].x, v);
-          i8x4_to_f32(T.vr[u][r].y, v + 4);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_lo(T.vr[u][r].w[i]);
-            v[2 * i + 1] = bf16_hi(T.vr[u][r].w[i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          x[i][0] = T.vr[u][i].x ^ 0x80808080u;
+          x[i][1] = T.vr[u][i].y ^ 0x80808080u;
         }
-        if (!I8 && !all_ok) {
-          const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float ph = row_bcast_dyn(pr[u][r], h);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+        for (int nb = 0; nb < 8; ++nb) {
+          const int w = nb >> 2, bsel = nb & 3;
+          // bytes [row i, 0, row i + 1, 0], then 0x64 above each: 1152 + c
+          const uint32_t sel = 0x0c000c00u | static_cast<uint32_t>((4 + bsel) << 16) |
+                               static_cast<uint32_t>(bsel);
+          const uint32_t b01 = __builtin_amdgcn_perm(x[1][w], x[0][w], sel) | 0x64006400u;
+          const uint32_t b23 = __builtin_amdgcn_perm(x[3][w], x[2][w], sel) | 0x64006400u;
+          const f16x2_t v01 = __builtin_bit_cast(f16x2_t, b01) + off;
+          const f16x2_t v23 = __builtin_bit_cast(f16x2_t, b23) + off;
+          const f16x4_t bv = {v01[0], v01[1], v23[0], v23[1]};
+          t[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bv, t[nb], 0, 0, 0);
         }
       }
-    };
+      float aj[4];  // alpha of head 4lq + j (lanes 0..15 hold heads 0..15)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * lq + j);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) accm[nb][j] = fmaf(t[nb][j], down, accm[nb][j] * aj[j]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float a = row_bcast_dyn(alpha, h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+      }
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[8];
+          if constexpr (I8) {
+            i8x4_to_f32(T.vr[u][r].x, v);
+            i8x4_to_f32(T.vr[u][r].y, v + 4);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[2 * i] = bf16_lo(T.vr[u][r].w[i]);
+              v[2 * i + 1] = bf16_hi(T.vr[u][r].w[i]);
+            }
+          }
+          if (!I8 && !all_ok) {
+            const bool ok = (T.vm[u] >> (4 * lq + r)) & 1u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float ph = row_bcast_dyn(pr[u][r], h);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+          }
+        }
+    }
+  };
 
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int c1 = min(c0 + kChunk, t1);
@@ -762,23 +836,32 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
     __syncthreads();  // the next chunk restages the block ids
   }
 
-  // Wave totals: sum the four row groups.
+  // Wave totals: sum the four row groups (the MFMA form has summed them).
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (!kMfmaPV) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16);
-      acc[h][e] += __shfl_xor(acc[h][e], 32);
-    }
+      for (int e = 0; e < 8; ++e) {
+        acc[h][e] += __shfl_xor(acc[h][e], 16);
+        acc[h][e] += __shfl_xor(acc[h][e], 32);
+      }
+  }
   float(*s_acc)[G][kD] = reinterpret_cast<float(*)[G][kD]>(sm.raw);
   __syncthreads();  // every wave is done with its K staging area (aliases s_acc)
   if (lane < G) {
     sm.m[wave][lane] = m;
     sm.l[wave][lane] = lsum;
   }
-  if (lq == 0) {
+  if constexpr (kMfmaPV) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * lq + j < G) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) s_acc[wave][4 * lq + j][8 * lc + nb] = accm[nb][j];
+      }
+  } else if (lq == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll

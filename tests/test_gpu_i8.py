@@ -192,3 +192,24 @@ def test_mha_ring_i8_full_size():
             assert np.array_equal(sp[b], ring_slot_table(w, b, 1))
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("scale", [1e-3, 40.0])
+@pytest.mark.parametrize("heads", [(6, 1), (8, 2), (4, 4)])
+def test_pool_i8_value_scales(scale, heads):
+    """Rows far from unit size (every draw times 1e-3, or times 40: flat and
+    one-hot softmax) through every P*V form (g = 6, 4: matrix core with the
+    per-tile power-of-two weight scaling; g = 1: VALU), relative to the
+    largest output: the bar 2e-3 scaled to the values' size."""
+    hq, hkv = heads
+    w = PoolWorkload(name="p8s", seed=88, batch=2, num_q_heads=hq, num_kv_heads=hkv,
+                     head_dim=128, dtype="bf16", block_size=64, logical_blocks=48, pool_slots=20,
+                     rope_base=10000.0, scale=scale, decode_steps=1, cache="i8")
+    st = _pool_state(w)
+    st.step(st.step_query(0))
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy()
+    for b in range(w.batch):
+        want, _ = pool_expected(w, b, 0)
+        bar = TOL * float(np.abs(want).max())
+        assert float(np.abs(out[b] - want).max()) <= bar, (b, scale, heads)
