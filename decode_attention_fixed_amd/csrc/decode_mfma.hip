@@ -243,18 +243,17 @@ struct PoolRows {
   int skip = -1;  // unused: pools have no fused step
 };
 
-// Row subtiles (16 rows each) per wave tile: 4 when few query heads share the
-// kv head, fewer when the P*V accumulators take more registers (two waves per
-// SIMD cap a wave at 256 VGPRs).  Pools stream best with one subtile per tile
-// for g >= 3 (measured: 1-1.5% over two on the paged and pool workloads);
-// ring caches with two for g = 3..6.
-// int8 rows carry half the bytes of a bf16 subtile and half its registers:
-// twice the subtiles on rings with g >= 3 and four times on pools (measured:
-// paged-i8 319 -> 285 us, long-pool-b16-i8 337 -> 282 us, gqa-ring-i8 152 ->
-// 148 us); g <= 2 keeps four, all the LDS staging area allows.
+// Row subtiles (16 rows each) per wave tile, as measured: 4 when few query
+// heads share the kv head (2 for bf16 pools with g = 2, which keeps them
+// clear of register spills); for g >= 3, one on bf16 pools (two were 1-2%
+// slower) and two on bf16 rings.  int8 rows carry half the bytes and half
+// the registers of bf16 ones: twice the subtiles on rings with g >= 3 and
+// four times on pools (two on pools: 2-5% slower); g <= 2 keeps four (eight,
+// or two tiles in flight, were slower).
 template <int G, bool POOL, bool I8 = false>
 constexpr int subtiles() {
-  return G <= 2 ? 4 : ((G < 8 && !POOL ? 2 : 1) * (I8 ? (POOL ? 4 : 2) : 1));
+  return G <= 2 ? (G == 2 && POOL && !I8 ? 2 : 4)
+                : ((G < 8 && !POOL ? 2 : 1) * (I8 ? (POOL ? 4 : 2) : 1));
 }
 
 // RC: 16-byte chunks per staged K row (16 for bf16 rows, 8 for int8 codes).
@@ -434,9 +433,9 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
   const KT* kb = static_cast<const KT*>(p.k);
   const KT* vb = static_cast<const KT*>(p.v);
   constexpr int KL = I8 ? 2 : 4;  // K load instructions per 16-row subtile
-  // int8 tiles with g >= 3 multiply P*V on the matrix core: the VALU form
-  // costs g FMAs per (row, dim), the MFMA form a fixed repacking of V
-  constexpr bool kMfmaPV = I8 && G >= 3;
+  // g >= 3 multiplies P*V on the matrix core: the VALU form costs g FMAs per
+  // (row, dim), the MFMA form a fixed repacking of V
+  constexpr bool kMfmaPV = G >= 3;
 
   // B operand: the g query heads of this kv head, zero-padded to 16 (the
   // fused step rotates them into LDS first).  Lane (lc, lq) holds 8 dims of
@@ -494,8 +493,8 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
   float m = kNegInf;  // running max of head lc (log2 units)
   float lsum = 0.f;   // this lane's share of the running sum of head lc
   // P*V accumulators.  VALU form: acc[h][e] = head h, dim 8lc + e, over this
-  // lane's rows.  MFMA form (int8 tiles, g >= 3): accm[nb][j] = head 4lq + j,
-  // dim 8lc + nb, over all rows of the wave.
+  // lane's rows.  MFMA form (g >= 3): accm[nb][j] = head 4lq + j, dim
+  // 8lc + nb, over all rows of the wave.
   float acc[kMfmaPV ? 1 : G][8];
   f32x4_t accm[kMfmaPV ? 8 : 1];
 #pragma unroll
@@ -724,66 +723,116 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
 
     // P * V
     if constexpr (kMfmaPV) {
-      // O[head][dim] += P[head][row] V[row][dim], v_mfma_f32_16x16x16_f16 per
-      // 16 rows and 16 dims: A = P (lane (lc, lq): head lc, rows 4lq + i,
-      // exactly pr[u][i]); B = V (lane (lc, lq): rows 4lq + i, dim 8lc + nb
-      // in block nb, byte nb of the lane's own codes of those rows, made
-      // fp16 as for K).  P carries the V scale; the tile's weights are scaled
-      // by 2^k, k from the largest V scale of its present rows, into fp16's
-      // range, and the tile's product by 2^-k on the way into accm.
-      float vmax = 0.f;
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        // vsl[u]: the scale of row 4lq + (lc & 3); absent rows' may hold anything
-        const bool okr = (T.vm[u] >> (4 * lq + (lc & 3))) & 1u;
-        vmax = fmaxf(vmax, okr ? T.vsl[u] : 0.f);
-      }
-      vmax = xor_max(vmax, 1);
-      vmax = xor_max(vmax, 2);
-      vmax = xor_max(vmax, 16);
-      vmax = xor_max(vmax, 32);
-      int k = 0;
-      if (vmax > 0.f && vmax <= 3.4e38f) {
-        k = 15 - __builtin_amdgcn_frexp_expf(vmax);
-        k = k < -126 ? -126 : (k > 126 ? 126 : k);
-      }
-      const float up = ldexpf(1.f, k), down = ldexpf(1.f, -k);
-      f32x4_t t[8];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) t[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const f16x2_t a01 = __builtin_convertvector(f32x2_t{pr[u][0] * up, pr[u][1] * up}, f16x2_t);
-        const f16x2_t a23 = __builtin_convertvector(f32x2_t{pr[u][2] * up, pr[u][3] * up}, f16x2_t);
-        const f16x4_t a = {a01[0], a01[1], a23[0], a23[1]};
-        uint32_t x[4][2];  // codes of rows 4lq + i, sign bits flipped
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i][0] = T.vr[u][i].x ^ 0x80808080u;
-          x[i][1] = T.vr[u][i].y ^ 0x80808080u;
-        }
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const int w = nb >> 2, bsel = nb & 3;
-          // bytes [row i, 0, row i + 1, 0], then 0x64 above each: 1152 + c
-          const uint32_t sel = 0x0c000c00u | static_cast<uint32_t>((4 + bsel) << 16) |
-                               static_cast<uint32_t>(bsel);
-          const uint32_t b01 = __builtin_amdgcn_perm(x[1][w], x[0][w], sel) | 0x64006400u;
-          const uint32_t b23 = __builtin_amdgcn_perm(x[3][w], x[2][w], sel) | 0x64006400u;
-          const f16x2_t v01 = __builtin_bit_cast(f16x2_t, b01) + off;
-          const f16x2_t v23 = __builtin_bit_cast(f16x2_t, b23) + off;
-          const f16x4_t bv = {v01[0], v01[1], v23[0], v23[1]};
-          t[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bv, t[nb], 0, 0, 0);
-        }
-      }
       float aj[4];  // alpha of head 4lq + j (lanes 0..15 hold heads 0..15)
 #pragma unroll
       for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * lq + j);
+      f32x4_t t[8];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+      for (int nb = 0; nb < 8; ++nb) t[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8) {
+        // O[head][dim] += P[head][row] V[row][dim], v_mfma_f32_16x16x16_f16 per
+        // 16 rows and 16 dims: A = P (lane (lc, lq): head lc, rows 4lq + i,
+        // exactly pr[u][i]); B = V (lane (lc, lq): rows 4lq + i, dim 8lc + nb
+        // in block nb, byte nb of the lane's own codes of those rows, made
+        // fp16 as for K).  P carries the V scale; the tile's weights are scaled
+        // by 2^k, k from the largest V scale of its present rows, into fp16's
+        // range, and the tile's product by 2^-k on the way into accm.
+        float vmax = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) accm[nb][j] = fmaf(t[nb][j], down, accm[nb][j] * aj[j]);
+        for (int u = 0; u < NS; ++u) {
+          // vsl[u]: the scale of row 4lq + (lc & 3); absent rows' may hold anything
+          const bool okr = (T.vm[u] >> (4 * lq + (lc & 3))) & 1u;
+          vmax = fmaxf(vmax, okr ? T.vsl[u] : 0.f);
+        }
+        vmax = xor_max(vmax, 1);
+        vmax = xor_max(vmax, 2);
+        vmax = xor_max(vmax, 16);
+        vmax = xor_max(vmax, 32);
+        int k = 0;
+        if (vmax > 0.f && vmax <= 3.4e38f) {
+          k = 15 - __builtin_amdgcn_frexp_expf(vmax);
+          k = k < -126 ? -126 : (k > 126 ? 126 : k);
+        }
+        const float up = ldexpf(1.f, k), down = ldexpf(1.f, -k);
+        const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const f16x2_t a01 = __builtin_convertvector(f32x2_t{pr[u][0] * up, pr[u][1] * up}, f16x2_t);
+          const f16x2_t a23 = __builtin_convertvector(f32x2_t{pr[u][2] * up, pr[u][3] * up}, f16x2_t);
+          const f16x4_t a = {a01[0], a01[1], a23[0], a23[1]};
+          uint32_t x[4][2];  // codes of rows 4lq + i, sign bits flipped
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i][0] = T.vr[u][i].x ^ 0x80808080u;
+            x[i][1] = T.vr[u][i].y ^ 0x80808080u;
+          }
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int w = nb >> 2, bsel = nb & 3;
+            // bytes [row i, 0, row i + 1, 0], then 0x64 above each: 1152 + c
+            const uint32_t sel = 0x0c000c00u | static_cast<uint32_t>((4 + bsel) << 16) |
+                                 static_cast<uint32_t>(bsel);
+            const uint32_t b01 = __builtin_amdgcn_perm(x[1][w], x[0][w], sel) | 0x64006400u;
+            const uint32_t b23 = __builtin_amdgcn_perm(x[3][w], x[2][w], sel) | 0x64006400u;
+            const f16x2_t v01 = __builtin_bit_cast(f16x2_t, b01) + off;
+            const f16x2_t v23 = __builtin_bit_cast(f16x2_t, b23) + off;
+            const f16x4_t bv = {v01[0], v01[1], v23[0], v23[1]};
+            t[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bv, t[nb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) accm[nb][j] = fmaf(t[nb][j], down, accm[nb][j] * aj[j]);
+      } else {
+        // O[head][dim] += P[head][row] V[row][dim] as above, with
+        // v_mfma_f32_16x16x16_bf16: B = the bf16 V rows as stored (absent
+        // rows zeroed: their bytes may be anything), A = P split into three
+        // bf16 terms (p with its low 16 bits cleared, then the same of the
+        // remainder, then the last remainder truncated), three products per
+        // block: P keeps 21 or more significant bits.
+        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hw[i] = __float_as_uint(pr[u][i]) & 0xffff0000u;
+            const float r1 = pr[u][i] - __uint_as_float(hw[i]);  // exact
+            mw[i] = __float_as_uint(r1) & 0xffff0000u;
+            lw[i] = __float_as_uint(r1 - __uint_as_float(mw[i]));  // exact
+          }
+          // the upper halves of two floats: one bf16 pair of the A operand
+          auto pack = [](const uint32_t* x) {
+            const uint32_t w[2] = {__builtin_amdgcn_perm(x[1], x[0], 0x07060302u),
+                                   __builtin_amdgcn_perm(x[3], x[2], 0x07060302u)};
+            return __builtin_bit_cast(s16x4_t, w);
+          };
+          const s16x4_t ah = pack(hw), am = pack(mw), al = pack(lw);
+          uint32_t vw[4][4];  // rows 4lq + i: bf16 pairs (dims 8lc + 2w, + 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = all_ok || ((T.vm[u] >> (4 * lq + i)) & 1u);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) vw[i][w] = ok ? T.vr[u][i].w[w] : 0u;
+          }
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int w = nb >> 1;
+            const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;  // the dim's half of each
+            const uint32_t bw[2] = {__builtin_amdgcn_perm(vw[1][w], vw[0][w], sel),
+                                    __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel)};
+            const s16x4_t bv = __builtin_bit_cast(s16x4_t, bw);
+            t[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, t[nb], 0, 0, 0);
+            t[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bv, t[nb], 0, 0, 0);
+            t[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, t[nb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) accm[nb][j] = fmaf(accm[nb][j], aj[j], t[nb][j]);
+      }
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -827,7 +876,8 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
     __syncthreads();
     for (int ts = c0 + wave * TILE; ts < c1; ts += NW * TILE) {
       Tile A;
-      if (ts + TILE <= c1)
+      // (two copies of the loads cost bf16 g = 2 its last free registers)
+      if (!(G == 2 && !I8) && ts + TILE <= c1)
         load_tile(A, ts, c0, c1, std::true_type{});
       else
         load_tile(A, ts, c0, c1, std::false_type{});
