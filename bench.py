@@ -46,7 +46,10 @@ token per sequence through the block manager (table and length updates, the
 token rows) and the decode over all tokens; KV bytes count each step's
 lengths after its append.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+--graph issues the timed steps as one captured HIP graph (every step keeps its
+own inputs and positions) instead of eager calls; `launch` says which.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--graph]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
 
@@ -171,7 +174,8 @@ def decode_source_sha() -> str:
 # GPU side
 # ---------------------------------------------------------------------------
 
-def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True) -> dict:
+def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True,
+            graph: bool = False) -> dict:
     import numpy as np
     import torch
 
@@ -333,15 +337,28 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
         decode(i)
     torch.cuda.synchronize()
 
-    # Region 1: whole steps, events only at the two ends.
+    # Region 1: whole steps, events only at the two ends.  With `graph`, the
+    # same steps (each with its own inputs and positions) are captured into
+    # one HIP graph beforehand and the region is its one replay.
     begin = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                i = warmup + s
+                pre(i)
+                decode(i)
+        torch.cuda.synchronize()
     wall0 = time.perf_counter()
     begin.record()
-    for s in range(steps):
-        i = warmup + s
-        pre(i)
-        decode(i)
+    if graph:
+        g.replay()
+    else:
+        for s in range(steps):
+            i = warmup + s
+            pre(i)
+            decode(i)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -561,6 +578,7 @@ def prefill_line(w, args, res) -> dict:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": describe(w),
         "tokens_per_s": round(w.batch * w.chunk * 1e3 / ms_per_step, 1),
         "roofline": roofline,
+        "launch": "one HIP graph of the timed steps" if args.graph else "eager calls",
     }
 
 
@@ -575,6 +593,10 @@ def main() -> int:
     ap.add_argument("--unfused", action="store_true",
                     help="ring caches: kv_append_rope + decode_attn_ring per step instead of "
                          "decode_step_ring")
+    ap.add_argument("--graph", action="store_true",
+                    help="issue the timed steps as one captured HIP graph (ring caches and "
+                         "read-only pools; the pager and the block manager run host logic "
+                         "every step)")
     ap.add_argument("--copy-stream", action="store_true",
                     help="long-pool-swap: run the block copies on a stream of their own, "
                          "overlapping the attention (default: on the attention stream)")
@@ -592,7 +614,11 @@ def main() -> int:
 
     from synth import WORKLOADS
     w = WORKLOADS[args.workload]
-    res = run_gpu(w, args.steps, args.warmup, args.unfused, not args.copy_stream)
+    if args.graph and w.kind in ("pager", "paged-append"):
+        print(f"--graph: workload {w.name} runs host logic every step and is not captured",
+              file=sys.stderr)
+        return 2
+    res = run_gpu(w, args.steps, args.warmup, args.unfused, not args.copy_stream, args.graph)
     if w.kind == "ring" and w.chunk:
         out = prefill_line(w, args, res)
         if not args.no_cpu_baseline:
@@ -628,6 +654,7 @@ def main() -> int:
         "steps_per_s": round(1e3 / ms_per_step, 1),
         "hbm_frac_of_peak": round(value_gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "launch": "one HIP graph of the timed steps" if args.graph else "eager calls",
     }
     if w.kind == "pager":
         per_step = res["blocks_loaded_region1"] / args.steps

@@ -76,6 +76,7 @@ _PROTOS = {
                                         _vp, _vp, ctypes.c_size_t, _vp]),
     "decode_step_ring_shifted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp,
                                                 _i32, _vp, _vp, ctypes.c_size_t, _vp]),
+    "swa_pos_advance": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "prefill_attn_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "prefill_attn_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
@@ -246,6 +247,14 @@ def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos:
                                 _ptr(out, "out"), _DTYPE_CODE[out.dtype],
                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pos_advance(pos: torch.Tensor, delta: int = 1, stream=None) -> None:
+    """pos += delta on the stream (int32 device tensor): lets a captured HIP
+    graph of decode steps replay at advancing positions."""
+    _check("swa_pos_advance",
+           LIB.swa_pos_advance(_ptr(pos, "pos", torch.int32), pos.numel(), delta,
+                               _stream(stream)))
 
 
 def decode_step_ring_shifted(handle: int, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libswa.so")
 
 SOURCES = ["swa_api.cpp", "pager_api.cpp", "blocks_api.cpp", "append_rope.hip", "decode.hip", "decode_mfma.hip",
-           "prefill.hip", "pager.hip"]
+           "prefill.hip", "pager.hip", "positions.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -399,6 +399,16 @@ swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const v
                    workspace_bytes, stream, true);
 }
 
+swa_status swa_pos_advance(int32_t* pos, int32_t n, int32_t delta, void* stream) {
+  if (n < 0) return fail(SWA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
+  if (n == 0) return ok();
+  if (pos == nullptr) return fail(SWA_ERR_INVALID_ARG, "pos is NULL");
+  if (!aligned(pos, 4)) return fail(SWA_ERR_INVALID_ARG, "pos must be 4-byte aligned");
+  return from_hip(swa::launch_add_i32(pos, static_cast<size_t>(n), delta,
+                                      static_cast<hipStream_t>(stream)),
+                  "swa_pos_advance");
+}
+
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t n_tokens, size_t* bytes) {
   if (bytes == nullptr) return fail(SWA_ERR_INVALID_ARG, "bytes is NULL");

@@ -151,6 +151,7 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
                                  int32_t head_dim, int32_t max_kv_tokens);
 
 hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream);
+hipError_t launch_add_i32(int32_t* dst, size_t n, int32_t delta, hipStream_t stream);
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream);
 hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream);
 hipError_t launch_write_paged_i8(const PagedWriteParams& p, hipStream_t stream);

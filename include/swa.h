@@ -201,6 +201,15 @@ swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const v
                                     float scale, void* out, swa_dtype out_dtype, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pos[i] += delta for i < n, on `stream` (one small kernel; results clamped
+ * to the int32 range).  Positions live in device memory, so a HIP graph that
+ * captures decode steps followed by this call replays with each step at the
+ * next position; every decode and append entry point above only launches
+ * kernels on `stream` (no allocation, synchronisation or memset), so it can
+ * be captured.  pos: [n] int32, device, 4-byte aligned; n >= 0 (0 launches
+ * nothing). */
+swa_status swa_pos_advance(int32_t* pos, int32_t n, int32_t delta, void* stream);
+
 /* Workspace (device bytes) of a prefill_attn_ring call with n_tokens tokens
  * per sequence.  Needs no initialisation. */
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

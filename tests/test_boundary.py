@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 29, declared
+    assert len(declared) == 30, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -159,6 +159,14 @@ def test_decode_ring_validation():
             B.SWA_ERR_INVALID_ARG
     finally:
         B.swa_cache_destroy(h)
+
+
+def test_pos_advance_validation():
+    L = B.LIB
+    assert L.swa_pos_advance(FAKE, -1, 1, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_pos_advance(None, 4, 1, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_pos_advance(FAKE + 2, 4, 1, None) == B.SWA_ERR_INVALID_ARG  # misaligned
+    assert L.swa_pos_advance(None, 0, 1, None) == B.SWA_OK  # nothing to do, nothing launched
 
 
 def test_decode_step_ring_validation():
