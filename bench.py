@@ -210,8 +210,6 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
         def decode(i):
             B.prefill_attn_ring(handle, inp["k"], inp["v"], pos_all[i], inp["q"], out, ws, lse)
     elif w.kind == "ring":
-        # int8 rings have no fused step: a step is the append, then the decode
-        unfused = unfused or getattr(w, "cache", "") == "i8"
         st = RingState(w)
         st.prefill()
         start = w.decode_start

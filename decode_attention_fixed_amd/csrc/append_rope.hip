@@ -253,23 +253,13 @@ __global__ __launch_bounds__(kAppendThreads) void blocks_update_kernel(BlocksUpd
   copy_rows16(src, head_bytes, dst, head_bytes, p.num_kv_heads, row_bytes * p.cow_rows[c]);
 }
 
-// int8 rows ([kvc] §5.1: INT8 cache).  A wave quantises one row of d values:
-// lane l < d/2 holds the row's elements e0 and e1 (a RoPE pair) as float64.
-//   a = max |x|,  s = float32(a / 127),  c = clamp(rint(x / s), -127, 127)
-// (s = 0 gives codes 0).  The scale is stored next to the codes' row.
+// Quantises the row held by the wave (quantize_pair_row) and stores its
+// codes, and its scale next to the codes' row.
 __device__ void quantize_row_store(double x0, double x1, bool active, int e0, int e1,
                                    int8_t* codes, float* scale) {
-  double a = active ? fmax(fabs(x0), fabs(x1)) : 0.0;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a = fmax(a, __shfl_xor(a, o));
-  const float s = static_cast<float>(a / 127.0);
-  const double sd = static_cast<double>(s);
+  double c0, c1;
+  const float s = quantize_pair_row(x0, x1, active, &c0, &c1);
   if (active) {
-    double c0 = 0.0, c1 = 0.0;
-    if (sd > 0.0) {
-      c0 = fmin(fmax(rint(x0 / sd), -127.0), 127.0);
-      c1 = fmin(fmax(rint(x1 / sd), -127.0), 127.0);
-    }
     codes[e0] = static_cast<int8_t>(c0);
     codes[e1] = static_cast<int8_t>(c1);
   }

@@ -311,8 +311,11 @@ struct NewRow {
 // per thread) and, in the workgroup that attends the token's slot, store the
 // rotated K row, the V row and the position, and compute the token's score
 // per head into nr.x.  Angles, rotation and rounding are the append
-// kernel's, so the cache is bit-identical to an append.
-template <int G, int NW>
+// kernel's, so the cache is bit-identical to an append.  int8 caches: the
+// K row is quantised from its float64 rotation and the V row from its bf16
+// values by the wave that holds the K pairs (quantize_pair_row, as the int8
+// append), and nr.k / nr.v hold the dequantised rows c * s.
+template <int G, int NW, bool I8 = false>
 __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const NewToken& nt,
                                     int b, int kvh, RingRows& rows) {
   constexpr int kHalf = kD / 2;
@@ -324,7 +327,9 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
   const size_t nrow = (static_cast<size_t>(b) * p.num_kv_heads + kvh) * kD;
   const uint16_t* qb = static_cast<const uint16_t*>(p.q) + head0 * kD;
   const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + nrow;
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + nrow;
   uint16_t r0[kPer], r1[kPer];
+  uint16_t w0[I8 ? kPer : 1], w1[I8 ? kPer : 1];  // int8: the V pair beside the K pair
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int w = min(tid + j * NW * 64, kItems - 1);
@@ -334,8 +339,13 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
     const uint16_t* src = h < G ? qb + h * kD : kn;
     r0[j] = src[i0];
     r1[j] = src[i1];
+    if constexpr (I8) {
+      w0[j] = vn[i0];
+      w1[j] = vn[i1];
+    }
   }
-  const Vec16 vraw = load16(static_cast<const uint16_t*>(p.v_new) + nrow + 8 * (tid & 15));
+  Vec16 vraw{};
+  if constexpr (!I8) vraw = load16(vn + 8 * (tid & 15));
   if (nt.app && tid < kHalf) {
     double sn, cs;
     rope_sincos(static_cast<double>(nt.pos), nt.theta, &sn, &cs);
@@ -348,7 +358,8 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
     }
   }
   __syncthreads();
-  const size_t crow = ((static_cast<size_t>(b) * p.num_kv_heads + kvh) * p.slots + nt.slot) * kD;
+  const size_t row = (static_cast<size_t>(b) * p.num_kv_heads + kvh) * p.slots + nt.slot;
+  const size_t crow = row * kD;  // elements (bytes of int8 codes) before the row
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int w = tid + j * NW * 64;
@@ -358,8 +369,8 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
     const int i0 = p.rope_half ? i : 2 * i;
     const int i1 = p.rope_half ? i + kHalf : 2 * i + 1;
     uint16_t o0 = r0[j], o1 = r1[j];
+    double x0 = 0.0, x1 = 0.0;  // the rotated pair in float64
     if (nt.app) {
-      double x0, x1;
       rope_rotate_pair(static_cast<double>(bf16_to_f32(r0[j])),
                        static_cast<double>(bf16_to_f32(r1[j])), nr.cs[i], nr.sn[i], &x0, &x1);
       o0 = f64_to_bf16_rne(x0);
@@ -375,6 +386,25 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
         nr.qs[h][i0] = f64_to_bf16_rne(x0);
         nr.qs[h][i1] = f64_to_bf16_rne(x1);
       }
+    } else if constexpr (I8) {  // the K and V rows, quantised, into the cache and LDS
+      double c0, c1, d0, d1;
+      const float ks = quantize_pair_row(x0, x1, true, &c0, &c1);
+      const float vs = quantize_pair_row(static_cast<double>(bf16_to_f32(w0[j])),
+                                         static_cast<double>(bf16_to_f32(w1[j])), true, &d0, &d1);
+      int8_t* kc = const_cast<int8_t*>(static_cast<const int8_t*>(p.k)) + crow;
+      int8_t* vc = const_cast<int8_t*>(static_cast<const int8_t*>(p.v)) + crow;
+      kc[i0] = static_cast<int8_t>(c0);
+      kc[i1] = static_cast<int8_t>(c1);
+      vc[i0] = static_cast<int8_t>(d0);
+      vc[i1] = static_cast<int8_t>(d1);
+      if (i == 0) {
+        const_cast<float*>(p.k_scale)[row] = ks;
+        const_cast<float*>(p.v_scale)[row] = vs;
+      }
+      nr.k[i0] = static_cast<float>(c0 * static_cast<double>(ks));
+      nr.k[i1] = static_cast<float>(c1 * static_cast<double>(ks));
+      nr.v[i0] = static_cast<float>(d0 * static_cast<double>(vs));
+      nr.v[i1] = static_cast<float>(d1 * static_cast<double>(vs));
     } else {  // the K row, rotated, into the cache and LDS
       uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k)) + crow;
       kc[i0] = o0;
@@ -383,7 +413,7 @@ __device__ void fused_step_prologue(const DecodeParams& p, NewRow<G>& nr, const 
       nr.k[i1] = bf16_to_f32(o1);
     }
   }
-  if (nt.mine && tid < kD / 8) {  // the V row
+  if (!I8 && nt.mine && tid < kD / 8) {  // the V row
     store16(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.v)) + crow + 8 * tid, vraw);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -417,7 +447,6 @@ template <int G, class Rows, int NW, bool FUSED = false, bool I8 = false, int NS
 __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16>& sm, int b, int kvh, int t0,
                              int t1, bool direct, size_t slot, NewRow<G>* nr = nullptr,
                              NewToken nt = NewToken{}) {
-  static_assert(!(FUSED && I8), "the fused step appends bf16 rows");
   using Sm = Smem<G, NW, NS_, I8 ? 8 : 16>;
   constexpr int NS = Sm::NS;
   constexpr int TILE = Sm::TILE;
@@ -446,7 +475,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
   // int8 tiles multiply in fp16: the query is scaled per head by the power
   // of two 2^k that brings its largest |element| into [2^14, 2^15), which is
   // exact (a bf16 value has 8 significant bits), and the scores by 2^-k.
-  if constexpr (FUSED) fused_step_prologue<G, NW>(p, *nr, nt, b, kvh, rows);
+  if constexpr (FUSED) fused_step_prologue<G, NW, I8>(p, *nr, nt, b, kvh, rows);
   Vec16 qop[kKSteps];
   float qinv = 1.f;
   {
@@ -665,7 +694,7 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
                                                       0, 0);
         }
       }
-      if constexpr (FUSED) {
+      if constexpr (FUSED && !I8) {  // (shifting: bf16 caches only)
         const int tu = ts + 16 * u;
         if (nt.shift && tu < p.sinks) {  // sink rows: the query at its cache position
           f32x4_t ds = {0.f, 0.f, 0.f, 0.f};
@@ -990,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
       nt.cpos = min(nt.pos, p.sinks + p.window - 1);
       nt.shift = p.shift_sinks && nt.cpos != nt.pos && t0 < p.sinks;
     }
-    attend_piece<G, RingRows, NW, true>(p, sm, b, kvh, t0, t1, ns == 1, slot, &nr, nt);
+    attend_piece<G, RingRows, NW, true, I8>(p, sm, b, kvh, t0, t1, ns == 1, slot, &nr, nt);
   } else {
     attend_piece<G, RingRows, NW, false, I8>(p, sm, b, kvh, t0, t1, ns == 1, slot);
   }
@@ -1420,11 +1449,14 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
   const unsigned grid =
       static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_kv_heads) * p.num_splits;
   // p.new_pos set: the fused step (append of one token per sequence + decode)
-  if (p.i8 && p.new_pos != nullptr) return hipErrorInvalidValue;  // fused step: bf16 only
-  hipError_t err = p.new_pos != nullptr
-                       ? decode_ring_kernel_launch<kRingWaves, true, false>(p, grid, stream)
-                       : (p.i8 ? decode_ring_kernel_launch<kRingWaves, false, true>(p, grid, stream)
-                               : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream));
+  const bool fused = p.new_pos != nullptr;
+  hipError_t err;
+  if (p.i8)
+    err = fused ? decode_ring_kernel_launch<kRingWaves, true, true>(p, grid, stream)
+                : decode_ring_kernel_launch<kRingWaves, false, true>(p, grid, stream);
+  else
+    err = fused ? decode_ring_kernel_launch<kRingWaves, true, false>(p, grid, stream)
+                : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream);
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);

@@ -63,6 +63,29 @@ __device__ __forceinline__ void rope_rotate_pair(double x0, double x1, double c,
   *o1 = fma(x0, s, x1 * c);
 }
 
+// int8 rows ([kvc] §5.1: INT8 cache).  A wave quantises one row of d values:
+// lane l < d/2 holds the row's elements e0 and e1 (a RoPE pair) as float64.
+//   a = max |x|,  s = float32(a / 127),  c = clamp(rint(x / s), -127, 127)
+// (s = 0 gives codes 0).  Every lane of the wave calls it; it returns s and
+// the lane's two codes (exact integers in float64).  Every kernel that
+// stores an int8 row takes its codes from here, so rows written by different
+// entry points are bit-identical.
+__device__ __forceinline__ float quantize_pair_row(double x0, double x1, bool active, double* c0,
+                                                   double* c1) {
+  double a = active ? fmax(fabs(x0), fabs(x1)) : 0.0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = fmax(a, __shfl_xor(a, o));
+  const float s = static_cast<float>(a / 127.0);
+  const double sd = static_cast<double>(s);
+  *c0 = 0.0;
+  *c1 = 0.0;
+  if (active && sd > 0.0) {
+    *c0 = fmin(fmax(rint(x0 / sd), -127.0), 127.0);
+    *c1 = fmin(fmax(rint(x1 / sd), -127.0), 127.0);
+  }
+  return s;
+}
+
 struct alignas(16) Vec16 {
   uint32_t w[4];
 };

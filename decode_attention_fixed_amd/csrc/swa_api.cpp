@@ -341,7 +341,7 @@ static swa_status step_ring(swa_cache* cache, const void* k_new, const void* v_n
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
     return fail(SWA_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (swa::use_mfma_path(p.bf16, p.head_dim)) {  // bf16: one launch (plus the split merge)
+  if (swa::use_mfma_path(p.bf16 || p.i8, p.head_dim)) {  // one launch (plus the split merge)
     p.k_new = k_new;
     p.v_new = v_new;
     p.new_pos = pos;

@@ -174,10 +174,11 @@ swa_status decode_attn_ring(const swa_cache* cache, const void* q, int32_t num_q
  * the same state bit for bit, and out / lse agree up to float32 rounding (the
  * new token's score is summed in another order).  A sequence with
  * pos[b] < 0 appends nothing and attends with q as given, as that pair of
- * calls does.  bf16 caches with d = 128 do both in the decode launch itself
- * (the workgroup whose rows hold the new token's slot writes the token and
- * takes it into its softmax from on-chip memory); other configurations run
- * the two steps as separate launches on `stream`.  The cache is updated by
+ * calls does.  bf16 and int8 caches with d = 128 do both in the decode
+ * launch itself (the workgroup whose rows hold the new token's slot writes
+ * the token, quantised as the int8 append quantises it, and takes it into
+ * its softmax from on-chip memory); other configurations run the two steps
+ * as separate launches on `stream`.  The cache is updated by
  * the same launch that reads it: do not read it concurrently. */
 swa_status decode_step_ring(swa_cache* cache, const void* k_new, const void* v_new,
                             const int32_t* pos, const void* q, int32_t num_q_heads, float scale,

@@ -57,6 +57,7 @@ def _same_ring(a, b, s):
     (dict(), True),                                   # one fused launch per step
     (dict(), False),                                  # append, then decode
     (dict(cache="i8"), False),                        # int8 rows
+    (dict(cache="i8"), True),                         # int8 rows, fused step
     (dict(positions="cache"), True),                  # cache position shifting
     (dict(dtype="f32", head_dim=64, num_q_heads=4, num_kv_heads=4, window=40), True),
 ])

@@ -110,6 +110,45 @@ def test_fused_step_equals_two_calls(kw):
         b.close()
 
 
+@pytest.mark.parametrize("kw", [
+    dict(),                                                                  # g=1, wraps
+    dict(num_q_heads=16, num_kv_heads=4, window=257, history="prefill:600", batch=3),  # g=4
+    dict(batch=1, num_q_heads=8, num_kv_heads=2, window=20000, sinks=4,
+         history="prefill:25000", decode_steps=4),                          # many splits + merge
+    dict(window=2, sinks=8, history="prefill:3", num_q_heads=8, num_kv_heads=2),    # S > W
+])
+def test_fused_step_equals_two_calls_i8(kw):
+    """int8 caches: the fused step quantises the new rows exactly as the int8
+    append does (codes and scales bit-identical).  Outputs: with g <= 2 both
+    paths weigh rows in float32 (1e-5 as above); with g >= 3 P*V runs on the
+    matrix core with fp16 weights (11 significant bits) while the fused step
+    adds the new token in float32 at the merge, so the two differ by up to
+    2^-11 of the new token's share of the output: 1e-3."""
+    w = _W(cache="i8", **kw)
+    tol = 1e-5 if w.num_q_heads // w.num_kv_heads <= 2 else 1e-3
+    a, b = _pair(w)
+    try:
+        for step in range(w.decode_steps):
+            inp = a.step_inputs(step)
+            q_before = inp["q"].clone()
+            _two_call_step(a, inp)
+            _fused_step(b, inp)
+            torch.cuda.synchronize()
+            assert torch.equal(inp["q"], q_before)
+            assert torch.equal(a.cache.slot_pos, b.cache.slot_pos), step
+            assert torch.equal(a.cache.k, b.cache.k), step
+            assert torch.equal(a.cache.v, b.cache.v), step
+            assert (a.out - b.out).abs().max().item() <= tol, step
+            fin = torch.isfinite(a.lse)
+            assert torch.equal(fin, torch.isfinite(b.lse)), step
+            if fin.any():
+                assert (a.lse[fin] - b.lse[fin]).abs().max().item() <= 1e-5, step
+        _log(f"i8 {kw}: {w.decode_steps} steps, cache bit-identical")
+    finally:
+        a.close()
+        b.close()
+
+
 def test_fused_step_negative_position():
     """A sequence whose position is negative appends nothing and attends with
     its query as given, in both paths."""
