@@ -178,3 +178,20 @@ def test_prefill_replays():
     finally:
         eager.close()
         graphed.close()
+
+
+def test_pos_advance_values():
+    """pos += delta on the device, clamped to the int32 range."""
+    from decode_attention_fixed_amd import binding as B
+    big = 2**31 - 1
+    vals = [0, -5, 7, big - 1, big, -(2**31), -(2**31) + 2]
+    pos = torch.tensor(vals, dtype=torch.int32, device="cuda")
+    B.pos_advance(pos, 3)
+    torch.cuda.synchronize()
+    want = [min(max(v + 3, -(2**31)), big) for v in vals]
+    assert pos.cpu().tolist() == want
+    B.pos_advance(pos, -10)
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == [min(max(v - 10, -(2**31)), big) for v in want]
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    B.pos_advance(empty, 1)  # nothing to do
