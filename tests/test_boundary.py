@@ -196,6 +196,22 @@ def test_decode_step_ring_validation():
         B.swa_cache_destroy(h)
 
 
+@pytest.mark.parametrize("kw", [dict(dtype="i8"), dict(dtype="f32"), dict(head_dim=64)])
+def test_shifted_step_needs_bf16_d128(kw):
+    """Cache position shifting is built for bf16 caches with head_dim 128;
+    other caches get SWA_ERR_UNSUPPORTED before anything is launched."""
+    h = _create(**kw)
+    try:
+        d = kw.get("head_dim", 128)
+        need = B.decode_attn_workspace_bytes(8, 32, 32, d, 4100)
+        rc = B.LIB.decode_step_ring_shifted(h, FAKE, FAKE, FAKE, FAKE, 32, 0.0, FAKE, B.SWA_F32,
+                                            None, FAKE, need, None)
+        assert rc == B.SWA_ERR_UNSUPPORTED, B.swa_last_error()
+        assert "shifting" in B.swa_last_error()
+    finally:
+        B.swa_cache_destroy(h)
+
+
 def test_prefill_validation():
     h = _create()
     L = B.LIB
