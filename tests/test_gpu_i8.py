@@ -112,6 +112,29 @@ def test_ring_i8(kw, fused):
         st.close()
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_ring_i8_half_pairs(fused):
+    """RoPE pairs (i, i + d/2) on an int8 ring: the append's and the fused
+    step's quantisation of the rotated K (rows checked against the oracle's),
+    and the outputs."""
+    from decode_attention_fixed_amd.workloads import RingState
+    w = _ring(seed=89, num_q_heads=16, num_kv_heads=4)
+    st = RingState(w, rope_style="half")
+    try:
+        st.prefill()
+        _check_ring_rows(st, w, "half")
+        for step in range(w.decode_steps):
+            st.step(st.step_inputs(step), fused=fused)
+            torch.cuda.synchronize()
+            out = st.out.cpu().numpy()
+            for b in range(w.batch):
+                want, _ = ring_expected(w, b, step, style="half")
+                assert float(np.abs(out[b] - want).max()) <= TOL, (step, b)
+        _check_ring_rows(st, w, "half")
+    finally:
+        st.close()
+
+
 def _pool_state(w):
     from decode_attention_fixed_amd.workloads import PagedState
     st = PagedState(w)
