@@ -161,13 +161,39 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const size_t head0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(kvh) * G;
   float* lse_out = p.ws_lse + head0 * p.num_splits + split;  // + g * num_splits
 
+  const int rl = lane / LPR;  // row within a load instruction
+  const int cl = lane % LPR;  // 16-byte column chunk within the row
+  // One split per sequence: this wave's result is final and goes straight
+  // to out / lse (what the merge of a single split would write), and the
+  // merge is not launched.
+  const bool direct = p.num_splits == 1;
+  auto write_out = [&](int g, int e0, const float* v) {  // v[0..3]: dims cl * EPL + e0 ..
+    const size_t at = (head0 + g) * D + cl * EPL + e0;
+    if (p.out_bf16) {
+      uint16_t* o = static_cast<uint16_t*>(p.out) + at;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(v[i]);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + at) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+  };
+
   if (t0 >= t1) {  // nothing of this sequence falls in the split
-    if (lane < G) lse_out[static_cast<size_t>(lane) * p.num_splits] = kNegInf;
+    if (direct) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      if (lane < LPR)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4) write_out(g, e, z);
+      if (lane < G && p.lse != nullptr) p.lse[head0 + lane] = kNegInf;
+    } else if (lane < G) {
+      lse_out[static_cast<size_t>(lane) * p.num_splits] = kNegInf;
+    }
     return;
   }
 
-  const int rl = lane / LPR;  // row within a load instruction
-  const int cl = lane % LPR;  // 16-byte column chunk within the row
   const float c = p.score_scale_log2;
 
   float q[G][EPL];
@@ -282,17 +308,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
       const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
       float* dst = p.ws_o + ((head0 + g) * p.num_splits + split) * D + cl * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(dst + e) =
-            make_float4(acc[g][e] * inv, acc[g][e + 1] * inv, acc[g][e + 2] * inv,
-                        acc[g][e + 3] * inv);
+      for (int e = 0; e < EPL; e += 4) {
+        const float v[4] = {acc[g][e] * inv, acc[g][e + 1] * inv, acc[g][e + 2] * inv,
+                            acc[g][e + 3] * inv};
+        if (direct)
+          write_out(g, e, v);
+        else
+          *reinterpret_cast<float4*>(dst + e) = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
-    if (lane == g)
-      lse_out[static_cast<size_t>(g) * p.num_splits] =
-          l[g] > 0.f ? m[g] * c + __log2f(l[g]) : kNegInf;
+    if (lane == g) {
+      const float lse2 = l[g] > 0.f ? m[g] * c + __log2f(l[g]) : kNegInf;
+      if (!direct)
+        lse_out[static_cast<size_t>(g) * p.num_splits] = lse2;
+      else if (p.lse != nullptr)
+        p.lse[head0 + g] = lse2 * kLn2;
+    }
 }
 
 // Combines the splits of one (sequence, query head):
@@ -375,7 +409,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   else
     err = p.head_dim == 64 ? launch_split<kF32, 64, Addr>(p, g, stream)
                            : launch_split<kF32, 128, Addr>(p, g, stream);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || p.num_splits == 1) return err;  // one split: written directly
   const unsigned grid = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
   if (p.head_dim == 64)
     merge_kernel<64><<<grid, 64, 0, stream>>>(p);
