@@ -3,10 +3,12 @@
 tests/capi/capi_check.c (built by __graft_entry__.build() with gcc against
 include/swa.h, the HIP runtime's C API and the in-tree libswa.so) allocates
 a ring cache with hipMalloc, appends a history with kv_append_rope, and runs
-fused decode steps with decode_step_ring.  Its inputs are the seeded
-synthetic rows, written to a file here; its outputs are checked against the
-float64 oracle with the usual bars (slot table exact, outputs within 2e-3,
-lse within 1e-3).
+fused decode steps with decode_step_ring; with --pool it fills a NaN-poisoned
+paged pool with kv_write_paged (K rotated on the way in) and runs
+decode_attn_paged over a block table with absent slots.  Its inputs are the
+seeded synthetic rows, written to a file here; its outputs are checked
+against the float64 oracle with the usual bars (slot table exact, outputs
+within 2e-3, lse within 1e-3).
 """
 
 import os
@@ -16,8 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.decode import ring_expected, ring_slot_table
-from synth import TENSOR_K, TENSOR_Q, TENSOR_V, RingWorkload
+from oracle.decode import pool_expected, ring_expected, ring_slot_table
+from synth import TENSOR_K, TENSOR_Q, TENSOR_V, PoolWorkload, RingWorkload
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +93,59 @@ def test_capi_ring_steps(tmp_path, kw):
     for b in range(B):
         assert np.array_equal(sp[b], ring_slot_table(w, b, n - 1)), b
     print(style, res.stdout.strip(), flush=True)
+
+
+@pytest.mark.parametrize("seed,rope_half", [(61, 0), (69, 1)])
+def test_capi_pool_steps(tmp_path, seed, rope_half):
+    assert os.path.exists(BIN), f"{BIN} is not built: run __graft_entry__.build()"
+    w = PoolWorkload(name="capi-pool", seed=seed, batch=3, num_q_heads=6, num_kv_heads=2,
+                     head_dim=128, dtype="bf16", block_size=32, logical_blocks=48,
+                     pool_slots=16, rope_base=10000.0, scale=0.5, decode_steps=3)
+    B, hq, hkv, d, n, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                            w.decode_steps, w.block_size)
+    valid = w.block_valid
+    assert valid.min() == 0  # some slots absent: their poisoned rows must stay unread
+    ks, vs, rows, pos = [], [], [], []
+    for b in range(B):  # every resident block of b, rows named from its table entry
+        slots = np.nonzero(w.slot_blocks[b] >= 0)[0]
+        p = (w.slot_blocks[b][slots][:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+        r = (w.block_table[b][slots].astype(np.int64)[:, None] * bs
+             + np.arange(bs)[None, :]).reshape(-1)
+        ks.append(w.rows(TENSOR_K, b, p))
+        vs.append(w.rows(TENSOR_V, b, p))
+        rows.append(r)
+        pos.append(p)
+    ks, vs = np.concatenate(ks), np.concatenate(vs)
+    rows, pos = np.concatenate(rows), np.concatenate(pos)
+    q = np.stack([np.stack([w.query(b, s) for b in range(B)]) for s in range(n)])
+    lens = np.full(B, w.pool_slots * bs, dtype=np.int32)
+
+    inp = tmp_path / "in.bin"
+    out = tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        f.write(np.array([B, hq, hkv, d, bs, w.pool_slots, B * w.pool_slots, len(rows), n,
+                          rope_half], dtype=np.int32).tobytes())
+        f.write(np.array([w.rope_base], dtype=np.float32).tobytes())
+        f.write(_bf16_bytes(ks))
+        f.write(_bf16_bytes(vs))
+        f.write(rows.astype(np.int32).tobytes())
+        f.write(pos.astype(np.int32).tobytes())
+        f.write(np.ascontiguousarray(w.block_table, dtype=np.int32).tobytes())
+        f.write(lens.tobytes())
+        f.write(np.ascontiguousarray(valid, dtype=np.uint8).tobytes())
+        f.write(_bf16_bytes(q))
+    print(f"capi_check --pool seed={seed} rope_half={rope_half}", flush=True)
+    res = subprocess.run([BIN, "--pool", str(inp), str(out)], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+
+    raw = np.fromfile(out, dtype=np.float32)
+    got = raw[:n * B * hq * d].reshape(n, B, hq, d)
+    lse = raw[n * B * hq * d:].reshape(n, B, hq)
+    style = "half" if rope_half else "interleaved"
+    for s in range(n):
+        for b in range(B):
+            want, want_lse = pool_expected(w, b, s, style=style)
+            assert float(np.abs(got[s, b] - want).max()) <= 2e-3, (s, b)
+            assert float(np.abs(lse[s, b] - want_lse).max()) <= 1e-3, (s, b)
+    print(res.stdout.strip(), flush=True)
