@@ -16,7 +16,8 @@
  * int32 slot_pos [B, S + W] after the last step.
  *
  * Pool input: int32 B, Hq, Hkv, d, block_size, max_blocks, num_phys, n_rows,
- * n_steps, rope_half; float32 rope_base; then bf16 k_src, v_src
+ * n_steps, rope_half, i8 (1: an SWA_I8 pool, quantised by the write; the
+ * rows and queries stay bf16); float32 rope_base; then bf16 k_src, v_src
  * [n_rows, Hkv, d] (K not rotated); int32 dst_rows [n_rows], pos [n_rows];
  * int32 block_table [B, max_blocks], seq_lens [B]; uint8 block_valid
  * [B, max_blocks]; bf16 q [n_steps, B, Hq, d] (already rotated).  Pool rows
@@ -168,12 +169,12 @@ static int run_ring(const char* in_path, const char* out_path) {
 static int run_pool(const char* in_path, const char* out_path) {
   FILE* in = fopen(in_path, "rb");
   if (in == NULL) return 2;
-  int32_t hdr[10];
+  int32_t hdr[11];
   float rope_base;
-  if (fread(hdr, sizeof(int32_t), 10, in) != 10 || fread(&rope_base, 4, 1, in) != 1) return 2;
+  if (fread(hdr, sizeof(int32_t), 11, in) != 11 || fread(&rope_base, 4, 1, in) != 1) return 2;
   const int32_t B = hdr[0], Hq = hdr[1], Hkv = hdr[2], d = hdr[3], bs = hdr[4];
   const int32_t max_blocks = hdr[5], num_phys = hdr[6], n_rows = hdr[7], n_steps = hdr[8];
-  const int32_t rope_half = hdr[9];
+  const int32_t rope_half = hdr[9], i8 = hdr[10];
   const size_t src_bytes = (size_t)n_rows * Hkv * d * 2;
   const size_t q_step = (size_t)B * Hq * d * 2;
   const size_t table_n = (size_t)B * max_blocks;
@@ -188,7 +189,7 @@ static int run_pool(const char* in_path, const char* out_path) {
   fclose(in);
   if (!ks || !vs || !rows || !pos || !table || !lens || !valid || !q) return 2;
 
-  swa_paged_desc desc = {B, Hq, Hkv, d, bs, max_blocks, num_phys, SWA_BF16};
+  swa_paged_desc desc = {B, Hq, Hkv, d, bs, max_blocks, num_phys, i8 ? SWA_I8 : SWA_BF16};
   size_t pool_bytes = 0, ws_bytes = 0;
   SWA(swa_pool_required_bytes(&desc, &pool_bytes));
   SWA(decode_attn_workspace_bytes(B, Hq, Hkv, d, max_blocks * bs, &ws_bytes));
@@ -198,7 +199,7 @@ static int run_pool(const char* in_path, const char* out_path) {
   HIP(hipMalloc(&ws, ws_bytes));
   HIP(hipMalloc(&out, (size_t)B * Hq * d * 4));
   HIP(hipMalloc(&lse, (size_t)B * Hq * 4));
-  HIP(hipMemset(k_pool, 0xFF, pool_bytes));  /* bf16 NaN in every unwritten row */
+  HIP(hipMemset(k_pool, 0xFF, pool_bytes));  /* bf16 NaN (int8: NaN scales) when unwritten */
   HIP(hipMemset(v_pool, 0xFF, pool_bytes));
   int err = 0;
   void* d_ks = to_device(ks, src_bytes, &err);

@@ -4,7 +4,8 @@ tests/capi/capi_check.c (built by __graft_entry__.build() with gcc against
 include/swa.h, the HIP runtime's C API and the in-tree libswa.so) allocates
 a ring cache with hipMalloc, appends a history with kv_append_rope, and runs
 fused decode steps with decode_step_ring; with --pool it fills a NaN-poisoned
-paged pool with kv_write_paged (K rotated on the way in) and runs
+paged pool (bf16, or int8 codes quantised by the write) with kv_write_paged
+(K rotated on the way in) and runs
 decode_attn_paged over a block table with absent slots.  Its inputs are the
 seeded synthetic rows, written to a file here; its outputs are checked
 against the float64 oracle with the usual bars (slot table exact, outputs
@@ -95,12 +96,12 @@ def test_capi_ring_steps(tmp_path, kw):
     print(style, res.stdout.strip(), flush=True)
 
 
-@pytest.mark.parametrize("seed,rope_half", [(61, 0), (69, 1)])
-def test_capi_pool_steps(tmp_path, seed, rope_half):
+@pytest.mark.parametrize("seed,rope_half,cache", [(61, 0, ""), (69, 1, ""), (66, 0, "i8")])
+def test_capi_pool_steps(tmp_path, seed, rope_half, cache):
     assert os.path.exists(BIN), f"{BIN} is not built: run __graft_entry__.build()"
     w = PoolWorkload(name="capi-pool", seed=seed, batch=3, num_q_heads=6, num_kv_heads=2,
                      head_dim=128, dtype="bf16", block_size=32, logical_blocks=48,
-                     pool_slots=16, rope_base=10000.0, scale=0.5, decode_steps=3)
+                     pool_slots=16, rope_base=10000.0, scale=0.5, decode_steps=3, cache=cache)
     B, hq, hkv, d, n, bs = (w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                             w.decode_steps, w.block_size)
     valid = w.block_valid
@@ -124,7 +125,7 @@ def test_capi_pool_steps(tmp_path, seed, rope_half):
     out = tmp_path / "out.bin"
     with open(inp, "wb") as f:
         f.write(np.array([B, hq, hkv, d, bs, w.pool_slots, B * w.pool_slots, len(rows), n,
-                          rope_half], dtype=np.int32).tobytes())
+                          rope_half, int(cache == "i8")], dtype=np.int32).tobytes())
         f.write(np.array([w.rope_base], dtype=np.float32).tobytes())
         f.write(_bf16_bytes(ks))
         f.write(_bf16_bytes(vs))
@@ -134,7 +135,7 @@ def test_capi_pool_steps(tmp_path, seed, rope_half):
         f.write(lens.tobytes())
         f.write(np.ascontiguousarray(valid, dtype=np.uint8).tobytes())
         f.write(_bf16_bytes(q))
-    print(f"capi_check --pool seed={seed} rope_half={rope_half}", flush=True)
+    print(f"capi_check --pool seed={seed} rope_half={rope_half} cache={cache!r}", flush=True)
     res = subprocess.run([BIN, "--pool", str(inp), str(out)], capture_output=True, text=True,
                          timeout=120)
     assert res.returncode == 0, res.stderr
