@@ -159,6 +159,56 @@ def _ptr(t: torch.Tensor | None, name: str, dtype=None) -> int | None:
     return t.data_ptr()
 
 
+# The C ABI takes bare pointers and cannot see a tensor's extent, so the
+# binding checks every tensor against the sizes the call will touch before
+# handing its pointer over; a mismatch raises ValueError and nothing runs.
+
+def _expect(t: torch.Tensor | None, name: str, shape: tuple, dtypes) -> None:
+    """t (if given) has exactly `shape` and one of `dtypes`."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {list(dtypes)}, got {t.dtype}")
+
+
+def _expect_numel(t: torch.Tensor | None, name: str, numel: int, dtype) -> None:
+    """t (if given) holds at least `numel` elements of `dtype` (flat views)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, got {t.numel()}")
+
+
+def _expect_bytes(t: torch.Tensor | None, name: str, nbytes: int) -> None:
+    if t is None:
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} must hold at least {nbytes} bytes, got {have}")
+
+
+_OUT_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _row_dtype(code: int):
+    """torch dtype of the rows and queries handed to a call on a cache or
+    pool of element type `code` (int8 caches take bf16 rows)."""
+    return torch.float32 if code == SWA_F32 else torch.bfloat16
+
+
+# ring-cache handle -> its config, recorded by swa_cache_create so that the
+# calls on the handle can check their tensors' shapes
+_RING_CFG: dict = {}
+
+
+def _ring_cfg(handle: int):
+    return _RING_CFG.get(handle)
+
+
 # ---------------------------------------------------------------------------
 # ring cache
 # ---------------------------------------------------------------------------
@@ -181,10 +231,17 @@ def swa_cache_create(cfg: SwaCacheConfig, k_cache: torch.Tensor, v_cache: torch.
                      slot_pos: torch.Tensor) -> int:
     handle = _vp()
     dt = _BUFFER_DTYPE[cfg.dtype]
+    kv_bytes, sp_bytes = swa_cache_required_bytes(cfg)
+    _expect_bytes(k_cache, "k_cache", kv_bytes)
+    _expect_bytes(v_cache, "v_cache", kv_bytes)
+    _expect_bytes(slot_pos, "slot_pos", sp_bytes)
     _check("swa_cache_create",
            LIB.swa_cache_create(ctypes.byref(cfg), _ptr(k_cache, "k_cache", dt),
                                 _ptr(v_cache, "v_cache", dt), _ptr(slot_pos, "slot_pos", torch.int32),
                                 ctypes.byref(handle)))
+    _RING_CFG[handle.value] = SwaCacheConfig(cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.window,
+                                             cfg.num_sinks, cfg.dtype, cfg.rope_base,
+                                             cfg.rope_style)
     return handle.value
 
 
@@ -193,6 +250,7 @@ def swa_cache_reset(handle: int, stream=None) -> None:
 
 
 def swa_cache_destroy(handle: int | None) -> None:
+    _RING_CFG.pop(handle, None)
     LIB.swa_cache_destroy(handle)
 
 
@@ -202,6 +260,13 @@ def kv_append_rope(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: t
     q_inout [B, T, Hq, d] or None, rotated in place."""
     n_tokens = k_new.shape[1]
     hq = q_inout.shape[2] if q_inout is not None else 0
+    cfg = _ring_cfg(handle)
+    if cfg is not None:
+        rt = (_row_dtype(cfg.dtype),)
+        _expect(k_new, "k_new", (cfg.batch, n_tokens, cfg.num_kv_heads, cfg.head_dim), rt)
+        _expect(v_new, "v_new", (cfg.batch, n_tokens, cfg.num_kv_heads, cfg.head_dim), rt)
+        _expect(pos, "pos", (cfg.batch,), (torch.int32,))
+        _expect(q_inout, "q_inout", (cfg.batch, n_tokens, hq, cfg.head_dim), rt)
     _check("kv_append_rope",
            LIB.kv_append_rope(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                               _ptr(pos, "pos", torch.int32), n_tokens, _ptr(q_inout, "q_inout"),
@@ -224,10 +289,26 @@ def new_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _check_ring_decode(handle: int, q: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor | None, k_new=None, v_new=None, pos=None) -> None:
+    cfg = _ring_cfg(handle)
+    if cfg is None:
+        return
+    hq = q.shape[1] if q.dim() == 3 else -1
+    rt = (_row_dtype(cfg.dtype),)
+    _expect(q, "q", (cfg.batch, hq, cfg.head_dim), rt)
+    _expect(out, "out", (cfg.batch, hq, cfg.head_dim), _OUT_DTYPES)
+    _expect(lse, "lse", (cfg.batch, hq), (torch.float32,))
+    _expect(k_new, "k_new", (cfg.batch, cfg.num_kv_heads, cfg.head_dim), rt)
+    _expect(v_new, "v_new", (cfg.batch, cfg.num_kv_heads, cfg.head_dim), rt)
+    _expect(pos, "pos", (cfg.batch,), (torch.int32,))
+
+
 def decode_attn_ring(handle: int, q: torch.Tensor, out: torch.Tensor,
                      workspace: torch.Tensor, lse: torch.Tensor | None = None,
                      scale: float = 0.0, stream=None) -> None:
     """q [B, Hq, d] (rotated); out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
+    _check_ring_decode(handle, q, out, lse)
     _check("decode_attn_ring",
            LIB.decode_attn_ring(handle, _ptr(q, "q"), q.shape[1], scale, _ptr(out, "out"),
                                 _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
@@ -241,6 +322,7 @@ def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos:
     """Append of one token per sequence + decode in one call.  k_new, v_new
     [B, Hkv, d]; pos [B] int32; q [B, Hq, d] NOT rotated (left unchanged);
     out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
+    _check_ring_decode(handle, q, out, lse, k_new, v_new, pos)
     _check("decode_step_ring",
            LIB.decode_step_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                                 _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1], scale,
@@ -263,6 +345,7 @@ def decode_step_ring_shifted(handle: int, k_new: torch.Tensor, v_new: torch.Tens
                              scale: float = 0.0, stream=None) -> None:
     """decode_step_ring with positions taken inside the cache (sinks scored
     against the query rotated at its cache position)."""
+    _check_ring_decode(handle, q, out, lse, k_new, v_new, pos)
     _check("decode_step_ring_shifted",
            LIB.decode_step_ring_shifted(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                                         _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1],
@@ -294,6 +377,17 @@ def prefill_attn_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos
     """Chunked prefill: k_new, v_new [B, T, Hkv, d]; pos [B] int32 (position of
     token 0); q [B, T, Hq, d] NOT rotated (left unchanged); out [B, T, Hq, d]
     float32 or bf16; lse [B, T, Hq] float32 or None."""
+    cfg = _ring_cfg(handle)
+    if cfg is not None:
+        T = k_new.shape[1] if k_new.dim() == 4 else -1
+        hq = q.shape[2] if q.dim() == 4 else -1
+        rt = (_row_dtype(cfg.dtype),)
+        _expect(k_new, "k_new", (cfg.batch, T, cfg.num_kv_heads, cfg.head_dim), rt)
+        _expect(v_new, "v_new", (cfg.batch, T, cfg.num_kv_heads, cfg.head_dim), rt)
+        _expect(pos, "pos", (cfg.batch,), (torch.int32,))
+        _expect(q, "q", (cfg.batch, T, hq, cfg.head_dim), rt)
+        _expect(out, "out", (cfg.batch, T, hq, cfg.head_dim), _OUT_DTYPES)
+        _expect(lse, "lse", (cfg.batch, T, hq), (torch.float32,))
     _check("prefill_attn_ring",
            LIB.prefill_attn_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
                                  _ptr(pos, "pos", torch.int32), k_new.shape[1], _ptr(q, "q"),
@@ -331,11 +425,26 @@ def new_pool(desc: SwaPagedDesc, device="cuda") -> tuple:
     return torch.empty(shape, dtype=dt, device=device), torch.empty(shape, dtype=dt, device=device)
 
 
+def _check_paged_decode(desc: SwaPagedDesc, q, k_pool, v_pool, block_table, seq_lens,
+                        block_valid, out, lse) -> None:
+    B_, hq, d = desc.batch, desc.num_q_heads, desc.head_dim
+    _expect(q, "q", (B_, hq, d), (_row_dtype(desc.dtype),))
+    _expect(out, "out", (B_, hq, d), _OUT_DTYPES)
+    _expect(lse, "lse", (B_, hq), (torch.float32,))
+    pool_bytes = swa_pool_required_bytes(desc)
+    _expect_bytes(k_pool, "k_pool", pool_bytes)
+    _expect_bytes(v_pool, "v_pool", pool_bytes)
+    _expect_numel(block_table, "block_table", B_ * desc.max_blocks_per_seq, torch.int32)
+    _expect_numel(seq_lens, "seq_lens", B_, torch.int32)
+    _expect_numel(block_valid, "block_valid", B_ * desc.max_blocks_per_seq, torch.uint8)
+
+
 def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
                       v_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                       block_valid: torch.Tensor | None, out: torch.Tensor,
                       workspace: torch.Tensor, lse: torch.Tensor | None = None,
                       scale: float = 0.0, stream=None) -> None:
+    _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
     _check("decode_attn_paged",
            LIB.decode_attn_paged(ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"),
                                  _ptr(v_pool, "v_pool"),
@@ -355,6 +464,7 @@ def prepare_decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch
     """decode_attn_paged's arguments marshalled once (stream included);
     returns a function of no arguments that makes the call, for a loop that
     repeats one call on the same buffers."""
+    _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
     args = (ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
             _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
             _ptr(block_valid, "block_valid", torch.uint8), scale, _ptr(out, "out"),
@@ -376,6 +486,15 @@ def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tenso
                    pos: torch.Tensor | None = None, rope_base: float = 10000.0,
                    rope_style: str = "interleaved", stream=None) -> None:
     """k_src, v_src [N, Hkv, d]; dst_rows [N] int32 physical token rows; pos [N] int32 or None."""
+    n = k_src.shape[0]
+    rt = (_row_dtype(desc.dtype),)
+    _expect(k_src, "k_src", (n, desc.num_kv_heads, desc.head_dim), rt)
+    _expect(v_src, "v_src", (n, desc.num_kv_heads, desc.head_dim), rt)
+    _expect(dst_rows, "dst_rows", (n,), (torch.int32,))
+    _expect(pos, "pos", (n,), (torch.int32,))
+    pool_bytes = swa_pool_required_bytes(desc)
+    _expect_bytes(k_pool, "k_pool", pool_bytes)
+    _expect_bytes(v_pool, "v_pool", pool_bytes)
     _check("kv_write_paged",
            LIB.kv_write_paged(ctypes.byref(desc), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
                               _ptr(k_src, "k_src"), _ptr(v_src, "v_src"),
@@ -450,6 +569,16 @@ def kv_append_paged(handle: int, desc: SwaPagedDesc, k_pool: torch.Tensor, v_poo
     else:
         n = len(seqs)
         arr = (_i32 * max(1, n))(*[int(x) for x in seqs])
+    T = k_new.shape[1] if k_new.dim() == 4 else -1
+    rt = (_row_dtype(desc.dtype),)
+    _expect(k_new, "k_new", (n, T, desc.num_kv_heads, desc.head_dim), rt)
+    _expect(v_new, "v_new", (n, T, desc.num_kv_heads, desc.head_dim), rt)
+    if desc.dtype != SWA_I8:  # (int8 pools are refused by the library itself)
+        pool_bytes = swa_pool_required_bytes(desc)
+        _expect_bytes(k_pool, "k_pool", pool_bytes)
+        _expect_bytes(v_pool, "v_pool", pool_bytes)
+    _expect_numel(block_table, "block_table", desc.batch * desc.max_blocks_per_seq, torch.int32)
+    _expect_numel(seq_lens, "seq_lens", desc.batch, torch.int32)
     _check("kv_append_paged",
            LIB.kv_append_paged(handle, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
                                _ptr(v_pool, "v_pool"),
@@ -484,6 +613,16 @@ def swa_pager_create(cfg: SwaPagerConfig, host_k: torch.Tensor, host_v: torch.Te
     [Nphys, Hkv, bs, d]; slot_phys: [B, C] int32 host array (copied);
     block_table [B, C] int32 and block_valid [B, C] uint8 on the device."""
     flat = [int(x) for row in slot_phys for x in row]
+    B_, C = cfg.batch, cfg.slots_per_seq
+    if len(flat) != B_ * C:
+        raise ValueError(f"slot_phys must hold {B_} x {C} entries, got {len(flat)}")
+    blk = cfg.num_kv_heads * cfg.block_size * cfg.head_dim * (4 if cfg.dtype == SWA_F32 else 2)
+    _expect_bytes(host_k, "host_k", B_ * cfg.logical_blocks * blk)
+    _expect_bytes(host_v, "host_v", B_ * cfg.logical_blocks * blk)
+    _expect_bytes(k_pool, "k_pool", cfg.num_phys_blocks * blk)
+    _expect_bytes(v_pool, "v_pool", cfg.num_phys_blocks * blk)
+    _expect_numel(block_table, "block_table", B_ * C, torch.int32)
+    _expect_numel(block_valid, "block_valid", B_ * C, torch.uint8)
     sp = (_i32 * len(flat))(*flat)
     handle = _vp()
     _check("swa_pager_create",

@@ -106,7 +106,8 @@ swa_status check_decode_common(const void* q, void* out, swa_dtype out_dtype, fl
                                void* workspace, size_t workspace_bytes, size_t need) {
   if (q == nullptr) return fail(SWA_ERR_INVALID_ARG, "q is NULL");
   if (out == nullptr) return fail(SWA_ERR_INVALID_ARG, "out is NULL");
-  if (!out_dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!out_dtype_valid(out_dtype))
+    return fail(SWA_ERR_INVALID_ARG, "out_dtype %d is not SWA_F32 or SWA_BF16", out_dtype);
   if (!aligned(q, 16) || !aligned(out, 16))
     return fail(SWA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(SWA_ERR_INVALID_ARG, "lse misaligned");
@@ -442,7 +443,9 @@ swa_status prefill_attn_ring(swa_cache* cache, const void* k_new, const void* v_
       static_cast<int64_t>(n_tokens) * cfg.num_kv_heads * cfg.head_dim * 2 > INT32_MAX)
     return fail(SWA_ERR_UNSUPPORTED, "prefill needs (S + W) * d * 2 and n_tokens * Hkv * d * 2 "
                                      "below 2^31 bytes");
-  if (!dtype_valid(out_dtype)) return fail(SWA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  // out holds float32 or bf16 rows only: an int8 code is not an output type
+  if (!out_dtype_valid(out_dtype))
+    return fail(SWA_ERR_INVALID_ARG, "out_dtype %d is not SWA_F32 or SWA_BF16", out_dtype);
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q, 16) || !aligned(out, 16) ||
       !aligned(pos, 4) || (lse != nullptr && !aligned(lse, 4)))
     return fail(SWA_ERR_INVALID_ARG, "k_new / v_new / q / out must be 16-byte aligned");

@@ -33,6 +33,10 @@
  *     not visible to the host: kernels skip out-of-range entries instead of
  *     reading or writing out of bounds (documented per entry point).
  *   - Device pointers to K/V/Q/output rows must be 16-byte aligned.
+ *   - Entry points that compute cite the page passage that defines what they
+ *     compute.  Calls marked "library helper" (sizing, reset, destroy, state
+ *     copies, error text) are bookkeeping of this library that no page
+ *     defines.
  */
 #ifndef SWA_H_
 #define SWA_H_
@@ -100,10 +104,12 @@ swa_status swa_cache_required_bytes(const swa_cache_config* cfg, size_t* kv_byte
 swa_status swa_cache_create(const swa_cache_config* cfg, void* k_cache, void* v_cache,
                             int32_t* slot_pos, swa_cache** out);
 
-/* Marks every slot empty (slot_pos := -1) with a fill kernel on `stream`. */
+/* Library helper (no page defines it): marks every slot empty
+ * (slot_pos := -1) with a fill kernel on `stream`. */
 swa_status swa_cache_reset(swa_cache* cache, void* stream);
 
-/* Frees the host descriptor (not the device buffers).  NULL is a no-op. */
+/* Library helper (no page defines it): frees the host descriptor (not the
+ * device buffers).  NULL is a no-op. */
 void swa_cache_destroy(swa_cache* cache);
 
 /* Appends n_tokens consecutive tokens per sequence ([ring] §3.3 and §5.1:
@@ -126,7 +132,8 @@ swa_status kv_append_rope(swa_cache* cache, const void* k_new, const void* v_new
                           const int32_t* pos, int32_t n_tokens, void* q_inout,
                           int32_t num_q_heads, void* stream);
 
-/* Workspace (device bytes) that decode_attn_ring / decode_step_ring /
+/* Library helper (no page defines it; the pages' decode keeps no scratch).
+ * Workspace (device bytes) that decode_attn_ring / decode_step_ring /
  * decode_attn_paged need for
  * these sizes; max_kv_tokens = S + W for a ring cache, max_blocks_per_seq *
  * block_size for a paged pool.  0 bytes is never returned.
@@ -202,7 +209,7 @@ swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const v
                                     float scale, void* out, swa_dtype out_dtype, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* pos[i] += delta for i < n, on `stream` (one small kernel; results clamped
+/* Library helper (no page defines it): pos[i] += delta for i < n, on `stream` (one small kernel; results clamped
  * to the int32 range).  Positions live in device memory, so a HIP graph that
  * captures decode steps followed by this call replays with each step at the
  * next position; every decode and append entry point above only launches
@@ -211,8 +218,9 @@ swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const v
  * nothing). */
 swa_status swa_pos_advance(int32_t* pos, int32_t n, int32_t delta, void* stream);
 
-/* Workspace (device bytes) of a prefill_attn_ring call with n_tokens tokens
- * per sequence.  Needs no initialisation. */
+/* Library helper (no page defines it): workspace (device bytes) of a
+ * prefill_attn_ring call with n_tokens tokens per sequence.  Needs no
+ * initialisation. */
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t n_tokens, size_t* bytes);
 
@@ -331,14 +339,17 @@ typedef struct swa_blocks swa_blocks;
 swa_status swa_blocks_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
                              int32_t max_blocks_per_seq, swa_blocks** out);
 
-/* Frees the host object.  NULL is a no-op. */
+/* Library helper (no page defines it): frees the host object.  NULL is a
+ * no-op. */
 void swa_blocks_destroy(swa_blocks* mgr);
 
-/* Every block free, every sequence empty (host state only; follow with
+/* Library helper (no page defines it): every block free, every sequence
+ * empty (host state only; follow with
  * swa_blocks_sync before the device mirrors are read). */
 swa_status swa_blocks_reset(swa_blocks* mgr);
 
-/* Writes the whole host state into the device mirrors the paged decode reads:
+/* Library helper (no page defines it): writes the whole host state into
+ * the device mirrors the paged decode reads:
  *   block_table  [max_seqs, max_blocks_per_seq] int32 (-1 = no block),
  *   seq_lens     [max_seqs] int32.
  * Returns when `stream` has done it (a set-up call). */
@@ -356,7 +367,8 @@ swa_status swa_blocks_share_prefix(swa_blocks* mgr, int32_t src, int32_t dst, in
  * (device mirror updated on `stream`). */
 swa_status swa_blocks_free(swa_blocks* mgr, int32_t seq, int32_t* seq_lens, void* stream);
 
-/* Host copies of the state; each output may be NULL:
+/* Library helper (no page defines it): host copies of the state; each
+ * output may be NULL:
  *   table [max_seqs * max_blocks_per_seq], lens [max_seqs],
  *   refs [num_blocks] reference counts, *free_blocks = free blocks. */
 swa_status swa_blocks_state(const swa_blocks* mgr, int32_t* table, int32_t* lens, int32_t* refs,
@@ -436,7 +448,7 @@ swa_status swa_pager_create(const swa_pager_config* cfg, const void* host_k, con
                             void* k_pool, void* v_pool, const int32_t* slot_phys,
                             int32_t* block_table, uint8_t* block_valid, swa_pager** out);
 
-/* Every slot empty: block_table := slot_phys, block_valid := 0, no block
+/* Library helper (no page defines it): every slot empty: block_table := slot_phys, block_valid := 0, no block
  * resident, LRU history cleared.  Waits for copies in flight and returns when
  * the stream has done it (a set-up call). */
 swa_status swa_pager_reset(swa_pager* pager, void* stream);
@@ -476,19 +488,21 @@ swa_status swa_pager_advance(swa_pager* pager, const int32_t* req_offsets,
                              const int32_t* req_blocks, void* stream, void* copy_stream,
                              int32_t* n_loaded);
 
-/* Makes the copies of the last advance visible to work enqueued on `stream`
+/* Library helper (no page defines it): makes the copies of the last advance visible to work enqueued on `stream`
  * after this call (it waits for them on the device, not on the host). */
 swa_status swa_pager_commit(swa_pager* pager, void* stream);
 
-/* Logical block held by each slot of sequence seq (-1 = empty), as the host
+/* Library helper (no page defines it): logical block held by each slot of sequence seq (-1 = empty), as the host
  * state stands (copies in flight included): out [C] int32, host. */
 swa_status swa_pager_slot_blocks(const swa_pager* pager, int32_t seq, int32_t* out);
 
-/* Frees the host object and its events (not the caller's memory).  Does not
+/* Library helper (no page defines it): frees the host object and its events (not the caller's memory).  Does not
  * wait for copies in flight.  NULL is a no-op. */
 void swa_pager_destroy(swa_pager* pager);
 
-/* Text of the last failure on the calling thread ("" if none). */
+/* Library helper (no page defines it): text of the last failure on the
+ * calling thread ("" if none).  The pointer stays valid until the thread's
+ * next call into the library. */
 const char* swa_last_error(void);
 
 #ifdef __cplusplus

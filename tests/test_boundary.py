@@ -373,3 +373,100 @@ def test_pager_null_handle():
     assert L.swa_pager_commit(None, None) == B.SWA_ERR_INVALID_ARG
     assert L.swa_pager_slot_blocks(None, 0, FAKE) == B.SWA_ERR_INVALID_ARG
     L.swa_pager_destroy(None)
+
+
+def test_int8_is_not_an_output_dtype():
+    """SWA_I8 names a cache element type, never an output type: every entry
+    point that writes `out` refuses it before anything is launched (an int8
+    out buffer would be a quarter of the float32 rows written into it)."""
+    L = B.LIB
+    h = _create()
+    need = B.decode_attn_workspace_bytes(8, 32, 32, 128, 4100)
+    pneed = B.prefill_attn_workspace_bytes(8, 32, 32, 128, 64)
+    try:
+        rcs = {
+            "decode_attn_ring": L.decode_attn_ring(h, FAKE, 32, 0.0, FAKE, B.SWA_I8, None, FAKE,
+                                                   need, None),
+            "decode_step_ring": L.decode_step_ring(h, FAKE, FAKE, FAKE, FAKE, 32, 0.0, FAKE,
+                                                   B.SWA_I8, None, FAKE, need, None),
+            "decode_step_ring_shifted": L.decode_step_ring_shifted(h, FAKE, FAKE, FAKE, FAKE, 32,
+                                                                   0.0, FAKE, B.SWA_I8, None,
+                                                                   FAKE, need, None),
+            "prefill_attn_ring": L.prefill_attn_ring(h, FAKE, FAKE, FAKE, 64, FAKE, 32, 0.0, FAKE,
+                                                     B.SWA_I8, None, FAKE, pneed, None),
+        }
+    finally:
+        B.swa_cache_destroy(h)
+    d = _desc()
+    pw = B.decode_attn_workspace_bytes(32, 32, 8, 128, 2048 * 16)
+    rcs["decode_attn_paged"] = L.decode_attn_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                   None, 0.0, FAKE, B.SWA_I8, None, FAKE, pw,
+                                                   None)
+    for name, rc in rcs.items():
+        assert rc == B.SWA_ERR_INVALID_ARG, name
+    assert "out_dtype" in B.swa_last_error()
+
+
+def test_binding_checks_shapes_before_the_call():
+    """The binding compares every tensor with the sizes the call will touch
+    and raises ValueError on a mismatch; no pointer reaches the library."""
+    import torch
+    d = B.make_paged_desc(2, 8, 2, 128, 16, 10, 20, "bf16")
+    pool_shape = (20, 2, 16, 128)
+    ok = dict(q=torch.zeros(2, 8, 128, dtype=torch.bfloat16),
+              k_pool=torch.zeros(pool_shape, dtype=torch.bfloat16),
+              v_pool=torch.zeros(pool_shape, dtype=torch.bfloat16),
+              block_table=torch.zeros(2, 10, dtype=torch.int32),
+              seq_lens=torch.zeros(2, dtype=torch.int32), block_valid=None,
+              out=torch.zeros(2, 8, 128), workspace=torch.zeros(16, dtype=torch.uint8))
+    bad = [
+        ("q", torch.zeros(2, 4, 128, dtype=torch.bfloat16), "shape"),
+        ("q", torch.zeros(2, 8, 128), "must be one of"),                    # f32 q on a bf16 pool
+        ("k_pool", torch.zeros(19, 2, 16, 128, dtype=torch.bfloat16), "bytes"),
+        ("block_table", torch.zeros(2, 9, dtype=torch.int32), "elements"),
+        ("block_table", torch.zeros(2, 10, dtype=torch.int64), "int32"),
+        ("seq_lens", torch.zeros(1, dtype=torch.int32), "elements"),
+        ("block_valid", torch.zeros(2, 9, dtype=torch.uint8), "elements"),
+        ("out", torch.zeros(2, 8, 64), "shape"),
+        ("out", torch.zeros(2, 8, 128, dtype=torch.float16), "must be one of"),
+    ]
+    for name, t, what in bad:
+        kw = dict(ok)
+        kw[name] = t
+        with pytest.raises(ValueError, match=what):
+            B.decode_attn_paged(d, **kw)
+    # the well-shaped CPU tensors get as far as the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        B.decode_attn_paged(d, **ok)
+    with pytest.raises(ValueError, match="shape"):
+        B.kv_write_paged(d, ok["k_pool"], ok["v_pool"], torch.zeros(5, 2, 64, dtype=torch.bfloat16),
+                         torch.zeros(5, 2, 128, dtype=torch.bfloat16),
+                         torch.zeros(5, dtype=torch.int32))
+
+
+def test_binding_checks_ring_tensors():
+    import torch
+    cfg = _cfg(batch=2, num_kv_heads=4, window=64)
+    kv, sp = B.swa_cache_required_bytes(cfg)
+    h = _create(batch=2, num_kv_heads=4, window=64)
+    B._RING_CFG[h] = cfg   # what swa_cache_create records for a handle it made
+    try:
+        q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+        with pytest.raises(ValueError, match="shape"):
+            B.decode_attn_ring(h, q, torch.zeros(2, 8, 64), torch.zeros(16, dtype=torch.uint8))
+        with pytest.raises(ValueError, match="shape"):
+            B.decode_step_ring(h, torch.zeros(2, 2, 128, dtype=torch.bfloat16),
+                               torch.zeros(2, 4, 128, dtype=torch.bfloat16),
+                               torch.zeros(2, dtype=torch.int32), q, torch.zeros(2, 8, 128),
+                               torch.zeros(16, dtype=torch.uint8))
+        with pytest.raises(ValueError, match="shape"):
+            B.kv_append_rope(h, torch.zeros(2, 3, 4, 128, dtype=torch.bfloat16),
+                             torch.zeros(2, 3, 4, 128, dtype=torch.bfloat16),
+                             torch.zeros(3, dtype=torch.int32))
+        with pytest.raises(ValueError, match="must be one of"):
+            B.prefill_attn_ring(h, torch.zeros(2, 3, 4, 128), torch.zeros(2, 3, 4, 128),
+                                torch.zeros(2, dtype=torch.int32), torch.zeros(2, 3, 8, 128),
+                                torch.zeros(2, 3, 8, 128), torch.zeros(16, dtype=torch.uint8))
+    finally:
+        B.swa_cache_destroy(h)
+    assert h not in B._RING_CFG
