@@ -1,13 +1,19 @@
 #!/usr/bin/env python3
 """Decode-step benchmark on one MI355X.
 
-A step is one pass of the whole decode path over one batch: for the ring
+A step is one pass of the whole decode path over one batch: for the paged /
+pool workloads, the decode over the pool and its merge; for the ring
 workloads, the RoPE append of the new token and the split-K decode, both done
 by one decode_step_ring call (one launch, plus the split merge when a head is
 spread over several workgroups; --unfused: kv_append_rope, then
-decode_attn_ring); for the paged / pool workloads, the decode and its merge.  Inputs are synthetic (synth/), resident
-in HBM before the timed region; every step's new-token rows and query are
-staged on the device beforehand.
+decode_attn_ring).  Inputs are synthetic (synth/), resident in HBM before the
+timed region; every step's new-token rows and query are staged on the device
+beforehand, and every timed call is marshalled before the timed region (the
+timed loops only issue the calls).
+
+The default workload is `paged` (32 sequences of 1K-32K tokens in 16-token
+blocks with a 2000-token shared prefix, GQA 32/8, bf16: the largest
+configuration and a target of the >= 70 % bar).
 
 Prints one JSON line:
   value            KV-read GB/s of the whole job: algorithmic KV bytes per step
@@ -18,14 +24,20 @@ Prints one JSON line:
                    the small split-merge launch that follows it in the same
                    call when there is one): algorithmic bytes per call / mean
                    call duration, from HIP events recorded on the launch
-                   stream at the two ends of a second region of `steps`
-                   decode calls issued back to back, against the 8 TB/s HBM
-                   peak; `traffic`
-                   is the measured HBM bytes per call from rocprofv3 counters
-                   (profiles/decode_<workload>_traffic.txt) when they were
-                   taken on the current kernel sources, else null.
+                   stream at the two ends of a second region of at least 64
+                   calls issued back to back, against the 8 TB/s HBM peak;
+                   `traffic` is the measured HBM bytes per call from rocprofv3
+                   counters (profiles/decode_<workload>_traffic.txt) when they
+                   were taken on the current kernel sources, else null.
   cpu_baseline     the float64 NumPy oracle on a bounded sample of the same
-                   workload (inputs already in host memory), host cores.
+                   workload (inputs already in host memory), on the host's
+                   cores (the cores this process may run on; the CPU model).
+  per_config       the other decode configurations (gqa-ring, long-pool-b1,
+                   long-pool-b16, mha-ring), each measured the same way in the
+                   same run: steps/s, step GB/s, the decode call's duration,
+                   GB/s and fraction of the peak, and the rocprofv3 average of
+                   the call's kernels from the committed profile when it was
+                   taken on the current kernel sources.
 
 Prefill workloads (mha-prefill, gqa-prefill): a step is one prefill_attn_ring
 call over a chunk of new tokens per sequence (rotation of the chunk, the
@@ -36,10 +48,10 @@ MFMA peak; `roofline` times the whole call (its three launches).
 
 Host-pool paging workload (long-pool-swap): a step is swa_pager_advance for
 the next step's block request (LRU decisions on the host, a validity launch
-on the attention stream, the block copies from pinned host memory on a copy
-stream, overlapping the attention) and the decode over the pool; `value`
-counts the blocks each decode actually saw.  `swap` reports the blocks and
-bytes copied per step, and the same steps without paging on the same pool.
+on the attention stream, the block copies from pinned host memory) and the
+decode over the pool; `value` counts the blocks each decode actually saw.
+`swap` reports the blocks and bytes copied per step, and the same steps
+without paging on the same pool.
 
 Paged pool grown by appends (paged-append): a step is kv_append_paged of one
 token per sequence through the block manager (table and length updates, the
@@ -49,7 +61,8 @@ lengths after its append.
 --graph issues the timed steps as one captured HIP graph (every step keeps its
 own inputs and positions) instead of eager calls; `launch` says which.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--graph]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                       [--no-per-config] [--graph]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
 """
 
@@ -60,6 +73,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -73,6 +87,9 @@ _CSRC = os.path.join(ROOT, "decode_attention_fixed_amd", "csrc")
 DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
 PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill.hip", "append_rope.hip",
                                                  "device_common.h")]
+DEFAULT_WORKLOAD = "paged"
+PER_CONFIG = ("gqa-ring", "long-pool-b1", "long-pool-b16", "mha-ring")
+MIN_CALLS = 64   # decode calls timed back to back for the roofline region
 
 
 def log(msg: str) -> None:
@@ -143,20 +160,38 @@ def prefill_flops(w, first_positions) -> int:
     return int(visible_keys(w, t).sum()) * w.num_q_heads * w.head_dim * 4
 
 
+def _records(path: str) -> dict:
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith(("#", "|", "-")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    return rec
+
+
 def traffic_record(name: str, prefix: str = "decode"):
     """Counter-measured HBM bytes per call of workload `name`, if they were
     taken on the current kernel sources."""
     path = os.path.join(PROFILES, f"{prefix}_{name}_traffic.txt")
     if not os.path.exists(path):
         return None
-    rec = {}
-    for line in open(path):
-        if ":" in line and not line.lstrip().startswith("#"):
-            k, v = line.split(":", 1)
-            rec[k.strip()] = v.strip()
+    rec = _records(path)
     if rec.get("source_sha256") != source_sha(prefix):
         return None
     return rec
+
+
+def profile_call_us(name: str, prefix: str = "decode"):
+    """rocprofv3's average duration of one decode call's kernels (attention
+    kernel plus merge) from profiles/<prefix>_<name>_kernel_stats.md, if that
+    profile was taken on the current kernel sources."""
+    path = os.path.join(PROFILES, f"{prefix}_{name}_kernel_stats.md")
+    if not os.path.exists(path):
+        return None
+    rec = _records(path)
+    if rec.get("source_sha256") != source_sha(prefix) or "call_us" not in rec:
+        return None
+    return float(rec["call_us"])
 
 
 def source_sha(prefix: str = "decode") -> str:
@@ -174,8 +209,25 @@ def decode_source_sha() -> str:
 # GPU side
 # ---------------------------------------------------------------------------
 
-def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True,
-            graph: bool = False) -> dict:
+class Run:
+    """The set-up of one workload on the device: `step[i]` issues timed step i
+    (its calls marshalled beforehand), `call[i]` one decode call of the
+    roofline region; `close()` frees everything."""
+
+    def __init__(self):
+        self.step = []
+        self.call = []
+        self.closers = []
+        self.extra = {}
+
+    def close(self) -> None:
+        for c in self.closers:
+            c()
+        self.step, self.call, self.closers = [], [], []
+
+
+def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: bool = True) -> Run:
+    """Stages inputs for n_steps steps and n_calls roofline calls."""
     import numpy as np
     import torch
 
@@ -184,11 +236,8 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
     from synth import TENSOR_K, TENSOR_Q, TENSOR_V
     from synth.draws import draw_rows_parallel
 
-    torch.cuda.set_device(0)
-    # steps with new tokens: warmup, then two timed regions (ring caches); the
-    # pools read the same state every step
-    total = warmup + 2 * steps
-    t0 = time.time()
+    run = Run()
+    total = n_steps + n_calls
     if w.kind == "ring" and w.chunk:
         # One chunk of rows drawn from the workload, reused by every call at
         # advancing positions (each call rotates and appends it anew).
@@ -202,13 +251,12 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
         lse = torch.empty(w.batch, w.chunk, w.num_q_heads, dtype=torch.float32, device="cuda")
         first = w.decode_start[None, :] + w.chunk * np.arange(total)[:, None]
         pos_all = torch.from_numpy(first.astype(np.int32)).cuda()
-        handle = st.cache.handle
-
-        def pre(i):
-            pass
-
-        def decode(i):
-            B.prefill_attn_ring(handle, inp["k"], inp["v"], pos_all[i], inp["q"], out, ws, lse)
+        calls = [B.prefill_attn_ring(st.cache.handle, inp["k"], inp["v"], pos_all[i], inp["q"],
+                                     out, ws, lse, prepare=True) for i in range(total)]
+        run.step, run.call = calls[:n_steps], calls[n_steps:]
+        run.extra["flops_step"] = [prefill_flops(w, first[i]) for i in range(n_steps)]
+        run.extra["flops_call"] = [prefill_flops(w, first[n_steps + i]) for i in range(n_calls)]
+        run.closers.append(st.close)
     elif w.kind == "ring":
         st = RingState(w)
         st.prefill()
@@ -228,23 +276,29 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
         pos_all = torch.from_numpy(
             (start[None, :] + np.arange(total)[:, None]).astype(np.int32)).cuda()
         handle = st.cache.handle
-
         if unfused:  # the two entry points: append (rotating q in place), then decode
-            def pre(i):
-                B.kv_append_rope(handle, k_all[i], v_all[i], pos_all[i], q_all[i])
+            appends = [B.kv_append_rope(handle, k_all[i], v_all[i], pos_all[i], q_all[i],
+                                        prepare=True) for i in range(n_steps)]
+            decodes = [B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse,
+                                          prepare=True) for i in range(n_steps)]
 
-            def decode(i):
-                B.decode_attn_ring(handle, q_all[i][:, 0], st.out, st.workspace, st.lse)
+            def both(a, d):
+                def f():
+                    a()
+                    d()
+                return f
+            run.step = [both(appends[i], decodes[i]) for i in range(n_steps)]
+            # the decode call alone, repeated on the state the last step left
+            last = B.decode_attn_ring(handle, q_all[n_steps - 1][:, 0], st.out, st.workspace,
+                                      st.lse, prepare=True)
+            run.call = [last] * n_calls
         else:  # one call per step: the decode launch appends the token itself
-            step_fn = (B.decode_step_ring_shifted if w.positions == "cache"
-                       else B.decode_step_ring)
-
-            def pre(i):
-                pass
-
-            def decode(i):
-                step_fn(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i], q_all[i][:, 0],
-                        st.out, st.workspace, st.lse)
+            fn = B.decode_step_ring_shifted if w.positions == "cache" else B.decode_step_ring
+            calls = [fn(handle, k_all[i][:, 0], v_all[i][:, 0], pos_all[i], q_all[i][:, 0],
+                        st.out, st.workspace, st.lse, prepare=True) for i in range(total)]
+            run.step, run.call = calls[:n_steps], calls[n_steps:]
+        run.extra["bytes_step"] = run.extra["bytes_call"] = kv_bytes_per_step(w)
+        run.closers.append(st.close)
     elif w.kind == "paged-append":
         import ctypes
 
@@ -252,12 +306,12 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
         st = build_paged_append(w, extra_steps=total)
 
         def staged(tensor):
-            arr = np.empty((w.batch, total, w.num_kv_heads, w.head_dim), dtype=np.float32)
+            arr = np.empty((w.batch, n_steps, w.num_kv_heads, w.head_dim), dtype=np.float32)
             for b in range(w.batch):
-                draw_rows_parallel(w.seed, tensor, b, int(w.lengths[b]), total, w.num_kv_heads,
+                draw_rows_parallel(w.seed, tensor, b, int(w.lengths[b]), n_steps, w.num_kv_heads,
                                    w.head_dim, w.scale, w.dtype, out=arr[b])
-            t = to_device(arr, w.dtype)                               # [B, total, Hkv, d]
-            return t.permute(1, 0, 2, 3).contiguous().unsqueeze(2)    # [total, B, 1, Hkv, d]
+            t = to_device(arr, w.dtype)                               # [B, steps, Hkv, d]
+            return t.permute(1, 0, 2, 3).contiguous().unsqueeze(2)    # [steps, B, 1, Hkv, d]
 
         k_all, v_all = staged(TENSOR_K), staged(TENSOR_V)
         nq = min(total, w.decode_steps)
@@ -266,175 +320,211 @@ def run_gpu(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
                                                               for b in range(w.batch)]), zero]),
                                     w.dtype) for i in range(nq)])
         seqs = (ctypes.c_int32 * w.batch)(*range(w.batch))
-        calls = [B.prepare_decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
-                                             st.seq_lens, None, st.out, st.workspace, st.lse)
-                 for j in range(nq)]
+        decs = [B.decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
+                                    st.seq_lens, None, st.out, st.workspace, st.lse,
+                                    prepare=True) for j in range(nq)]
 
-        def pre(i):
-            st.append(seqs, k_all[i], v_all[i])
-
-        def decode(i):
-            calls[i % nq]()
+        def step(i):
+            def f():
+                st.append(seqs, k_all[i], v_all[i])
+                decs[i % nq]()
+            return f
+        run.step = [step(i) for i in range(n_steps)]
+        # the roofline region repeats the decode on the state the steps left
+        run.call = [decs[i % nq] for i in range(n_calls)]
+        base = int(w.lengths.sum())
+        run.extra["bytes_steps"] = [(base + w.batch * (s + 1)) * w.kv_bytes_per_token()
+                                    for s in range(n_steps)]
+        run.extra["bytes_call"] = (base + w.batch * n_steps) * w.kv_bytes_per_token()
+        run.closers.append(st.close)
     elif w.kind == "pager":
         import dataclasses
 
         from decode_attention_fixed_amd.workloads import PagerState
-        wl = dataclasses.replace(w, decode_steps=total + 1)
+        wl = dataclasses.replace(w, decode_steps=n_steps + 1)
         st = PagerState(wl)
         st.fill_host()
         st.reset()
         copy_stream = torch.cuda.Stream()
         st.warm(copy_stream)
         torch.cuda.synchronize()
-        qs = torch.stack([st.step_query(i) for i in range(min(total, w.decode_steps))])
-        reqs = [B.pack_requests(st.step_requests(i + 1)) for i in range(total)]
+        qs = torch.stack([st.step_query(i) for i in range(min(n_steps, w.decode_steps))])
+        reqs = [B.pack_requests(st.step_requests(i + 1)) for i in range(n_steps)]
         filled = sum(1 for b in range(w.batch) for x in st.slot_blocks(b) if x >= 0)
-        seen_blocks = {}   # step -> blocks the decode of that step sees
-        loaded = {}
-
+        seen, loaded = {}, {}
         host_us = {"advance": 0.0, "decode": 0.0}
-        calls = [B.prepare_decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
-                                             st.seq_lens, st.block_valid, st.out, st.workspace,
-                                             st.lse) for j in range(qs.shape[0])]
-        copy_stream = None if same_stream else copy_stream
+        decs = [B.decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
+                                    st.seq_lens, st.block_valid, st.out, st.workspace, st.lse,
+                                    prepare=True) for j in range(qs.shape[0])]
+        cs = None if same_stream else copy_stream
 
-        def pre(i):
-            t = time.perf_counter()
-            n = st.advance(reqs[i], copy_stream)
-            host_us["advance"] += (time.perf_counter() - t) * 1e6
-            loaded[i] = n
-            seen_blocks[i] = filled - n
-
-        def decode(i):
-            t = time.perf_counter()
-            calls[i % len(calls)]()
-            host_us["decode"] += (time.perf_counter() - t) * 1e6
+        def step(i):
+            def f():
+                t = time.perf_counter()
+                n = st.advance(reqs[i], cs)
+                host_us["advance"] += (time.perf_counter() - t) * 1e6
+                loaded[i] = n
+                seen[i] = filled - n
+                t = time.perf_counter()
+                decs[i % len(decs)]()
+                host_us["decode"] += (time.perf_counter() - t) * 1e6
+            return f
+        run.step = [step(i) for i in range(n_steps)]
+        run.extra.update(pager_state=st, pager_seen=seen, pager_loaded=loaded,
+                         pager_host_us=host_us, pager_decs=decs, pager_q=qs,
+                         block_bytes=2 * w.num_kv_heads * w.block_size * w.head_dim * 2)
+        run.closers.append(st.close)
     else:
         st = PagedState(w, out_dtype=torch.float32)
         st.fill()
         qs = torch.stack([st.step_query(i) for i in range(min(total, w.decode_steps))])
         # Pools smaller than the ~256 MB last-level cache are cycled through
-        # enough copies (>= 600 MB) that a step cannot be served from cache.
+        # enough copies (>= 600 MB) that a call cannot be served from cache.
         pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
         copies = max(1, math.ceil(600e6 / pool_bytes)) if pool_bytes < 300e6 else 1
         pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
                                             for _ in range(copies - 1)]
+        calls = [B.decode_attn_paged(st.desc, qs[i % qs.shape[0]], *pools[i % copies],
+                                     st.block_table, st.seq_lens, st.block_valid, st.out,
+                                     st.workspace, st.lse, prepare=True) for i in range(total)]
+        run.step, run.call = calls[:n_steps], calls[n_steps:]
+        run.extra["bytes_step"] = run.extra["bytes_call"] = kv_bytes_per_step(w)
+        run.extra["pool_copies"] = copies
 
-        def pre(i):
-            pass
-
-        def decode(i):
-            k, v = pools[i % copies]
-            B.decode_attn_paged(st.desc, qs[i % qs.shape[0]], k, v, st.block_table, st.seq_lens,
-                                st.block_valid, st.out, st.workspace, st.lse)
+        def free():
+            pools.clear()
+        run.closers.append(free)
     torch.cuda.synchronize()
-    log(f"setup {time.time() - t0:.1f} s")
+    return run
 
-    for i in range(warmup):
-        pre(i)
-        decode(i)
-    torch.cuda.synchronize()
 
-    # Region 1: whole steps, events only at the two ends.  With `graph`, the
-    # same steps (each with its own inputs and positions) are captured into
-    # one HIP graph beforehand and the region is its one replay.
+def time_region(fns, graph: bool = False) -> float:
+    """ms of issuing every function of `fns` once, in order, between two HIP
+    events on the current stream (or one replay of a graph capturing them)."""
+    import torch
     begin = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     if graph:
+        # captured on the stream the calls were marshalled for (the current one)
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for s in range(steps):
-                i = warmup + s
-                pre(i)
-                decode(i)
+        with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+            for f in fns:
+                f()
         torch.cuda.synchronize()
-    wall0 = time.perf_counter()
+    torch.cuda.synchronize()
     begin.record()
     if graph:
         g.replay()
     else:
-        for s in range(steps):
-            i = warmup + s
-            pre(i)
-            decode(i)
+        for f in fns:
+            f()
     end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = begin.elapsed_time(end)
+    return begin.elapsed_time(end)
 
-    # Region 2: `steps` decode calls back to back, events at the two ends: the
-    # mean duration of one decode call as the kernels run in a stream.  Ring
-    # caches: the fused steps go on with new tokens (with --unfused, the
-    # decode call alone, repeated on the state the last step left).  Every
-    # call reads the whole resident cache again (larger than the last-level
-    # cache, or cycled through pool copies that together are).
-    torch.cuda.synchronize()
-    begin.record()
-    for s in range(steps):
-        i = warmup + steps + s
-        decode(warmup + steps - 1 if unfused and w.kind == "ring" and not w.chunk else i)
-    end.record()
-    torch.cuda.synchronize()
-    dec_ms = begin.elapsed_time(end) / steps
-    res = {"total_ms": total_ms, "wall_s": wall, "decode_ms_mean": dec_ms}
-    if w.kind == "paged-append":
-        # tokens each timed step attends: every sequence's length after its append
-        base = int(w.lengths.sum())
-        res["kv_bytes_region1"] = sum(base + w.batch * (warmup + s + 1) for s in range(steps)) * \
-            w.kv_bytes_per_token()
-        # region 2 repeats the decode on the state region 1 left (no appends)
-        res["kv_bytes_region2"] = (base + w.batch * (warmup + steps)) * w.kv_bytes_per_token()
-        st.close()
-    if w.kind == "pager":
-        res["host_us_per_step"] = {k: round(v / (warmup + steps), 1) for k, v in host_us.items()}
-        timed = range(warmup, warmup + steps)
-        res["kv_bytes_region1"] = sum(seen_blocks[i] for i in timed) * w.block_size * \
-            w.kv_bytes_per_token()
-        res["blocks_loaded_region1"] = sum(loaded[i] for i in timed)
-        res["block_bytes"] = 2 * w.num_kv_heads * w.block_size * w.head_dim * 2
-        st.commit()
-        torch.cuda.synchronize()
-        # Region 2 for the pager: the decode alone, back to back, over cycled
-        # copies of the pool (>= 600 MB together, so none is served from the
-        # last-level cache): the attention kernel's own rate.
-        pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
-        copies = max(1, math.ceil(600e6 / pool_bytes))
-        pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
-                                            for _ in range(copies - 1)]
-        visible = int(st.block_valid.sum().item())
-        cyc = [B.prepare_decode_attn_paged(st.desc, qs[j % qs.shape[0]], k, v, st.block_table,
-                                           st.seq_lens, st.block_valid, st.out, st.workspace,
-                                           st.lse) for j, (k, v) in enumerate(pools)]
+
+def measure(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True,
+            graph: bool = False) -> dict:
+    """Sets the workload up and times it, everything on one stream of its own
+    (the marshalled calls carry that stream; a graph is captured on it)."""
+    import torch
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        return _measure(w, steps, warmup, unfused, same_stream, graph)
+
+
+def _measure(w, steps, warmup, unfused, same_stream, graph) -> dict:
+    import torch
+    t0 = time.time()
+    # the pager and the block manager keep host state per step: no roofline
+    # region of extra steps for them (their region 2 repeats the decode)
+    n_calls = 0 if w.kind in ("pager",) else max(steps, MIN_CALLS)
+    run = setup(w, warmup + steps, n_calls, unfused, same_stream)
+    log(f"{w.name}: setup {time.time() - t0:.1f} s")
+    try:
         for i in range(warmup):
-            cyc[i % copies]()
+            run.step[i]()
         torch.cuda.synchronize()
-        begin.record()
-        for s in range(steps):
-            cyc[s % copies]()
-        end.record()
+        # Region 1: whole steps, events only at the two ends.
+        timed = run.step[warmup:warmup + steps]
+        wall0 = time.perf_counter()
+        total_ms = time_region(timed, graph)
+        wall = time.perf_counter() - wall0
+        res = {"total_ms": total_ms, "wall_s": wall}
+        if w.kind == "pager":
+            return _pager_regions(w, run, warmup, steps, res)
+        # Region 2: decode calls back to back (the dominant kernel as it runs
+        # in a stream), events at the two ends.
+        res["calls"] = len(run.call)
+        res["decode_ms_mean"] = time_region(run.call) / len(run.call)
+        if w.kind == "ring" and w.chunk:
+            res["flops_region1"] = sum(run.extra["flops_step"][warmup:])
+            res["flops_per_call"] = sum(run.extra["flops_call"]) / len(run.call)
+        elif w.kind == "paged-append":
+            res["kv_bytes_region1"] = sum(run.extra["bytes_steps"][warmup:])
+            res["kv_bytes_call"] = run.extra["bytes_call"]
+        else:
+            res["kv_bytes_region1"] = run.extra["bytes_step"] * steps
+            res["kv_bytes_call"] = run.extra["bytes_call"]
+        return res
+    finally:
+        run.close()
         torch.cuda.synchronize()
-        res["decode_ms_mean"] = begin.elapsed_time(end) / steps
-        res["kv_bytes_region2"] = visible * w.block_size * w.kv_bytes_per_token()
-        # Region 3: the same steps without paging, on the one live pool (the
-        # cache conditions of region 1): what the paging adds to a step.
-        begin.record()
-        for s in range(steps):
-            calls[s % len(calls)]()
-        end.record()
-        torch.cuda.synchronize()
-        res["no_swap_ms"] = begin.elapsed_time(end) / steps
-        st.close()
-    if w.kind == "ring" and w.chunk:
-        first = w.decode_start[None, :] + w.chunk * np.arange(total)[:, None]
-        res["flops_region1"] = sum(prefill_flops(w, first[warmup + s]) for s in range(steps))
-        res["flops_region2"] = sum(prefill_flops(w, first[warmup + steps + s])
-                                   for s in range(steps))
+        torch.cuda.empty_cache()
+
+
+def _pager_regions(w, run, warmup, steps, res) -> dict:
+    import torch
+
+    from decode_attention_fixed_amd import binding as B
+    st = run.extra["pager_state"]
+    timed = range(warmup, warmup + steps)
+    res["host_us_per_step"] = {k: round(v / (warmup + steps), 1)
+                               for k, v in run.extra["pager_host_us"].items()}
+    res["kv_bytes_region1"] = sum(run.extra["pager_seen"][i] for i in timed) * w.block_size * \
+        w.kv_bytes_per_token()
+    res["blocks_loaded_region1"] = sum(run.extra["pager_loaded"][i] for i in timed)
+    res["block_bytes"] = run.extra["block_bytes"]
+    st.commit()
+    torch.cuda.synchronize()
+    # Region 2: the decode alone, back to back, over cycled copies of the pool
+    # (>= 600 MB together, so none is served from the last-level cache).
+    pool_bytes = st.k_pool.numel() * st.k_pool.element_size() * 2
+    copies = max(1, math.ceil(600e6 / pool_bytes))
+    pools = [(st.k_pool, st.v_pool)] + [(st.k_pool.clone(), st.v_pool.clone())
+                                        for _ in range(copies - 1)]
+    visible = int(st.block_valid.sum().item())
+    decs = run.extra["pager_decs"]
+    q0 = run.extra["pager_q"][0]
+    cyc = [B.decode_attn_paged(st.desc, q0, k, v, st.block_table, st.seq_lens, st.block_valid,
+                               st.out, st.workspace, st.lse, prepare=True) for k, v in pools]
+    n = max(steps, MIN_CALLS)
+    for i in range(warmup):
+        cyc[i % copies]()
+    res["calls"] = n
+    res["decode_ms_mean"] = time_region([cyc[s % copies] for s in range(n)]) / n
+    res["kv_bytes_call"] = visible * w.block_size * w.kv_bytes_per_token()
+    # Region 3: the same steps without paging, on the one live pool (the
+    # cache conditions of region 1): what the paging adds to a step.
+    res["no_swap_ms"] = time_region([decs[s % len(decs)] for s in range(steps)]) / steps
+    pools.clear()
     return res
 
 
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
 
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     """Times the float64 oracle on whole (sequence, decode step) samples, in
@@ -509,16 +599,17 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         done = done or step >= w.decode_steps
     per_seq = timed / n
     steps_per_s = 1.0 / (per_seq * w.batch)
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    blas = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+    host = {"cores": cores, "blas_threads": blas, "cpu_model": cpu_model(), "kind": "oracle"}
     if w.kind == "ring" and w.chunk:
-        return {"value": round(flops / timed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-                "kind": "oracle",
+        return {"value": round(flops / timed / 1e12, 6), "unit": "TFLOP/s", **host,
                 "sample": (f"{n} (sequence, chunk row) samples of {w.name} (sequences in "
                            f"order, rows from the first chunk's first; all heads; a chunk "
                            f"row is the decode step at its position), inputs pre-drawn in "
-                           f"host memory; float64 NumPy, {timed:.1f} s timed; BLAS threads "
-                           f"{threads}, elementwise ops on one thread; useful flops of the "
-                           f"sampled rows / time")}
+                           f"host memory; float64 NumPy, {timed:.1f} s timed; {cores} cores "
+                           f"available, BLAS threads {blas}, elementwise ops on one thread; "
+                           f"useful flops of the sampled rows / time")}
     if w.kind == "pager":
         step_bytes = len(pager_sets[0][0]) * w.block_size * w.kv_bytes_per_token() * w.batch
     elif w.kind == "paged-append":
@@ -526,11 +617,12 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     else:
         step_bytes = kv_bytes_per_step(w)
     return {"value": round(steps_per_s * step_bytes / 1e9, 4), "unit": "GB/s",
-            "steps_per_s": round(steps_per_s, 4), "cores": threads, "kind": "oracle",
+            "steps_per_s": round(steps_per_s, 4), **host,
             "sample": (f"{n} (sequence, decode step) samples of {w.name} (sequences in order, "
                        f"steps from 0; all heads), inputs pre-drawn in host memory; float64 "
-                       f"NumPy, {timed:.1f} s timed; BLAS threads {threads}, elementwise ops "
-                       f"on one thread; scaled to one step of the full batch")}
+                       f"NumPy, {timed:.1f} s timed; {cores} cores available, BLAS threads "
+                       f"{blas}, elementwise ops on one thread; scaled to one step of the "
+                       f"full batch")}
 
 
 def copy_calibration(nbytes: int = 1 << 30) -> None:
@@ -554,10 +646,14 @@ def copy_calibration(nbytes: int = 1 << 30) -> None:
                       "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# the JSON line
+# ---------------------------------------------------------------------------
+
 def prefill_line(w, args, res) -> dict:
     ms_per_step = res["total_ms"] / args.steps
     value = res["flops_region1"] / (res["total_ms"] / 1e3) / 1e12
-    per_call = res["flops_region2"] / args.steps
+    per_call = res["flops_per_call"]
     achieved = per_call / (res["decode_ms_mean"] / 1e3) / 1e12
     traffic = traffic_record(w.name, "prefill")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -568,6 +664,7 @@ def prefill_line(w, args, res) -> dict:
                 "kernel": ("prefill call: chunk rotation, the windowed causal attention "
                            "kernel (S in bf16, P V in fp16 MFMA, fp32 accumulation) and the "
                            "append, on the launch stream, timed together"),
+                "calls": res["calls"], "call_us": round(res["decode_ms_mean"] * 1e3, 2),
                 "algorithmic_flops": int(per_call)}
     return {
         "metric": "prefill-attention TFLOP/s", "value": round(value, 2), "unit": "TFLOP/s",
@@ -580,13 +677,39 @@ def prefill_line(w, args, res) -> dict:
     }
 
 
+def decode_numbers(w, steps: int, res: dict) -> dict:
+    ms_per_step = res["total_ms"] / steps
+    value = res["kv_bytes_region1"] / (res["total_ms"] / 1e3) / 1e9
+    achieved = res["kv_bytes_call"] / (res["decode_ms_mean"] / 1e3) / 1e9
+    return {"ms_per_step": ms_per_step, "value": value, "achieved": achieved,
+            "call_us": res["decode_ms_mean"] * 1e3}
+
+
+def per_config_entry(name: str, args) -> dict:
+    from synth import WORKLOADS
+    w = WORKLOADS[name]
+    res = measure(w, args.steps, args.warmup)
+    n = decode_numbers(w, args.steps, res)
+    prof = profile_call_us(name)
+    return {"workload": describe(w)["workload"], "steps_per_s": round(1e3 / n["ms_per_step"], 1),
+            "ms_per_step": round(n["ms_per_step"], 5), "gbs": round(n["value"], 1),
+            "call_us": round(n["call_us"], 2), "call_gbs": round(n["achieved"], 1),
+            "frac": round(n["achieved"] / HBM_PEAK_GBS, 4),
+            "profile_call_us": prof,
+            "profile_frac": (round(res["kv_bytes_call"] / (prof * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                             if prof else None),
+            "algorithmic_bytes": res["kv_bytes_call"]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha-ring")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure the named workload only (the profiling runs use this)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring caches: kv_append_rope + decode_attn_ring per step instead of "
@@ -616,41 +739,36 @@ def main() -> int:
         print(f"--graph: workload {w.name} runs host logic every step and is not captured",
               file=sys.stderr)
         return 2
-    res = run_gpu(w, args.steps, args.warmup, args.unfused, not args.copy_stream, args.graph)
+    res = measure(w, args.steps, args.warmup, args.unfused, not args.copy_stream, args.graph)
     if w.kind == "ring" and w.chunk:
         out = prefill_line(w, args, res)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(w)
         print(json.dumps(out), flush=True)
         return 0
-    if w.kind in ("pager", "paged-append"):
-        kv_bytes = res["kv_bytes_region2"]
-        ms_per_step = res["total_ms"] / args.steps
-        value_gbs = res["kv_bytes_region1"] / (res["total_ms"] / 1e3) / 1e9
-    else:
-        kv_bytes = kv_bytes_per_step(w)
-        ms_per_step = res["total_ms"] / args.steps
-        value_gbs = kv_bytes * args.steps / (res["total_ms"] / 1e3) / 1e9
-    achieved = kv_bytes / (res["decode_ms_mean"] / 1e3) / 1e9
+    n = decode_numbers(w, args.steps, res)
     traffic = traffic_record(w.name)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+    prof = profile_call_us(w.name)
+    roofline = {"bound": "hbm", "achieved": round(n["achieved"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(n["achieved"] / HBM_PEAK_GBS, 4),
                 "traffic": (int(float(traffic["fetch_bytes_per_call"])
                                 + float(traffic["write_bytes_per_call"]))
                             if traffic else None),
                 "kernel": ("decode call: the attention kernel, plus the split merge "
                            "launch when a head's rows are spread over several workgroups; "
                            "both on the launch stream, timed together"),
-                "algorithmic_bytes": kv_bytes}
+                "calls": res["calls"], "call_us": round(n["call_us"], 2),
+                "profile_call_us": prof,
+                "algorithmic_bytes": res["kv_bytes_call"]}
     out = {
-        "metric": "decode-attention KV-read GB/s", "value": round(value_gbs, 1), "unit": "GB/s",
+        "metric": "decode-attention KV-read GB/s", "value": round(n["value"], 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(n["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8" if getattr(w, "cache", "") == "i8" else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic", "config": describe(w),
-        "steps_per_s": round(1e3 / ms_per_step, 1),
-        "hbm_frac_of_peak": round(value_gbs / HBM_PEAK_GBS, 4),
+        "steps_per_s": round(1e3 / n["ms_per_step"], 1),
+        "hbm_frac_of_peak": round(n["value"] / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "launch": "one HIP graph of the timed steps" if args.graph else "eager calls",
     }
@@ -659,7 +777,7 @@ def main() -> int:
         out["swap"] = {
             "blocks_per_step": round(per_step, 3),
             "bytes_per_step": int(per_step * res["block_bytes"]),
-            "host_to_device_gbs": round(per_step * res["block_bytes"] / ms_per_step / 1e6, 2),
+            "host_to_device_gbs": round(per_step * res["block_bytes"] / n["ms_per_step"] / 1e6, 2),
             "no_swap_ms_per_step": round(res["no_swap_ms"], 5),
             "host_us_per_step": res["host_us_per_step"],
             "wall_ms_per_step": round(res["wall_s"] * 1e3 / args.steps, 5),
@@ -668,6 +786,11 @@ def main() -> int:
                      "no_swap_ms_per_step is the same decode on the same pool without "
                      "paging"),
         }
+    if not args.no_per_config and w.name == DEFAULT_WORKLOAD and not args.graph:
+        out["per_config"] = []
+        for name in PER_CONFIG:
+            out["per_config"].append(per_config_entry(name, args))
+            log(f"per-config {name}: {out['per_config'][-1]['call_gbs']} GB/s per call")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

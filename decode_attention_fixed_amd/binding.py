@@ -135,6 +135,24 @@ def _check(fn: str, code: int) -> None:
         raise SwaError(fn, code)
 
 
+def _invoke(name: str, args: tuple, keep: tuple, prepare: bool):
+    """Calls LIB.<name>(*args), or with prepare=True returns a function of no
+    arguments that makes that call (the arguments marshalled once, for loops
+    that repeat one call on the same buffers; the tensors in `keep` stay alive
+    as long as the function)."""
+    fn = getattr(LIB, name)
+    if not prepare:
+        _check(name, fn(*args))
+        return None
+
+    def call() -> None:
+        code = fn(*args)
+        if code != SWA_OK:
+            raise SwaError(name, code)
+    call.keep = keep
+    return call
+
+
 def swa_last_error() -> str:
     return LIB.swa_last_error().decode()
 
@@ -255,9 +273,10 @@ def swa_cache_destroy(handle: int | None) -> None:
 
 
 def kv_append_rope(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
-                   q_inout: torch.Tensor | None = None, stream=None) -> None:
+                   q_inout: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """k_new, v_new [B, T, Hkv, d]; pos [B] int32 (position of token 0);
-    q_inout [B, T, Hq, d] or None, rotated in place."""
+    q_inout [B, T, Hq, d] or None, rotated in place.  prepare=True: return the
+    call marshalled once instead of making it."""
     n_tokens = k_new.shape[1]
     hq = q_inout.shape[2] if q_inout is not None else 0
     cfg = _ring_cfg(handle)
@@ -267,10 +286,9 @@ def kv_append_rope(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: t
         _expect(v_new, "v_new", (cfg.batch, n_tokens, cfg.num_kv_heads, cfg.head_dim), rt)
         _expect(pos, "pos", (cfg.batch,), (torch.int32,))
         _expect(q_inout, "q_inout", (cfg.batch, n_tokens, hq, cfg.head_dim), rt)
-    _check("kv_append_rope",
-           LIB.kv_append_rope(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
-                              _ptr(pos, "pos", torch.int32), n_tokens, _ptr(q_inout, "q_inout"),
-                              hq, _stream(stream)))
+    args = (handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _ptr(pos, "pos", torch.int32),
+            n_tokens, _ptr(q_inout, "q_inout"), hq, _stream(stream))
+    return _invoke("kv_append_rope", args, (k_new, v_new, pos, q_inout), prepare)
 
 
 def decode_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -306,29 +324,34 @@ def _check_ring_decode(handle: int, q: torch.Tensor, out: torch.Tensor,
 
 def decode_attn_ring(handle: int, q: torch.Tensor, out: torch.Tensor,
                      workspace: torch.Tensor, lse: torch.Tensor | None = None,
-                     scale: float = 0.0, stream=None) -> None:
-    """q [B, Hq, d] (rotated); out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
+                     scale: float = 0.0, stream=None, prepare: bool = False):
+    """q [B, Hq, d] (rotated); out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None.
+    prepare=True: return the call marshalled once instead of making it."""
     _check_ring_decode(handle, q, out, lse)
-    _check("decode_attn_ring",
-           LIB.decode_attn_ring(handle, _ptr(q, "q"), q.shape[1], scale, _ptr(out, "out"),
-                                _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
-                                _ptr(workspace, "workspace"), workspace.numel() *
-                                workspace.element_size(), _stream(stream)))
+    args = (handle, _ptr(q, "q"), q.shape[1], scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+            _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return _invoke("decode_attn_ring", args, (q, out, lse, workspace), prepare)
+
+
+def _step_args(handle, k_new, v_new, pos, q, out, workspace, lse, scale, stream) -> tuple:
+    _check_ring_decode(handle, q, out, lse, k_new, v_new, pos)
+    return (handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _ptr(pos, "pos", torch.int32),
+            _ptr(q, "q"), q.shape[1], scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
+            _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def decode_step_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
                      q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                     lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+                     lse: torch.Tensor | None = None, scale: float = 0.0, stream=None,
+                     prepare: bool = False):
     """Append of one token per sequence + decode in one call.  k_new, v_new
     [B, Hkv, d]; pos [B] int32; q [B, Hq, d] NOT rotated (left unchanged);
-    out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None."""
-    _check_ring_decode(handle, q, out, lse, k_new, v_new, pos)
-    _check("decode_step_ring",
-           LIB.decode_step_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
-                                _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1], scale,
-                                _ptr(out, "out"), _DTYPE_CODE[out.dtype],
-                                _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
-                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    out [B, Hq, d] float32 or bf16; lse [B, Hq] float32 or None.
+    prepare=True: return the call marshalled once instead of making it."""
+    args = _step_args(handle, k_new, v_new, pos, q, out, workspace, lse, scale, stream)
+    return _invoke("decode_step_ring", args, (k_new, v_new, pos, q, out, workspace, lse), prepare)
 
 
 def pos_advance(pos: torch.Tensor, delta: int = 1, stream=None) -> None:
@@ -342,18 +365,12 @@ def pos_advance(pos: torch.Tensor, delta: int = 1, stream=None) -> None:
 def decode_step_ring_shifted(handle: int, k_new: torch.Tensor, v_new: torch.Tensor,
                              pos: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
                              workspace: torch.Tensor, lse: torch.Tensor | None = None,
-                             scale: float = 0.0, stream=None) -> None:
+                             scale: float = 0.0, stream=None, prepare: bool = False):
     """decode_step_ring with positions taken inside the cache (sinks scored
     against the query rotated at its cache position)."""
-    _check_ring_decode(handle, q, out, lse, k_new, v_new, pos)
-    _check("decode_step_ring_shifted",
-           LIB.decode_step_ring_shifted(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
-                                        _ptr(pos, "pos", torch.int32), _ptr(q, "q"), q.shape[1],
-                                        scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
-                                        _ptr(lse, "lse", torch.float32),
-                                        _ptr(workspace, "workspace"),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream(stream)))
+    args = _step_args(handle, k_new, v_new, pos, q, out, workspace, lse, scale, stream)
+    return _invoke("decode_step_ring_shifted", args, (k_new, v_new, pos, q, out, workspace, lse),
+                   prepare)
 
 
 def prefill_attn_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -373,7 +390,8 @@ def new_prefill_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_
 
 def prefill_attn_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
                       q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                      lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+                      lse: torch.Tensor | None = None, scale: float = 0.0, stream=None,
+                      prepare: bool = False):
     """Chunked prefill: k_new, v_new [B, T, Hkv, d]; pos [B] int32 (position of
     token 0); q [B, T, Hq, d] NOT rotated (left unchanged); out [B, T, Hq, d]
     float32 or bf16; lse [B, T, Hq] float32 or None."""
@@ -388,12 +406,13 @@ def prefill_attn_ring(handle: int, k_new: torch.Tensor, v_new: torch.Tensor, pos
         _expect(q, "q", (cfg.batch, T, hq, cfg.head_dim), rt)
         _expect(out, "out", (cfg.batch, T, hq, cfg.head_dim), _OUT_DTYPES)
         _expect(lse, "lse", (cfg.batch, T, hq), (torch.float32,))
-    _check("prefill_attn_ring",
-           LIB.prefill_attn_ring(handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
-                                 _ptr(pos, "pos", torch.int32), k_new.shape[1], _ptr(q, "q"),
-                                 q.shape[2], scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype],
-                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (handle, _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _ptr(pos, "pos", torch.int32),
+            k_new.shape[1], _ptr(q, "q"), q.shape[2], scale, _ptr(out, "out"),
+            _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return _invoke("prefill_attn_ring", args, (k_new, v_new, pos, q, out, workspace, lse),
+                   prepare)
 
 
 # ---------------------------------------------------------------------------
@@ -443,17 +462,16 @@ def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
                       v_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                       block_valid: torch.Tensor | None, out: torch.Tensor,
                       workspace: torch.Tensor, lse: torch.Tensor | None = None,
-                      scale: float = 0.0, stream=None) -> None:
+                      scale: float = 0.0, stream=None, prepare: bool = False):
+    """prepare=True: return the call marshalled once instead of making it."""
     _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
-    _check("decode_attn_paged",
-           LIB.decode_attn_paged(ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"),
-                                 _ptr(v_pool, "v_pool"),
-                                 _ptr(block_table, "block_table", torch.int32),
-                                 _ptr(seq_lens, "seq_lens", torch.int32),
-                                 _ptr(block_valid, "block_valid", torch.uint8), scale,
-                                 _ptr(out, "out"), _DTYPE_CODE[out.dtype],
-                                 _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+            _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
+            _ptr(block_valid, "block_valid", torch.uint8), scale, _ptr(out, "out"),
+            _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, workspace, lse)
+    return _invoke("decode_attn_paged", args, keep, prepare)
 
 
 def prepare_decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
@@ -462,23 +480,9 @@ def prepare_decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch
                               out: torch.Tensor, workspace: torch.Tensor,
                               lse: torch.Tensor | None = None, scale: float = 0.0, stream=None):
     """decode_attn_paged's arguments marshalled once (stream included);
-    returns a function of no arguments that makes the call, for a loop that
-    repeats one call on the same buffers."""
-    _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
-    args = (ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
-            _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
-            _ptr(block_valid, "block_valid", torch.uint8), scale, _ptr(out, "out"),
-            _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace"),
-            workspace.numel() * workspace.element_size(), _stream(stream))
-    fn = LIB.decode_attn_paged
-    keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, workspace, lse)
-
-    def call() -> None:
-        code = fn(*args)
-        if code != SWA_OK:
-            raise SwaError("decode_attn_paged", code)
-    call.keep = keep  # the tensors stay alive as long as the call
-    return call
+    returns a function of no arguments that makes the call."""
+    return decode_attn_paged(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out,
+                             workspace, lse, scale, stream, prepare=True)
 
 
 def kv_write_paged(desc: SwaPagedDesc, k_pool: torch.Tensor, v_pool: torch.Tensor,
