@@ -86,6 +86,8 @@ _PROTOS = {
     "decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
+    "decode_attn_paged_noalloc": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp,
+                                                 _vp, _vp, ctypes.c_float, _vp, _i32, _vp, _vp]),
     "kv_write_paged": (ctypes.c_int, [ctypes.POINTER(SwaPagedDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i32, ctypes.c_float, _i32, _vp]),
     "swa_blocks_create": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
@@ -472,6 +474,25 @@ def decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
             workspace.numel() * workspace.element_size(), _stream(stream))
     keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, workspace, lse)
     return _invoke("decode_attn_paged", args, keep, prepare)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SWA_NOALLOC_SCRATCH_BYTES of include/swa.h
+
+
+def decode_attn_paged_noalloc(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
+                              v_pool: torch.Tensor, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, block_valid: torch.Tensor | None,
+                              out: torch.Tensor, lse: torch.Tensor | None = None,
+                              scale: float = 0.0, stream=None, prepare: bool = False):
+    """decode_attn_paged without a workspace: the partial results go to the
+    library's fixed per-device array (calls on one device must not overlap)."""
+    _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
+    args = (ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+            _ptr(block_table, "block_table", torch.int32), _ptr(seq_lens, "seq_lens", torch.int32),
+            _ptr(block_valid, "block_valid", torch.uint8), scale, _ptr(out, "out"),
+            _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32), _stream(stream))
+    keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
+    return _invoke("decode_attn_paged_noalloc", args, keep, prepare)
 
 
 def prepare_decode_attn_paged(desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,

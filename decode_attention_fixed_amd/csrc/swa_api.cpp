@@ -4,12 +4,13 @@
 // contract of every entry point.
 #include "swa.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>  // __device__ storage (scratch) and HIP_SYMBOL
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -550,11 +551,13 @@ swa_status swa_pool_required_bytes(const swa_paged_desc* desc, size_t* kv_bytes_
   return ok();
 }
 
-swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const void* k_pool,
-                             const void* v_pool, const int32_t* block_table,
-                             const int32_t* seq_lens, const uint8_t* block_valid, float scale,
-                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Checks a paged decode call (workspace included) and launches it; shared by
+// decode_attn_paged and decode_attn_paged_noalloc.
+static swa_status paged_decode(const swa_paged_desc* desc, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const uint8_t* block_valid, float scale,
+                               void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream, const char* name) {
   swa_status st = check_paged_desc(desc);
   if (st != SWA_OK) return st;
   st = check_group(desc->num_q_heads, desc->num_kv_heads);
@@ -605,8 +608,92 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
     p.v_scale = i8_scales(const_cast<void*>(v_pool), rows, desc->head_dim);
   }
   fill_workspace_ptrs(p, workspace, lay);
-  return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream)),
-                  "decode_attn_paged");
+  return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream)), name);
+}
+
+swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, const uint8_t* block_valid, float scale,
+                             void* out, swa_dtype out_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, scale, out,
+                      out_dtype, lse, workspace, workspace_bytes, stream, "decode_attn_paged");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode_attn_paged_noalloc: the paged decode with its partial results in a
+// fixed device array of this library instead of a caller's workspace, for
+// callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static_assert(SWA_NOALLOC_SCRATCH_BYTES == kScratchBytes, "swa.h states the scratch maximum");
+
+// One copy per device, held from the module's load until the process ends.
+// In host code this name is only a handle for hipGetSymbolAddress: kernels
+// get the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with the device current) and kept.
+swa_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return from_hip(err, "decode_attn_paged_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SWA_ERR_UNSUPPORTED, "decode_attn_paged_noalloc: device %d beyond %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess)
+      return from_hip(err, "decode_attn_paged_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256))
+      return fail(SWA_ERR_HIP, "decode_attn_paged_noalloc: scratch address unusable");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+swa_status decode_attn_paged_noalloc(const swa_paged_desc* desc, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const uint8_t* block_valid, float scale, void* out,
+                                     swa_dtype out_dtype, float* lse, void* stream) {
+  // The size check comes first, on the host: a call beyond the fixed
+  // maximum is refused before any HIP call.
+  swa_status st = check_paged_desc(desc);
+  if (st != SWA_OK) return st;
+  st = check_group(desc->num_q_heads, desc->num_kv_heads);
+  if (st != SWA_OK) return st;
+  const size_t need =
+      swa::workspace_layout(desc->batch, desc->num_q_heads, desc->num_kv_heads, desc->head_dim,
+                            desc->max_blocks_per_seq * desc->block_size)
+          .total;
+  if (need > kScratchBytes)
+    return fail(SWA_ERR_WORKSPACE,
+                "decode_attn_paged_noalloc: these sizes need %zu bytes of partial results, "
+                "above the fixed %zu-byte maximum (use decode_attn_paged with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != SWA_OK) return st;
+  return paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, scale, out,
+                      out_dtype, lse, ws, kScratchBytes, stream, "decode_attn_paged_noalloc");
 }
 
 swa_status kv_write_paged(const swa_paged_desc* desc, void* k_pool, void* v_pool,

@@ -307,6 +307,30 @@ swa_status decode_attn_paged(const swa_paged_desc* desc, const void* q, const vo
                              void* out, swa_dtype out_dtype, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* decode_attn_paged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation and arguments as decode_attn_paged, with
+ * no workspace: the partial results live in a fixed array of this library
+ * in device memory, SWA_NOALLOC_SCRATCH_BYTES bytes per device, which each
+ * device holds from the library's first use on it until the process ends.
+ * Its device address is looked up on the first call on a device (that device
+ * current); no call allocates or frees anything.
+ *
+ *   Limit: sizes whose decode_attn_workspace_bytes(batch, Hq, Hkv, d,
+ *   max_blocks_per_seq * block_size) exceeds SWA_NOALLOC_SCRATCH_BYTES are
+ *   refused with SWA_ERR_WORKSPACE before any HIP call.
+ *   Sharing: every call on one device uses that device's one array; it needs
+ *   no initialisation (each call writes every entry it reads) and keeps the
+ *   last call's contents.  Calls that overlap on one device (two streams, two
+ *   threads, two captured graphs replayed concurrently) race on it: issue
+ *   them in one stream's order. */
+#define SWA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+swa_status decode_attn_paged_noalloc(const swa_paged_desc* desc, const void* q,
+                                     const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const uint8_t* block_valid, float scale, void* out,
+                                     swa_dtype out_dtype, float* lse, void* stream);
+
 /* Writes n_tokens rows into a paged pool, rotating K at a given position
  * first ([pool] "bake RoPE into K": each block becomes self-contained).
  *

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 30, declared
+    assert len(declared) == 31, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -470,3 +470,20 @@ def test_binding_checks_ring_tensors():
     finally:
         B.swa_cache_destroy(h)
     assert h not in B._RING_CFG
+
+
+def test_noalloc_refuses_beyond_its_maximum():
+    """decode_attn_paged_noalloc refuses sizes whose partial results exceed
+    its fixed array, on the host and before any HIP call (no GPU here: any HIP
+    call would fail with SWA_ERR_HIP instead)."""
+    d = B.make_paged_desc(512, 64, 8, 128, 16, 4096, 1 << 16, "bf16")
+    assert B.decode_attn_workspace_bytes(512, 64, 8, 128, 4096 * 16) > B.NOALLOC_SCRATCH_BYTES
+    rc = B.LIB.decode_attn_paged_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.0,
+                                         FAKE, B.SWA_F32, None, None)
+    assert rc == B.SWA_ERR_WORKSPACE
+    assert "maximum" in B.swa_last_error()
+    # and the argument checks of decode_attn_paged come first
+    bad = B.make_paged_desc(4, 12, 8, 128, 16, 64, 256, "bf16")    # 12 heads over 8 kv heads
+    assert B.LIB.decode_attn_paged_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                           0.0, FAKE, B.SWA_F32, None, None) == \
+        B.SWA_ERR_INVALID_ARG
