@@ -8,12 +8,14 @@ standard form is used: pairs of coordinates rotated by angle pos * theta_i,
 theta_i = base ** (-2 i / d), i < d/2.
 
 Two pairings are offered: "interleaved" pairs (2i, 2i+1), "half" pairs
-(i, i + d/2).  The choice of pairing and the frequencies beyond theta_0 are
-parity unpinned (the pages do not fix them): the GPU path only has to agree
-with this file.  Pinned: rotation at position 0 is the identity, norms are
-preserved, d = 2 rotates by `pos` radians, scores depend only on the
-position difference, and the two pairings are the same map up to a fixed
-coordinate permutation (tests/test_oracle_rope.py).
+(i, i + d/2).  The pages fix neither the pairing nor the frequencies, so the
+reading is the standard rotary embedding as library implementations define
+it, and both are pinned against two of them: GPT-J's interleaved form and
+LLaMA's half-split form in `transformers`, frequencies included
+(tests/test_oracle_rope_library.py).  Also pinned: rotation at position 0 is
+the identity, norms are preserved, d = 2 rotates by `pos` radians, scores
+depend only on the position difference, and the two pairings are the same
+map up to a fixed coordinate permutation (tests/test_oracle_rope.py).
 """
 
 from __future__ import annotations

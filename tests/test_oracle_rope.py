@@ -1,6 +1,6 @@
-"""Pins for oracle/rope.py.  The pairing convention and frequencies beyond the
-first pair are not fixed by the pages (parity unpinned); what any rotary
-embedding must satisfy is pinned here."""
+"""Pins for oracle/rope.py: what any rotary embedding must satisfy.  The
+pairings and frequencies themselves are pinned against library
+implementations in tests/test_oracle_rope_library.py."""
 
 import math
 
