@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libswa.so")
 
-SOURCES = ["swa_api.cpp", "pager_api.cpp", "blocks_api.cpp", "append_rope.hip", "decode.hip", "decode_mfma.hip",
+SOURCES = ["swa_api.cpp", "pager_api.cpp", "blocks_api.cpp", "append_rope.hip", "decode.hip", "decode_mfma.hip", "decode_shared.hip",
            "prefill.hip", "pager.hip", "positions.hip"]
 ARCH = "gfx950"
 FLAGS = [

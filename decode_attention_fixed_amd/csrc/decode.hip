@@ -474,10 +474,14 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
     slots = n > slots ? n : slots;
   }
   WorkspaceLayout w;
+  w.shared_base = static_cast<int64_t>(slots);
+  // partials of the shared-prefix pass
+  slots += static_cast<size_t>(prefix_chunks(batch, num_q_heads, num_kv_heads)) * units;
   w.o_offset = 0;
   w.lse_offset = up(slots * g * head_dim * sizeof(float));
   w.q_offset = w.lse_offset + up(slots * g * sizeof(float));
-  w.total = w.q_offset + up(static_cast<size_t>(batch) * num_q_heads * head_dim * sizeof(float));
+  w.plan_offset = w.q_offset + up(static_cast<size_t>(batch) * num_q_heads * head_dim * sizeof(float));
+  w.total = w.plan_offset + up((static_cast<size_t>(kPlanHead) + batch) * sizeof(int32_t));
   return w;
 }
 

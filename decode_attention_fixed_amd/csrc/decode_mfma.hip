@@ -1033,8 +1033,14 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
 // u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
 // granule order move u or w forward by one each, so the slots are distinct
 // and fewer than units + W).
+// Rows of sequence b that the shared-prefix pass attends (0 without a plan);
+// the pool kernel attends rows [shared_rows, len) of each sequence.
+__device__ __forceinline__ int shared_rows(const DecodeParams& p, int b) {
+  return p.plan != nullptr ? p.plan[kPlanHead + b] : 0;
+}
+
 __device__ __forceinline__ int granules(const DecodeParams& p, int b) {
-  return (PoolRows::tokens(p, b) + 63) >> 6;
+  return (PoolRows::tokens(p, b) - shared_rows(p, b) + 63) >> 6;
 }
 
 // W is a power of two (the host launches kPoolGrid or kPoolGrid / 2): the
@@ -1095,7 +1101,8 @@ __device__ void block_sum2(int64_t& x, int64_t& y, int64_t* s_red) {
 // in registers, while a piece is attended).
 template <int NT>
 struct SeqChunk {
-  int32_t len[NT];
+  int32_t len[NT];    // rows attended here (after the shared ones)
+  int32_t start[NT];  // rows attended by the shared-prefix pass
   int32_t excl[NT];
   int64_t red[2 * NT / 64];
   int32_t wsum[NT / 64];
@@ -1111,7 +1118,8 @@ __device__ int32_t load_chunk(const DecodeParams& p, SeqChunk<NT>& sc, int first
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = first + static_cast<int>(threadIdx.x);
-  const int len = b < p.batch ? PoolRows::tokens(p, b) : 0;
+  const int start = b < p.batch ? shared_rows(p, b) : 0;
+  const int len = b < p.batch ? PoolRows::tokens(p, b) - start : 0;
   const int x = (len + 63) >> 6;
   int incl = x;
 #pragma unroll
@@ -1129,6 +1137,7 @@ __device__ int32_t load_chunk(const DecodeParams& p, SeqChunk<NT>& sc, int first
     total += v;
   }
   sc.len[threadIdx.x] = len;
+  sc.start[threadIdx.x] = start;
   sc.excl[threadIdx.x] = before + incl - x;
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(total);
@@ -1181,12 +1190,14 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
     if (u0 >= g1) break;
     if (u1 > g0) {
       const int64_t e = ((g1 < u1 ? g1 : u1) - u0) * 64;
+      const int start = __builtin_amdgcn_readfirstlane(sc.start[i]);
       pc.b = b;
       pc.h = h;
-      pc.t0 = static_cast<int>(((g0 > u0 ? g0 : u0) - u0) * 64);
-      pc.t1 = static_cast<int>(e < len ? e : static_cast<int64_t>(len));
+      pc.t0 = start + static_cast<int>(((g0 > u0 ? g0 : u0) - u0) * 64);
+      pc.t1 = start + static_cast<int>(e < len ? e : static_cast<int64_t>(len));
       if (pc.t1 < pc.t0) pc.t1 = pc.t0;
-      pc.direct = g0 <= u0 && u1 <= g1;
+      // a sharer's output also has the shared pass's partials: never direct
+      pc.direct = g0 <= u0 && u1 <= g1 && start == 0;
       pc.slot = static_cast<size_t>(static_cast<int64_t>(b) * hkv + h + blockIdx.x);
       found = true;
     }
@@ -1256,23 +1267,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
 
 // Combines the partials of one (sequence, query head) spread over several
 // workgroups (a separate launch, so the partials written by the attention
-// kernel are visible without any cross-workgroup fence):
+// kernels are visible without any cross-workgroup fence):
 //   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
 //   lse = (M + log2 sum_s w_s) ln 2.
 // The partials of a (sequence, kv head) sit in consecutive slots: ring
 // splits at (b * Hkv + kv head) * num_splits + split; pool pieces at
 // u + w for the workgroups w whose share of granules meets the unit
-// (workgroups with an empty share own no piece and are skipped).  A unit
-// done by one workgroup wrote its output directly and is skipped; a pool
-// sequence of length 0 gets out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
+// (workgroups with an empty share own no piece and are skipped), then, for a
+// sequence the shared-prefix pass served, its prefix_chunks chunk partials
+// at shared_base + c * B * Hkv + u.  A unit done by one workgroup wrote its
+// output directly and is skipped; a pool sequence with nothing resident gets
+// out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
 // the partial rows are read by independent loads in flight together, and
 // slots with lse = -inf are dropped with selects.
 template <int PER>  // partial rows per thread held in registers
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
-  static_assert(kMaxSplits <= 512, "two slots per thread");
-  __shared__ float s_lse[kMaxSplits];
+  constexpr int kSlots = 1024;  // pool pieces (at most the grid) plus the shared chunks
+  static_assert(kMaxSplits + kPrefixChunks <= kSlots && kPoolGrid + kPrefixChunks <= kSlots,
+                "four slots per thread");
+  __shared__ float s_lse[kSlots];
   __shared__ float s_red_f[8];
   __shared__ float4 s_part[GROUPS][COLS];
   const size_t bh = blockIdx.x;
@@ -1285,8 +1300,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   const int col = threadIdx.x % COLS;
   const int grp = threadIdx.x / COLS;
 
-  int64_t first;  // slot of the first partial
-  int count;      // partials (consecutive slots)
+  int64_t first;  // slot of the first piece partial
+  int count;      // piece partials (consecutive slots)
+  int shared = 0; // chunk partials of the shared-prefix pass
   int64_t w0 = 0, nwg = 1, total = 0;
   if (!pool) {
     first = unit * p.num_splits;
@@ -1298,6 +1314,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
     const int64_t hkv = p.num_kv_heads;
     nwg = p.num_splits;
     const int64_t n = granules(p, b);
+    shared = shared_rows(p, b) > 0 ? p.prefix_chunks : 0;
     int64_t all = 0, pb = 0;
     for (int bb = threadIdx.x; bb < p.batch; bb += 256) {
       const int x = granules(p, bb);
@@ -1325,46 +1342,56 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
       first = unit + w0;
     }
   }
-  if (count == 1) return;  // written directly by the attention kernel
+  if (count == 1 && shared == 0) return;  // written directly by the attention kernel
+  const int slots = count + shared;
   auto present = [&](int k) {  // pool: the k-th workgroup of the run owns rows
-    if (!pool) return true;
+    if (!pool || k >= count) return true;
     const int64_t wk = w0 + k;
     const int64_t a = share_start(wk, total, nwg);
     const int64_t e = wk + 1 == nwg ? total : share_start(wk + 1, total, nwg);
     return a < e;
   };
+  auto slot_of = [&](int k) -> size_t {  // partial slot of the k-th partial
+    if (k < count) return static_cast<size_t>(first + k);
+    return static_cast<size_t>(p.shared_base) +
+           static_cast<size_t>(k - count) * p.batch * p.num_kv_heads + static_cast<size_t>(unit);
+  };
   const float* lse = p.ws_lse;
   const float4* po = reinterpret_cast<const float4*>(p.ws_o);
-  const size_t stride = static_cast<size_t>(g) * COLS;  // float4s between consecutive slots
-  const size_t at0 = (static_cast<size_t>(first) * g + h) * COLS + col;
+  auto at = [&](int k) { return (slot_of(k) * g + h) * COLS + col; };
   float4 v[PER];
   float lv[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int s = grp + GROUPS * k;
     lv[k] = kNegInf;
-    if (s < count && present(s)) {
-      v[k] = po[at0 + s * stride];
-      lv[k] = lse[(static_cast<size_t>(first) + s) * g + h];
+    if (s < slots && present(s)) {
+      v[k] = po[at(s)];
+      lv[k] = lse[slot_of(s) * g + h];
     }
   }
-  // Every slot's lse (thread t holds slots t and t + 256; count <= 512),
-  // then the maximum and the weight sum by block reductions.
-  float la = kNegInf, lb = kNegInf;
-  const int sa = threadIdx.x, sb = threadIdx.x + 256;
-  if (sa < count && present(sa)) la = lse[(static_cast<size_t>(first) + sa) * g + h];
-  if (sb < count && present(sb)) lb = lse[(static_cast<size_t>(first) + sb) * g + h];
-  if (sa < count) s_lse[sa] = la;
-  if (sb < count) s_lse[sb] = lb;
-  float mx = fmaxf(la, lb);
+  // Every slot's lse (thread t holds slots t + 256 i), then the maximum and
+  // the weight sum by block reductions.
+  float la[kSlots / 256];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < kSlots / 256; ++i) {
+    const int sa = threadIdx.x + 256 * i;
+    la[i] = kNegInf;
+    if (sa < slots && present(sa)) la[i] = lse[slot_of(sa) * g + h];
+    if (sa < slots) s_lse[sa] = la[i];
+    mx = fmaxf(mx, la[i]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((threadIdx.x & 63) == 0) s_red_f[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red_f[0], s_red_f[1]), fmaxf(s_red_f[2], s_red_f[3]));
   float wsum = 0.f;
-  if (mx != kNegInf)
-    wsum = (la == kNegInf ? 0.f : exp2f(la - mx)) + (lb == kNegInf ? 0.f : exp2f(lb - mx));
+  if (mx != kNegInf) {
+#pragma unroll
+    for (int i = 0; i < kSlots / 256; ++i) wsum += la[i] == kNegInf ? 0.f : exp2f(la[i] - mx);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   if ((threadIdx.x & 63) == 0) s_red_f[4 + (threadIdx.x >> 6)] = wsum;
@@ -1380,11 +1407,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
     acc.z += use ? w * v[k].z : 0.f;
     acc.w += use ? w * v[k].w : 0.f;
   }
-  for (int s = grp + GROUPS * PER; s < count; s += GROUPS) {  // beyond the registers
+  for (int s = grp + GROUPS * PER; s < slots; s += GROUPS) {  // beyond the registers
     const float l = s_lse[s];
     if (l == kNegInf || mx == kNegInf) continue;
     const float w = exp2f(l - mx);
-    const float4 t = po[at0 + s * stride];
+    const float4 t = po[at(s)];
     acc.x = fmaf(w, t.x, acc.x);
     acc.y = fmaf(w, t.y, acc.y);
     acc.z = fmaf(w, t.z, acc.z);
@@ -1463,11 +1490,18 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream) {
   // p.num_splits carries the size of the balanced grid: kPoolGrid 4-wave
   // workgroups, or half as many 8-wave ones for small pools
-  const unsigned grid = static_cast<unsigned>(p.num_splits);
+  DecodeParams p = p_in;
   hipError_t err;
+  if (prefix_pass_applies(p)) {  // finds and attends the shared prefix, writes the plan
+    err = launch_shared_prefix(p, stream);
+    if (err != hipSuccess) return err;
+  } else {
+    p.plan = nullptr;
+  }
+  const unsigned grid = static_cast<unsigned>(p.num_splits);
   if (p.i8)
     err = grid == static_cast<unsigned>(kPoolGrid) ? decode_pool_kernel_launch<4, true>(p, grid, stream)
                                                    : decode_pool_kernel_launch<8, true>(p, grid, stream);

@@ -130,6 +130,9 @@ void fill_workspace_ptrs(swa::DecodeParams& p, void* workspace,
   char* base = static_cast<char*>(workspace);
   p.ws_o = reinterpret_cast<float*>(base + lay.o_offset);
   p.ws_lse = reinterpret_cast<float*>(base + lay.lse_offset);
+  p.plan = reinterpret_cast<int32_t*>(base + lay.plan_offset);
+  p.shared_base = lay.shared_base;
+  p.prefix_chunks = swa::prefix_chunks(p.batch, p.num_q_heads, p.num_kv_heads);
 }
 
 // Split grid of a decode call.  The paged bf16 / head_dim 128 path runs a

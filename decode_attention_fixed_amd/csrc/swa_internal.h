@@ -28,6 +28,31 @@ constexpr int64_t kPoolSmallRows = 2048;
 constexpr int kMaxMfmaSplits = 512;             // ring splits per sequence on that path
 constexpr int64_t kMaxMfmaTokens = 512 * 8192;  // rows per sequence on that path
 
+// Shared-prefix pass of the paged decode (bf16 pools, head_dim 128, batch
+// 2 .. kPrefixMaxBatch): the leading blocks that sequences' tables share with
+// the longest sequence's table are attended once per kv head for all of them
+// (their query heads stacked as matrix-core columns), in kPrefixChunks key
+// chunks; the pool kernel then attends each sequence's remaining rows and
+// the merge adds the chunks' partials.  The plan the pass finds lives in the
+// workspace: plan[0] shared rows (0: nothing shared), plan[1] the reference
+// sequence, plan[2] sharers, plan[kPlanHead + b] rows of sequence b served by
+// the pass (0: not a sharer).
+constexpr int kPrefixChunks = 16;      // key chunks per kv head, at most
+constexpr int kPrefixCols = 128;       // query columns per workgroup of the pass
+constexpr int kPrefixMaxBatch = 1024;
+constexpr int kPrefixMaxRows = 16384;  // shared rows scanned for (more stay private)
+constexpr int kPlanHead = 4;
+// Key chunks per kv head: enough workgroups (kv heads x chunks x column
+// blocks) to cover the chip, at most kPrefixChunks.  The workspace sizing,
+// the pass and the merge all take it from here.
+inline int prefix_chunks(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads) {
+  const int64_t col_blocks =
+      (static_cast<int64_t>(batch) * (num_q_heads / num_kv_heads) + kPrefixCols - 1) / kPrefixCols;
+  const int64_t wgs = static_cast<int64_t>(num_kv_heads) * col_blocks;
+  const int64_t c = (256 + wgs - 1) / wgs;
+  return static_cast<int>(c < 1 ? 1 : (c > kPrefixChunks ? kPrefixChunks : c));
+}
+
 // RoPE frequencies theta_i = base^(-2i/d), i < d/2 (d <= 128), computed on
 // the host in float64 and passed by value to every kernel that rotates.
 constexpr int kMaxRopePairs = 64;
@@ -122,6 +147,12 @@ struct DecodeParams {
   int32_t shift_sinks;        // fused step: positions inside the cache (sinks scored
                               // against the query rotated at its cache position)
   RopeFreq freq;
+  // Paged pools: the shared-prefix plan in the workspace, or null when the
+  // pass does not run; partial slot of chunk c of unit u: shared_base + c *
+  // B * Hkv + u.
+  int32_t* plan;
+  int64_t shared_base;
+  int32_t prefix_chunks;      // prefix_chunks(batch, Hq, Hkv)
 };
 
 struct SplitPlan {
@@ -144,7 +175,9 @@ SplitPlan plan_splits_mfma(int32_t batch, int32_t num_kv_heads, int32_t max_kv_t
 struct WorkspaceLayout {
   size_t o_offset;
   size_t lse_offset;
-  size_t q_offset;  // [B, Hq, d] query copy of a fused step that runs as two launches
+  size_t q_offset;     // [B, Hq, d] query copy of a fused step that runs as two launches
+  size_t plan_offset;  // [kPlanHead + B] int32: the shared-prefix plan
+  int64_t shared_base; // first partial slot of the shared-prefix pass
   size_t total;
 };
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -160,6 +193,9 @@ hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream);
+// The shared-prefix pass (one launch; finds and writes the plan too).
+bool prefix_pass_applies(const DecodeParams& p);
+hipError_t launch_shared_prefix(const DecodeParams& p, hipStream_t stream);
 
 bool group_supported(int g);
 
