@@ -232,7 +232,7 @@ def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: boo
     import torch
 
     from decode_attention_fixed_amd import binding as B
-    from decode_attention_fixed_amd.workloads import PagedState, RingState, to_device
+    from tests.device_data import PagedState, RingState, to_device
     from synth import TENSOR_K, TENSOR_Q, TENSOR_V
     from synth.draws import draw_rows_parallel
 
@@ -302,7 +302,7 @@ def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: boo
     elif w.kind == "paged-append":
         import ctypes
 
-        from decode_attention_fixed_amd.workloads import build_paged_append
+        from tests.device_data import build_paged_append
         st = build_paged_append(w, extra_steps=total)
 
         def staged(tensor):
@@ -340,7 +340,7 @@ def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: boo
     elif w.kind == "pager":
         import dataclasses
 
-        from decode_attention_fixed_amd.workloads import PagerState
+        from tests.device_data import PagerState
         wl = dataclasses.replace(w, decode_steps=n_steps + 1)
         st = PagerState(wl)
         st.fill_host()

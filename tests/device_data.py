@@ -3,7 +3,8 @@
 Device memory is allocated with torch; every cache write goes through the
 library's own entry points (kv_append_rope for ring caches, kv_write_paged
 for pools), so a loaded workload is exactly what the decode path sees in use.
-Used by the GPU tests, the smoke check and the benchmark.
+Harness code (not part of the product package), used by the GPU tests, the
+smoke check and the benchmark.
 """
 
 from __future__ import annotations
@@ -15,7 +16,7 @@ from synth import (TENSOR_K, TENSOR_Q, TENSOR_V, PagedAppendWorkload, PagedWorkl
                    PagerWorkload, PoolWorkload, RingWorkload)
 from synth.draws import SHARED_SEQUENCE, draw_rows_parallel
 
-from . import binding as B
+from decode_attention_fixed_amd import binding as B
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 

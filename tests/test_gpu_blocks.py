@@ -52,7 +52,7 @@ def _dev(a, dtype="bf16"):
 
 
 def _state(num_blocks, bs, max_seqs, max_blocks, dtype="bf16"):
-    from decode_attention_fixed_amd.workloads import BlockPoolState
+    from tests.device_data import BlockPoolState
     st = BlockPoolState(num_blocks, bs, max_seqs, max_blocks, HQ, HKV, D, dtype)
     st.k_pool.fill_(float("nan"))
     st.v_pool.fill_(float("nan"))
@@ -239,7 +239,7 @@ def test_paged_append_full_size():
     """The paged workload (B = 32, lengths 1K-32K, a 2000-token prefix shared
     by reference) built through the manager, then decode steps that each
     append one token per sequence; sampled steps against the oracle."""
-    from decode_attention_fixed_amd.workloads import build_paged_append, to_device
+    from tests.device_data import build_paged_append, to_device
     w = workload("paged-append")
     steps = 6
     st = build_paged_append(w)

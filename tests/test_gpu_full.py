@@ -45,7 +45,7 @@ def _log(msg):
 
 @pytest.mark.parametrize("name", ["mha-ring", "gqa-ring"])
 def test_ring_workload_full(name):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = WORKLOADS[name]
     rng = np.random.default_rng(123)
     st = RingState(w)
@@ -97,7 +97,7 @@ def test_ring_workload_full(name):
 
 @pytest.mark.parametrize("name", ["mha-prefill", "gqa-prefill"])
 def test_prefill_workload_full(name):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = WORKLOADS[name]
     rng = np.random.default_rng(77)
     st = RingState(w)
@@ -130,7 +130,7 @@ def test_prefill_workload_full(name):
 
 @pytest.mark.parametrize("name", ["paged", "long-pool-b1", "long-pool-b16"])
 def test_paged_workload_full(name):
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     w = WORKLOADS[name]
     rng = np.random.default_rng(321)
     st = PagedState(w)

@@ -35,7 +35,7 @@ def _ring(**kw):
 
 
 def _twins(w):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     a, b = RingState(w), RingState(w)
     for st in (a, b):
         st.cache.k.zero_()   # slots never written hold the same bytes in both
@@ -97,7 +97,7 @@ def test_ring_step_replays(kw, fused):
 @pytest.mark.parametrize("cache", ["", "i8"])
 def test_pool_decode_replays(cache):
     from decode_attention_fixed_amd import binding as B
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     w = PoolWorkload(name="gp", seed=62, batch=2, num_q_heads=6, num_kv_heads=1, head_dim=128,
                      dtype="bf16", block_size=64, logical_blocks=64, pool_slots=20,
                      rope_base=10000.0, scale=0.5, decode_steps=REPLAYS, cache=cache)
@@ -130,7 +130,7 @@ def test_prefill_replays():
     once and replayed on successive chunks, positions moved on by the chunk
     length inside the graph."""
     from decode_attention_fixed_amd import binding as B
-    from decode_attention_fixed_amd.workloads import to_device
+    from tests.device_data import to_device
     T = 32
     w = _ring(history="chunks:64:4", window=160)
     eager, graphed = _twins(w)

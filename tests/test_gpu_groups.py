@@ -55,7 +55,7 @@ def _ring(hq, hkv, cache, **kw):
 @pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "fused"])
 @pytest.mark.parametrize("shape", ["wrapped", "splits"])
 def test_ring_groups(cache, heads, fused, shape):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     hq, hkv = heads
     kw = {} if shape == "wrapped" else dict(batch=1, window=20000, history="prefill:25000",
                                            decode_steps=3)
@@ -88,7 +88,7 @@ def test_fused_step_bit_identical_groups(cache, heads):
     to float32 rounding (g = 3 on int8: P*V weights in fp16, the new token
     added in float32 at the merge: 1e-3)."""
     from decode_attention_fixed_amd import binding as B
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     hq, hkv = heads
     w = _ring(hq, hkv, cache, decode_steps=6)
     a, b = RingState(w), RingState(w)
@@ -117,7 +117,7 @@ def test_fused_step_bit_identical_groups(cache, heads):
 
 
 def _poisoned_state(w):
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     st = PagedState(w)
     if getattr(w, "cache", "") == "i8":
         st.k_pool.fill_(255)   # codes -1, scales NaN

@@ -89,7 +89,7 @@ def _check_ring_rows(st, w, style="interleaved"):
 ])
 @pytest.mark.parametrize("fused", [False, True])
 def test_ring_i8(kw, fused):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _ring(**kw)
     st = RingState(w)
     try:
@@ -117,7 +117,7 @@ def test_ring_i8_half_pairs(fused):
     """RoPE pairs (i, i + d/2) on an int8 ring: the append's and the fused
     step's quantisation of the rotated K (rows checked against the oracle's),
     and the outputs."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _ring(seed=89, num_q_heads=16, num_kv_heads=4)
     st = RingState(w, rope_style="half")
     try:
@@ -136,7 +136,7 @@ def test_ring_i8_half_pairs(fused):
 
 
 def _pool_state(w):
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     st = PagedState(w)
     st.k_pool.fill_(255)   # codes -1, scales NaN: never to be read
     st.v_pool.fill_(255)
@@ -198,7 +198,7 @@ def test_pool_i8_full_size(name):
 def test_mha_ring_i8_full_size():
     """The int8 MHA ring workload (B = 8, W = 4096 + 4 sinks, history wrapped
     twice) at full size: decode steps 0 and 1 through decode_step_ring."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = workload("mha-ring-i8")
     st = RingState(w)
     try:

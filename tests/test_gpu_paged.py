@@ -49,7 +49,7 @@ def _pool(**kw):
 
 
 def _state(w, poison=True):
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     st = PagedState(w)
     if poison:  # rows nobody writes hold NaN: they must never reach the arithmetic
         st.k_pool.fill_(float("nan"))

@@ -43,7 +43,7 @@ def _pager(**kw):
 
 
 def _state(w):
-    from decode_attention_fixed_amd.workloads import PagerState
+    from tests.device_data import PagerState
     st = PagerState(w)
     st.k_pool.fill_(float("nan"))
     st.v_pool.fill_(float("nan"))

@@ -40,7 +40,7 @@ def _log(msg):
 
 
 def _pair(w):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     a, b = RingState(w), RingState(w)
     for st in (a, b):
         st.cache.k.zero_()
@@ -100,7 +100,7 @@ def test_prefill_negative_positions_and_empty_cache():
     """A chunk starting at position -3 on an empty cache: rows at negative
     positions give out = 0, lse = -inf; the others attend the chunk's tokens
     from position 0 up to their own (and nothing else)."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _W(num_q_heads=8, num_kv_heads=2, window=16, sinks=2, batch=1, history="prefill:0")
     st = RingState(w)
     try:
@@ -136,7 +136,7 @@ def test_prefill_negative_positions_and_empty_cache():
 def test_prefill_chunks_continue_the_ring():
     """Two chunks in a row (the second attends the first through the ring),
     sampled rows against the oracle."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _W(num_q_heads=16, num_kv_heads=4, window=200, history="chunks:64:2", decode_steps=160)
     st = RingState(w)
     try:

@@ -59,7 +59,7 @@ def check_cache_rows(state, b: int, table: np.ndarray, style: str = "interleaved
 
 
 def run_and_check(w: RingWorkload, steps, style="interleaved", check_every_append=False):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     st = RingState(w, rope_style=style)
     try:
         def after(first, n):
@@ -146,7 +146,7 @@ def test_half_rope_style():
 
 
 def _fresh(w):
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     return RingState(w)
 
 

@@ -40,7 +40,7 @@ def _W(**kw):
 def _pair(w):
     """A shifted state and an unshifted twin of the same workload."""
     import dataclasses
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     a = RingState(w)
     b = RingState(dataclasses.replace(w, positions=""))
     a.prefill()
@@ -106,7 +106,7 @@ def test_shifted_equals_unshifted_when_nothing_moves(kw):
 
 def test_shifted_unsupported_on_float32():
     from decode_attention_fixed_amd.binding import SWA_ERR_UNSUPPORTED, SwaError
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _W(dtype="f32", head_dim=64, num_q_heads=4, num_kv_heads=4)
     st = RingState(w)
     try:
@@ -120,7 +120,7 @@ def test_shifted_unsupported_on_float32():
 
 def test_shifted_full_size():
     """mha-ring with shifting: B = 8, W = 4096 + 4 sinks, steps 0 and 1."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = workload("mha-ring-shift")
     st = RingState(w)
     try:

@@ -57,7 +57,7 @@ def _fused_step(st, inp):
 def _pair(w):
     """Two caches with the same history; rows never written hold the same
     (zero) bytes in both, so whole caches can be compared."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     a, b = RingState(w), RingState(w)
     for st in (a, b):
         st.cache.k.zero_()
@@ -176,7 +176,7 @@ def test_fused_step_negative_position():
 ])
 def test_fused_step_oracle(kw):
     """Decode steps run through decode_step_ring only, against the oracle."""
-    from decode_attention_fixed_amd.workloads import RingState
+    from tests.device_data import RingState
     w = _W(**kw)
     st = RingState(w)
     try:

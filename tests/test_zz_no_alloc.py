@@ -28,7 +28,7 @@ def _gpu():
 
 
 def _state(w):
-    from decode_attention_fixed_amd.workloads import PagedState
+    from tests.device_data import PagedState
     st = PagedState(w)
     st.k_pool.fill_(float("nan"))
     st.v_pool.fill_(float("nan"))
