@@ -84,7 +84,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 _CSRC = os.path.join(ROOT, "decode_attention_fixed_amd", "csrc")
-DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "decode.hip", "device_common.h")]
+DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "decode_shared.hip", "decode.hip",
+                                                "device_common.h")]
 PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill.hip", "append_rope.hip",
                                                  "device_common.h")]
 DEFAULT_WORKLOAD = "paged"
@@ -646,6 +647,33 @@ def copy_calibration(nbytes: int = 1 << 30) -> None:
                       "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def read_ceiling(nbytes: int = 4 << 30, reps: int = 20) -> dict:
+    """The HBM read rate the chip achieves: swa_stream_read (nontemporal
+    16-byte loads, 2048 workgroups, nothing written but one word per wave)
+    over a buffer far larger than the caches, timed with HIP events on its
+    own stream."""
+    import torch
+    from decode_attention_fixed_amd import binding as B
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        sink = torch.empty(B.STREAM_READ_SINK_BYTES, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            B.stream_read(x, sink, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            B.stream_read(x, sink, stream)
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+    del x, sink
+    torch.cuda.empty_cache()
+    return {"read_gbs": round(nbytes / ms / 1e6, 1), "bytes": nbytes, "reps": reps,
+            "kernel": "swa_stream_read"}
+
+
 # ---------------------------------------------------------------------------
 # the JSON line
 # ---------------------------------------------------------------------------
@@ -685,7 +713,7 @@ def decode_numbers(w, steps: int, res: dict) -> dict:
             "call_us": res["decode_ms_mean"] * 1e3}
 
 
-def per_config_entry(name: str, args) -> dict:
+def per_config_entry(name: str, args, ceiling_gbs: float | None = None) -> dict:
     from synth import WORKLOADS
     w = WORKLOADS[name]
     res = measure(w, args.steps, args.warmup)
@@ -695,6 +723,8 @@ def per_config_entry(name: str, args) -> dict:
             "ms_per_step": round(n["ms_per_step"], 5), "gbs": round(n["value"], 1),
             "call_us": round(n["call_us"], 2), "call_gbs": round(n["achieved"], 1),
             "frac": round(n["achieved"] / HBM_PEAK_GBS, 4),
+            "frac_of_read_ceiling": (round(n["achieved"] / ceiling_gbs, 4)
+                                     if ceiling_gbs else None),
             "profile_call_us": prof,
             "profile_frac": (round(res["kv_bytes_call"] / (prof * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                              if prof else None),
@@ -711,6 +741,9 @@ def main() -> int:
     ap.add_argument("--no-per-config", action="store_true",
                     help="measure the named workload only (the profiling runs use this)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="print only the streaming HBM read rate (swa_stream_read)")
+    ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring caches: kv_append_rope + decode_attn_ring per step instead of "
                          "decode_step_ring")
@@ -731,6 +764,9 @@ def main() -> int:
 
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.read_ceiling:
+        print(json.dumps(read_ceiling()), flush=True)
         return 0
 
     from synth import WORKLOADS
@@ -786,10 +822,17 @@ def main() -> int:
                      "no_swap_ms_per_step is the same decode on the same pool without "
                      "paging"),
         }
+    ceiling = None
+    if not args.no_read_ceiling:
+        ceiling = read_ceiling()
+        roofline["read_ceiling_gbs"] = ceiling["read_gbs"]
+        roofline["frac_of_read_ceiling"] = round(n["achieved"] / ceiling["read_gbs"], 4)
+        log(f"streaming read ceiling {ceiling['read_gbs']} GB/s")
     if not args.no_per_config and w.name == DEFAULT_WORKLOAD and not args.graph:
         out["per_config"] = []
         for name in PER_CONFIG:
-            out["per_config"].append(per_config_entry(name, args))
+            out["per_config"].append(per_config_entry(name, args,
+                                                      ceiling["read_gbs"] if ceiling else None))
             log(f"per-config {name}: {out['per_config'][-1]['call_gbs']} GB/s per call")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -77,6 +77,7 @@ _PROTOS = {
     "decode_step_ring_shifted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp,
                                                 _i32, _vp, _vp, ctypes.c_size_t, _vp]),
     "swa_pos_advance": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "swa_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]),
     "prefill_attn_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "prefill_attn_ring": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
@@ -361,6 +362,19 @@ def pos_advance(pos: torch.Tensor, delta: int = 1, stream=None) -> None:
     graph of decode steps replay at advancing positions."""
     _check("swa_pos_advance",
            LIB.swa_pos_advance(_ptr(pos, "pos", torch.int32), pos.numel(), delta,
+                               _stream(stream)))
+
+
+STREAM_READ_SINK_BYTES = 32768
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Reads all of src (device, contiguous, a multiple of 16 bytes) once:
+    the measuring aid for the achievable HBM read rate."""
+    _expect_bytes(sink, "sink", STREAM_READ_SINK_BYTES)
+    _check("swa_stream_read",
+           LIB.swa_stream_read(_ptr(src, "src"), src.numel() * src.element_size(),
+                               _ptr(sink, "sink"), sink.numel() * sink.element_size(),
                                _stream(stream)))
 
 

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libswa.so")
 
 SOURCES = ["swa_api.cpp", "pager_api.cpp", "blocks_api.cpp", "append_rope.hip", "decode.hip", "decode_mfma.hip", "decode_shared.hip",
-           "prefill.hip", "pager.hip", "positions.hip"]
+           "prefill.hip", "pager.hip", "positions.hip", "stream_read.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

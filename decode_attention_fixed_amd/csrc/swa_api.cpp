@@ -414,6 +414,21 @@ swa_status swa_pos_advance(int32_t* pos, int32_t n, int32_t delta, void* stream)
                   "swa_pos_advance");
 }
 
+swa_status swa_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes,
+                           void* stream) {
+  static_assert(SWA_STREAM_READ_SINK_BYTES == swa::kStreamReadSinkBytes, "sink size");
+  if (bytes % 16 != 0) return fail(SWA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (src == nullptr || sink == nullptr) return fail(SWA_ERR_INVALID_ARG, "src or sink is NULL");
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(SWA_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
+  if (sink_bytes < SWA_STREAM_READ_SINK_BYTES)
+    return fail(SWA_ERR_INVALID_ARG, "sink needs %zu bytes", SWA_STREAM_READ_SINK_BYTES);
+  return from_hip(swa::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink),
+                                          static_cast<hipStream_t>(stream)),
+                  "swa_stream_read");
+}
+
 swa_status prefill_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t n_tokens, size_t* bytes) {
   if (bytes == nullptr) return fail(SWA_ERR_INVALID_ARG, "bytes is NULL");

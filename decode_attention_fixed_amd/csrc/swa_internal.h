@@ -185,6 +185,11 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num
 
 hipError_t launch_fill_i32(int32_t* dst, size_t n, int32_t value, hipStream_t stream);
 hipError_t launch_add_i32(int32_t* dst, size_t n, int32_t delta, hipStream_t stream);
+// Reads bytes (a multiple of 16, 16-byte aligned) of src once; one XOR word
+// per wave of the kStreamReadGrid workgroups to sink.
+constexpr int kStreamReadGrid = 2048;
+constexpr size_t kStreamReadSinkBytes = 32768;
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_append_rope(const AppendParams& p, hipStream_t stream);
 hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream);
 hipError_t launch_write_paged_i8(const PagedWriteParams& p, hipStream_t stream);

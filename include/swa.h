@@ -218,6 +218,19 @@ swa_status decode_step_ring_shifted(swa_cache* cache, const void* k_new, const v
  * nothing). */
 swa_status swa_pos_advance(int32_t* pos, int32_t n, int32_t delta, void* stream);
 
+/* Library helper (no page defines it): reads `bytes` of device memory at
+ * `src` once, with nontemporal 16-byte loads spread over 2048 workgroups, on
+ * `stream`; it measures the HBM read rate the chip achieves, the practical
+ * ceiling for the decode kernels.  bytes: a multiple of 16 (0 launches
+ * nothing); src: 16-byte aligned device memory the caller owns; sink:
+ * device memory of at least SWA_STREAM_READ_SINK_BYTES, 4-byte aligned,
+ * which receives a checksum per wave (its contents mean nothing else).
+ * SWA_ERR_INVALID_ARG for NULL pointers, misalignment, a size that is not a
+ * multiple of 16 or a sink that is too small. */
+#define SWA_STREAM_READ_SINK_BYTES ((size_t)32768)
+swa_status swa_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes,
+                           void* stream);
+
 /* Library helper (no page defines it): workspace (device bytes) of a
  * prefill_attn_ring call with n_tokens tokens per sequence.  Needs no
  * initialisation. */

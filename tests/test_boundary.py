@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     declared = _declared_functions()
-    assert len(declared) == 31, declared
+    assert len(declared) == 32, declared
     assert sorted(B.EXPORTED) == declared
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
@@ -159,6 +159,18 @@ def test_decode_ring_validation():
             B.SWA_ERR_INVALID_ARG
     finally:
         B.swa_cache_destroy(h)
+
+
+def test_stream_read_validation():
+    L = B.LIB
+    sink = B.STREAM_READ_SINK_BYTES
+    assert L.swa_stream_read(FAKE, 0, None, 0, None) == B.SWA_OK          # nothing to read
+    assert L.swa_stream_read(FAKE, 24, FAKE, sink, None) == B.SWA_ERR_INVALID_ARG  # not 16-byte units
+    assert L.swa_stream_read(None, 32, FAKE, sink, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_stream_read(FAKE, 32, None, sink, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_stream_read(FAKE + 8, 32, FAKE, sink, None) == B.SWA_ERR_INVALID_ARG  # misaligned
+    assert L.swa_stream_read(FAKE, 32, FAKE + 2, sink, None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_stream_read(FAKE, 32, FAKE, sink - 4, None) == B.SWA_ERR_INVALID_ARG
 
 
 def test_pos_advance_validation():
