@@ -46,12 +46,14 @@ TFLOP/s of useful attention arithmetic (4 x d flops per visible (query head,
 key) pair: S = Q K^T and O = P V) against the 2.5 PFLOP/s dense bf16 / fp16
 MFMA peak; `roofline` times the whole call (its three launches).
 
-Host-pool paging workload (long-pool-swap): a step is swa_pager_advance for
-the next step's block request (LRU decisions on the host, a validity launch
-on the attention stream, the block copies from pinned host memory) and the
-decode over the pool; `value` counts the blocks each decode actually saw.
-`swap` reports the blocks and bytes copied per step, and the same steps
-without paging on the same pool.
+Host-pool paging workload (long-pool-swap): a step is swa_pager_stage for
+the next step's block request (LRU decisions on the host) and
+swa_pager_decode, whose launches attend the pool as the step found it and
+then copy the staged blocks from pinned host memory into the slots they
+evict (--pager-mode advance: swa_pager_advance, its copies before the decode,
+which does not attend the slots they fill); `value` counts the blocks each
+decode actually saw. `swap` reports the blocks and bytes copied per step, and
+the same steps without paging on the same pool.
 
 Paged pool grown by appends (paged-append): a step is kv_append_paged of one
 token per sequence through the block manager (table and length updates, the
@@ -227,7 +229,8 @@ class Run:
         self.step, self.call, self.closers = [], [], []
 
 
-def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: bool = True) -> Run:
+def setup(w, n_steps: int, n_calls: int, unfused: bool = False,
+          pager_mode: str = "fused") -> Run:
     """Stages inputs for n_steps steps and n_calls roofline calls."""
     import numpy as np
     import torch
@@ -357,9 +360,10 @@ def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: boo
         decs = [B.decode_attn_paged(st.desc, qs[j], st.k_pool, st.v_pool, st.block_table,
                                     st.seq_lens, st.block_valid, st.out, st.workspace, st.lse,
                                     prepare=True) for j in range(qs.shape[0])]
-        cs = None if same_stream else copy_stream
+        cs = copy_stream if pager_mode == "advance-side-stream" else None
 
-        def step(i):
+        def advance_step(i):
+            # the loads land before the attention: their slots are invalid for it
             def f():
                 t = time.perf_counter()
                 n = st.advance(reqs[i], cs)
@@ -370,6 +374,29 @@ def setup(w, n_steps: int, n_calls: int, unfused: bool = False, same_stream: boo
                 decs[i % len(decs)]()
                 host_us["decode"] += (time.perf_counter() - t) * 1e6
             return f
+
+        fused = [st.fused_decode(qs[j], prepare=True) for j in range(qs.shape[0])]
+
+        def fused_step(i):
+            # the attention reads the pool as the step found it; the loads
+            # for the next step are copied in the same launches, after it
+            def f():
+                t = time.perf_counter()
+                n = st.stage(reqs[i])
+                host_us["stage"] += (time.perf_counter() - t) * 1e6
+                loaded[i] = n
+                seen[i] = filled
+                t = time.perf_counter()
+                fused[i % len(fused)]()
+                host_us["decode"] += (time.perf_counter() - t) * 1e6
+            return f
+        if pager_mode == "fused":
+            # every slot is filled after the warm-up, so each load evicts and
+            # the attention of every step sees all of them
+            if filled != w.batch * w.pool_slots:
+                raise RuntimeError(f"{w.name}: pool not full after the warm-up")
+            host_us = {"stage": 0.0, "decode": 0.0}
+        step = fused_step if pager_mode == "fused" else advance_step
         run.step = [step(i) for i in range(n_steps)]
         run.extra.update(pager_state=st, pager_seen=seen, pager_loaded=loaded,
                          pager_host_us=host_us, pager_decs=decs, pager_q=qs,
@@ -424,7 +451,7 @@ def time_region(fns, graph: bool = False) -> float:
     return begin.elapsed_time(end)
 
 
-def measure(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool = True,
+def measure(w, steps: int, warmup: int, unfused: bool = False, pager_mode: str = "fused",
             graph: bool = False) -> dict:
     """Sets the workload up and times it, everything on one stream of its own
     (the marshalled calls carry that stream; a graph is captured on it)."""
@@ -432,16 +459,16 @@ def measure(w, steps: int, warmup: int, unfused: bool = False, same_stream: bool
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        return _measure(w, steps, warmup, unfused, same_stream, graph)
+        return _measure(w, steps, warmup, unfused, pager_mode, graph)
 
 
-def _measure(w, steps, warmup, unfused, same_stream, graph) -> dict:
+def _measure(w, steps, warmup, unfused, pager_mode, graph) -> dict:
     import torch
     t0 = time.time()
     # the pager and the block manager keep host state per step: no roofline
     # region of extra steps for them (their region 2 repeats the decode)
     n_calls = 0 if w.kind in ("pager",) else max(steps, MIN_CALLS)
-    run = setup(w, warmup + steps, n_calls, unfused, same_stream)
+    run = setup(w, warmup + steps, n_calls, unfused, pager_mode)
     log(f"{w.name}: setup {time.time() - t0:.1f} s")
     try:
         for i in range(warmup):
@@ -751,9 +778,13 @@ def main() -> int:
                     help="issue the timed steps as one captured HIP graph (ring caches and "
                          "read-only pools; the pager and the block manager run host logic "
                          "every step)")
-    ap.add_argument("--copy-stream", action="store_true",
-                    help="long-pool-swap: run the block copies on a stream of their own, "
-                         "overlapping the attention (default: on the attention stream)")
+    ap.add_argument("--pager-mode", choices=("fused", "advance", "advance-side-stream"),
+                    default="fused",
+                    help="long-pool-swap: 'fused' stages the next step's loads and copies "
+                         "them in the decode's own launches, after the attention read the "
+                         "pool (swa_pager_stage + swa_pager_decode); 'advance' copies them "
+                         "before the decode on the attention stream (swa_pager_advance); "
+                         "'advance-side-stream' does so on a stream of its own")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -775,7 +806,7 @@ def main() -> int:
         print(f"--graph: workload {w.name} runs host logic every step and is not captured",
               file=sys.stderr)
         return 2
-    res = measure(w, args.steps, args.warmup, args.unfused, not args.copy_stream, args.graph)
+    res = measure(w, args.steps, args.warmup, args.unfused, args.pager_mode, args.graph)
     if w.kind == "ring" and w.chunk:
         out = prefill_line(w, args, res)
         if not args.no_cpu_baseline:
@@ -817,10 +848,14 @@ def main() -> int:
             "no_swap_ms_per_step": round(res["no_swap_ms"], 5),
             "host_us_per_step": res["host_us_per_step"],
             "wall_ms_per_step": round(res["wall_s"] * 1e3 / args.steps, 5),
-            "copies_on": "a stream of their own" if args.copy_stream else "the attention stream",
-            "note": ("copies from pinned host memory by one kernel launch per step; "
-                     "no_swap_ms_per_step is the same decode on the same pool without "
-                     "paging"),
+            "mode": args.pager_mode,
+            "copies_on": {"fused": "extra workgroups of the decode's merge launch",
+                          "advance": "a launch of their own before the decode, on the "
+                                     "attention stream",
+                          "advance-side-stream": "a launch of their own on a stream of "
+                                                 "its own"}[args.pager_mode],
+            "note": ("copies from pinned host memory; no_swap_ms_per_step is the same "
+                     "decode on the same pool without paging"),
         }
     ceiling = None
     if not args.no_read_ceiling:

@@ -105,6 +105,10 @@ _PROTOS = {
     "swa_pager_reset": (ctypes.c_int, [_vp, _vp]),
     "swa_pager_advance": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i32)]),
     "swa_pager_commit": (ctypes.c_int, [_vp, _vp]),
+    "swa_pager_stage": (ctypes.c_int, [_vp, _vp, _vp, ctypes.POINTER(_i32)]),
+    "swa_pager_decode": (ctypes.c_int, [_vp, _vp, _i32, _vp, ctypes.c_float, _vp, _i32, _vp, _vp,
+                                        ctypes.c_size_t, _vp]),
+    "swa_pager_workspace_bytes": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "swa_pager_slot_blocks": (ctypes.c_int, [_vp, _i32, _vp]),
     "swa_pager_destroy": (None, [_vp]),
     "swa_last_error": (ctypes.c_char_p, []),
@@ -703,6 +707,42 @@ def swa_pager_advance(handle: int, requests, stream=None, copy_stream=None) -> i
 
 def swa_pager_commit(handle: int, stream=None) -> None:
     _check("swa_pager_commit", LIB.swa_pager_commit(handle, _stream(stream)))
+
+
+def swa_pager_stage(handle: int, requests) -> int:
+    """The LRU decisions of swa_pager_advance for the next step's requests,
+    with the copies left to the next swa_pager_decode.  Returns the number
+    of blocks staged."""
+    off, blocks = requests if isinstance(requests, tuple) else pack_requests(requests)
+    n = _i32()
+    _check("swa_pager_stage", LIB.swa_pager_stage(handle, ctypes.cast(off, _vp),
+                                                  ctypes.cast(blocks, _vp), ctypes.byref(n)))
+    return n.value
+
+
+def swa_pager_decode(handle: int, desc: SwaPagedDesc, q: torch.Tensor, k_pool: torch.Tensor,
+                     v_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                     block_valid: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     lse: torch.Tensor | None = None, scale: float = 0.0, stream=None,
+                     prepare: bool = False):
+    """decode_attn_paged over the pager's pool, then the staged copies in the
+    same launches.  desc and the pool tensors are the ones the pager was made
+    with (their extents are checked here; the library uses its own pointers).
+    prepare=True: return the call marshalled once instead of making it."""
+    _check_paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, lse)
+    args = (handle, _ptr(q, "q"), desc.num_q_heads, _ptr(seq_lens, "seq_lens", torch.int32),
+            scale, _ptr(out, "out"), _DTYPE_CODE[out.dtype], _ptr(lse, "lse", torch.float32),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    keep = (desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, out, workspace, lse)
+    return _invoke("swa_pager_decode", args, keep, prepare)
+
+
+def swa_pager_workspace_bytes(handle: int, num_q_heads: int) -> int:
+    n = ctypes.c_size_t()
+    _check("swa_pager_workspace_bytes",
+           LIB.swa_pager_workspace_bytes(handle, num_q_heads, ctypes.byref(n)))
+    return n.value
 
 
 def swa_pager_slot_blocks(handle: int, seq: int, slots_per_seq: int) -> list:

@@ -25,6 +25,7 @@
 // score is replaced by -inf and their V by 0 with selects, so NaN garbage in
 // an empty slot cannot leak ([pool] "absent blocks are as if they did not
 // exist").
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -490,9 +491,30 @@ hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream) {
   return launch_decode<RingAddr>(p, stream);
 }
 
-hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  if (use_mfma_path(p.bf16 || p.i8, p.head_dim)) return launch_decode_mfma_pool(p, stream);
-  return launch_decode<PoolAddr>(p, stream);
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream, const PagerFuse* fuse) {
+  if (use_mfma_path(p.bf16 || p.i8, p.head_dim)) return launch_decode_mfma_pool(p, stream, fuse);
+  hipError_t err = launch_decode<PoolAddr>(p, stream);
+  if (err != hipSuccess || fuse == nullptr || fuse->n == 0) return err;
+  // this path's merge takes no copies: the paging step's launches follow it
+  PagerCopyParams c{};
+  c.host_k = fuse->host_k;
+  c.host_v = fuse->host_v;
+  c.k_pool = fuse->k_pool;
+  c.v_pool = fuse->v_pool;
+  c.block_u4 = fuse->block_u4;
+  c.piece_u4 = std::min(fuse->block_u4, kPagerCopyPieceU4);
+  c.pieces = (c.block_u4 + c.piece_u4 - 1) / c.piece_u4;
+  c.n = fuse->n;
+  PagerValidParams v{};
+  v.valid = fuse->valid;
+  v.n = fuse->n;
+  for (int i = 0; i < fuse->n; ++i) {
+    c.src_block[i] = fuse->src_block[i];
+    c.dst_block[i] = fuse->dst_block[i];
+    v.entries[i] = fuse->slot[i];
+  }
+  err = launch_pager_copy(c, stream);
+  return err != hipSuccess ? err : launch_pager_valid(v, stream);
 }
 
 }  // namespace swa

@@ -60,6 +60,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "pager_copy.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -1025,10 +1026,33 @@ __global__ __launch_bounds__(NW * 64) void decode_ring_kernel(DecodeParams p) {
   }
 }
 
+// A paging step folded into a pool decode (PagerFuse), split by launch: the
+// attention launch fetches the staged blocks from the host store into the
+// staging area, the merge launch places them in the pool.
+constexpr unsigned kFetchCus = 8;  // one per XCD
+struct PoolFetch {
+  const void* host_k;
+  const void* host_v;
+  void* stage_k;
+  void* stage_v;
+  int32_t block_u4, n;
+  int32_t src_block[kPagerFuseMax];
+};
+struct PoolPlace {
+  const void* stage_k;
+  const void* stage_v;
+  void* k_pool;
+  void* v_pool;
+  uint8_t* valid;
+  int32_t block_u4, n;
+  int32_t dst_block[kPagerFuseMax];
+  int32_t slot[kPagerFuseMax];
+};
+
 // Balanced schedule of a paged pool, in granules of 64 rows.  Sequence b
 // contributes Hkv ranges of n_b = ceil(len_b / 64) granules (one per kv head,
 // heads laid end to end), sequences in order; the total is
-// T = Hkv * sum_b n_b.  Workgroup w of W (a power of two) owns granules
+// T = Hkv * sum_b n_b.  Workgroup w of W (see share_start) owns granules
 // [s(w), s(w+1)) with s(w) = floor(w T / W).  The piece of unit
 // u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
 // granule order move u or w forward by one each, so the slots are distinct
@@ -1043,9 +1067,12 @@ __device__ __forceinline__ int granules(const DecodeParams& p, int b) {
   return (PoolRows::tokens(p, b) - shared_rows(p, b) + 63) >> 6;
 }
 
-// W is a power of two (the host launches kPoolGrid or kPoolGrid / 2): the
-// share boundaries need no 64-bit division.
+// W is kPoolGrid or kPoolGrid / 2, a power of two (no 64-bit division), or
+// that less the workgroups of kFetchCus CUs in a call with a folded paging
+// step.
 __device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg) {
+  if ((nwg & (nwg - 1)) != 0)
+    return static_cast<int64_t>(static_cast<uint64_t>(w * total) / static_cast<uint64_t>(nwg));
   const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg));
   return (w * total) >> shift;
 }
@@ -1217,15 +1244,32 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 }
 
 // 8 / NW workgroups per CU (two 4-wave or one 8-wave): two waves per SIMD, at
-// most 256 registers per lane.
+// most 256 registers per lane.  The balanced grid is the first p.num_splits
+// workgroups; those past it fetch the staged blocks of a folded paging step
+// (f.n > 0) from the host store into the staging area, over the bus, while
+// the attention workgroups read the pool.  They take CUs of their own: a CU
+// holding an attention workgroup has no room for another.
 template <int G, int NW, bool I8>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p,
+                                                                        PoolFetch f) {
   constexpr int NT = NW * 64;
   __shared__ Smem<G, NW, subtiles<G, true, I8>(), I8 ? 8 : 16> sm;
   __shared__ SeqChunk<NT> sc;
   const int64_t hkv = p.num_kv_heads;
-  const int64_t nwg = gridDim.x;
+  const int64_t nwg = p.num_splits;
   const int64_t w = blockIdx.x;
+  if (w >= nwg) {  // fetch workgroup w - nwg of gridDim.x - nwg takes every such piece
+    const int pieces = f.n * 2 * copy_pieces(f.block_u4, NT);
+    for (int j = static_cast<int>(w - nwg); j < pieces; j += static_cast<int>(gridDim.x - nwg)) {
+      const CopyPiece c = copy_piece(j, f.block_u4, NT);
+      const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.host_k : f.host_v) +
+                         static_cast<size_t>(f.src_block[c.item]) * f.block_u4;
+      uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
+                   static_cast<size_t>(c.item) * f.block_u4;
+      copy_block_piece(src, dst, c.begin, c.end, NT);
+    }
+    return;
+  }
 
   // Total granules: the first chunk's sum, plus a strided sum over the
   // sequences past it when the batch is larger than the workgroup.
@@ -1280,8 +1324,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
 // out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
 // the partial rows are read by independent loads in flight together, and
 // slots with lse = -inf are dropped with selects.
+// The place part of a paging step folded into the call (f.n > 0) runs here
+// too: f.n * 2 * copy_pieces(block_u4, 256) workgroups after the B * Hq merge
+// workgroups move its blocks from the staging area into the pool and set
+// their validity bytes.
+// The attention kernel that read the pool has finished when this launch
+// starts, and nothing in this launch reads the pool or the validity bytes,
+// so the moves overlap the merge and are visible to the launches after it.
 template <int PER>  // partial rows per thread held in registers
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, PoolPlace f) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
   constexpr int kSlots = 1024;  // pool pieces (at most the grid) plus the shared chunks
@@ -1290,6 +1341,17 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
   __shared__ float s_lse[kSlots];
   __shared__ float s_red_f[8];
   __shared__ float4 s_part[GROUPS][COLS];
+  const size_t heads = static_cast<size_t>(p.batch) * p.num_q_heads;
+  if (blockIdx.x >= heads) {
+    const CopyPiece c = copy_piece(static_cast<int>(blockIdx.x - heads), f.block_u4, 256);
+    const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
+                       static_cast<size_t>(c.item) * f.block_u4;
+    uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.k_pool : f.v_pool) +
+                 static_cast<size_t>(f.dst_block[c.item]) * f.block_u4;
+    copy_block_piece(src, dst, c.begin, c.end, 256);
+    if (c.tensor == 0 && c.begin == 0 && threadIdx.x == 0) f.valid[f.slot[c.item]] = 1;
+    return;
+  }
   const size_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / p.num_q_heads);
   const int hq = static_cast<int>(bh - static_cast<size_t>(b) * p.num_q_heads);
@@ -1443,14 +1505,18 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
 }
 
 template <int NW, bool I8>
-hipError_t decode_pool_kernel_launch(const DecodeParams& p, unsigned grid, hipStream_t stream) {
+hipError_t decode_pool_kernel_launch(const DecodeParams& p, const PoolFetch& f,
+                                     hipStream_t stream) {
+  // the balanced grid, then the fetch workgroups of a folded paging step:
+  // those of one CU per XCD
+  const unsigned grid = static_cast<unsigned>(p.num_splits) + (f.n > 0 ? kFetchCus * (8 / NW) : 0u);
   switch (p.num_q_heads / p.num_kv_heads) {
-    case 1: decode_pool_kernel<1, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 2: decode_pool_kernel<2, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 3: decode_pool_kernel<3, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 4: decode_pool_kernel<4, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 6: decode_pool_kernel<6, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
-    case 8: decode_pool_kernel<8, NW, I8><<<grid, NW * 64, 0, stream>>>(p); break;
+    case 1: decode_pool_kernel<1, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 2: decode_pool_kernel<2, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 3: decode_pool_kernel<3, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 4: decode_pool_kernel<4, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 6: decode_pool_kernel<6, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 8: decode_pool_kernel<8, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1486,11 +1552,12 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
                 : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream);
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);
+  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0, PoolPlace{});
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream) {
+hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream,
+                                   const PagerFuse* fuse) {
   // p.num_splits carries the size of the balanced grid: kPoolGrid 4-wave
   // workgroups, or half as many 8-wave ones for small pools
   DecodeParams p = p_in;
@@ -1501,16 +1568,40 @@ hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream)
   } else {
     p.plan = nullptr;
   }
-  const unsigned grid = static_cast<unsigned>(p.num_splits);
+  PoolFetch fetch{};
+  PoolPlace place{};
+  if (fuse != nullptr && fuse->n > 0) {
+    fetch.host_k = fuse->host_k;
+    fetch.host_v = fuse->host_v;
+    fetch.stage_k = fuse->stage_k;
+    fetch.stage_v = fuse->stage_v;
+    place.stage_k = fuse->stage_k;
+    place.stage_v = fuse->stage_v;
+    place.k_pool = fuse->k_pool;
+    place.v_pool = fuse->v_pool;
+    place.valid = fuse->valid;
+    fetch.block_u4 = place.block_u4 = fuse->block_u4;
+    fetch.n = place.n = fuse->n;
+    for (int i = 0; i < fuse->n; ++i) {
+      fetch.src_block[i] = fuse->src_block[i];
+      place.dst_block[i] = fuse->dst_block[i];
+      place.slot[i] = fuse->slot[i];
+    }
+  }
+  const bool wide = p.num_splits == kPoolGrid;  // 4-wave workgroups
+  // a folded paging step leaves kFetchCus CUs to the fetch: the balanced
+  // grid (and the merge) covers the rest
+  if (fetch.n > 0) p.num_splits -= static_cast<int>(kFetchCus) * (wide ? 2 : 1);
   if (p.i8)
-    err = grid == static_cast<unsigned>(kPoolGrid) ? decode_pool_kernel_launch<4, true>(p, grid, stream)
-                                                   : decode_pool_kernel_launch<8, true>(p, grid, stream);
+    err = wide ? decode_pool_kernel_launch<4, true>(p, fetch, stream)
+               : decode_pool_kernel_launch<8, true>(p, fetch, stream);
   else
-    err = grid == static_cast<unsigned>(kPoolGrid) ? decode_pool_kernel_launch<4, false>(p, grid, stream)
-                                                   : decode_pool_kernel_launch<8, false>(p, grid, stream);
+    err = wide ? decode_pool_kernel_launch<4, false>(p, fetch, stream)
+               : decode_pool_kernel_launch<8, false>(p, fetch, stream);
   if (err != hipSuccess) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 1);
+  const unsigned copy_wgs = static_cast<unsigned>(place.n * 2 * copy_pieces(place.block_u4, 256));
+  merge_kernel<8><<<copy_wgs + heads, 256, 0, stream>>>(p, 1, place);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 //   pager_valid_kernel  sets or clears a list of validity bytes.
 //   fill_u8_kernel      fills a byte array (reset).
 #include "device_common.h"
+#include "pager_copy.h"
 #include "swa_internal.h"
 
 namespace swa {
@@ -18,7 +19,6 @@ namespace swa {
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;  // independent 16-byte loads in flight per thread
 
 // Workgroup w copies piece (w % pieces) of tensor ((w / pieces) % 2) of item
 // w / (2 * pieces).  Every index is checked against the item count and the
@@ -35,21 +35,7 @@ __global__ __launch_bounds__(kCopyThreads) void pager_copy_kernel(PagerCopyParam
   uint4* dst = static_cast<uint4*>(tensor == 0 ? p.k_pool : p.v_pool) +
                static_cast<size_t>(p.dst_block[item]) * p.block_u4;
   const int begin = piece * p.piece_u4;
-  const int end = min(begin + p.piece_u4, p.block_u4);
-  for (int i = begin + static_cast<int>(threadIdx.x); i < end;
-       i += kCopyThreads * kCopyUnroll) {
-    uint4 v[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int j = i + u * kCopyThreads;
-      if (j < end) v[u] = src[j];
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int j = i + u * kCopyThreads;
-      if (j < end) dst[j] = v[u];
-    }
-  }
+  copy_block_piece(src, dst, begin, min(begin + p.piece_u4, p.block_u4), kCopyThreads);
 }
 
 __global__ void pager_valid_kernel(PagerValidParams p) {

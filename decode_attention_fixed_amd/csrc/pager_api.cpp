@@ -2,8 +2,13 @@
 // lives in pinned host memory; a fixed pool of device slots holds the blocks
 // the attention needs, each slot with a validity byte that decode_attn_paged
 // reads.  The residency policy is LRU ([pool] "residency policy": evict the
-// block used longest ago).  Copies run on a stream of their own while the
-// attention of the current step runs ([pool]: copies overlap the attention).
+// block used longest ago).  The copies overlap the attention ([pool]: copies
+// run beside the attention kernel): swa_pager_stage + swa_pager_decode fold
+// them into the decode's own launches (fetched from the host store into a
+// staging area of the workspace by workgroups of their own during the
+// attention, placed into the pool by the merge launch after it); with
+// swa_pager_advance they run as a launch of their own, on the attention
+// stream or a stream of their own.
 //
 // State per sequence b (host only):
 //   slot_block[b][j]  logical block in slot j, or -1
@@ -26,6 +31,23 @@
 #include "swa.h"
 #include "swa_internal.h"
 
+namespace swa {
+// decode_attn_paged with a paging step run after the attention (swa_api.cpp).
+swa_status paged_decode_with_copies(const swa_paged_desc* desc, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_table,
+                                    const int32_t* seq_lens, const uint8_t* block_valid,
+                                    float scale, void* out, swa_dtype out_dtype, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const PagerFuse* fuse);
+}  // namespace swa
+
+// A block to bring in: host store block b * L + k, pool block, slot b * C + j.
+struct PagerLoad {
+  int32_t src;
+  int32_t dst;
+  int32_t slot;
+};
+
 struct swa_pager {
   swa_pager_config cfg;
   const void* host_k;  // device views of the pinned host store
@@ -40,6 +62,7 @@ struct swa_pager {
   std::vector<int64_t> last_use;    // [B * L]
   std::vector<int64_t> mark;        // [B * L] request stamp (dedup, membership)
   std::vector<int32_t> pending;     // global slots copied by the last advance, not yet valid
+  std::vector<PagerLoad> staged;    // loads of the last swa_pager_stage, not yet launched
   int64_t clock = 1;                // index of the next request
   int64_t stamp = 0;
   size_t block_bytes = 0;           // bytes of one block of K (or V)
@@ -116,19 +139,19 @@ hipError_t launch_valid(uint8_t* valid, const std::vector<int32_t>& entries, hip
   return hipSuccess;
 }
 
-struct Load {
-  int32_t src;  // b * L + logical block
-  int32_t dst;  // physical pool block
-};
+// 16-byte units each copy workgroup moves: 8 KiB.
+int32_t copy_piece_u4(const swa_pager* pg) {
+  return std::min<int32_t>(static_cast<int32_t>(pg->block_bytes / 16), swa::kPagerCopyPieceU4);
+}
 
-hipError_t launch_copies(const swa_pager* pg, const std::vector<Load>& loads, hipStream_t s) {
+hipError_t launch_copies(const swa_pager* pg, const std::vector<PagerLoad>& loads, hipStream_t s) {
   swa::PagerCopyParams p{};
   p.host_k = pg->host_k;
   p.host_v = pg->host_v;
   p.k_pool = pg->k_pool;
   p.v_pool = pg->v_pool;
   p.block_u4 = static_cast<int32_t>(pg->block_bytes / 16);
-  p.piece_u4 = std::min<int32_t>(p.block_u4, 512);  // 8 KiB per workgroup
+  p.piece_u4 = copy_piece_u4(pg);
   p.pieces = (p.block_u4 + p.piece_u4 - 1) / p.piece_u4;
   for (size_t i = 0; i < loads.size(); i += swa::kPagerMaxCopies) {
     const size_t n = std::min(loads.size() - i, static_cast<size_t>(swa::kPagerMaxCopies));
@@ -141,6 +164,40 @@ hipError_t launch_copies(const swa_pager* pg, const std::vector<Load>& loads, hi
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// Staging area of a fused step, at the end of the decode's workspace: K
+// blocks, then as many V blocks; at most kStageBudget bytes, so a step with
+// more (or larger) blocks runs its copies as separate launches instead.
+constexpr size_t kStageBudget = size_t{16} << 20;
+constexpr size_t kStageAlign = 256;
+
+int32_t stage_blocks(const swa_pager* pg) {
+  return static_cast<int32_t>(
+      std::min<size_t>(swa::kPagerFuseMax, kStageBudget / (2 * pg->block_bytes)));
+}
+
+// Bytes swa_pager_decode needs: the decode's workspace for the pool, then the
+// staging area.  Returns the offset of the staging area in *stage_at.
+swa_status pager_workspace(const swa_pager* pg, int32_t num_q_heads, size_t* bytes,
+                           size_t* stage_at) {
+  const swa_pager_config& c = pg->cfg;
+  size_t dec = 0;
+  const swa_status st = decode_attn_workspace_bytes(c.batch, num_q_heads, c.num_kv_heads,
+                                                    c.head_dim, c.slots_per_seq * c.block_size,
+                                                    &dec);
+  if (st != SWA_OK) return st;
+  *stage_at = (dec + kStageAlign - 1) / kStageAlign * kStageAlign;
+  *bytes = *stage_at + 2 * static_cast<size_t>(stage_blocks(pg)) * pg->block_bytes;
+  return SWA_OK;
+}
+
+// The copies of a staged step and their validity bytes, as separate launches.
+hipError_t launch_staged(const swa_pager* pg, hipStream_t s) {
+  std::vector<int32_t> entries;
+  for (const PagerLoad& l : pg->staged) entries.push_back(l.slot);
+  hipError_t err = launch_copies(pg, pg->staged, s);
+  return err != hipSuccess ? err : launch_valid(pg->block_valid, entries, s);
 }
 
 }  // namespace
@@ -228,15 +285,24 @@ swa_status swa_pager_reset(swa_pager* pg, void* stream) {
   std::fill(pg->last_use.begin(), pg->last_use.end(), -1);
   std::fill(pg->mark.begin(), pg->mark.end(), -1);
   pg->pending.clear();
+  pg->staged.clear();
   pg->clock = 1;
   pg->stamp = 0;
   return ok();
 }
 
-swa_status swa_pager_advance(swa_pager* pg, const int32_t* req_offsets, const int32_t* req_blocks,
-                             void* stream, void* copy_stream, int32_t* n_loaded) {
-  if (pg == nullptr) return fail(SWA_ERR_INVALID_ARG, "pager is NULL");
-  if (req_offsets == nullptr) return fail(SWA_ERR_INVALID_ARG, "req_offsets is NULL");
+}  // extern "C"
+
+namespace {
+
+// Serves one request on the host state (LRU, the rules of
+// swa_pager_advance): checks it, then lists the blocks to bring in and the
+// slots whose block is evicted, in order.  A refused request changes nothing.
+swa_status serve_request(swa_pager* pg, const int32_t* req_offsets, const int32_t* req_blocks,
+                         std::vector<PagerLoad>& loads, std::vector<int32_t>& evicted,
+                         const char* name) {
+  if (pg == nullptr) return fail(SWA_ERR_INVALID_ARG, "%s: pager is NULL", name);
+  if (req_offsets == nullptr) return fail(SWA_ERR_INVALID_ARG, "%s: req_offsets is NULL", name);
   const swa_pager_config& c = pg->cfg;
   const int32_t B = c.batch, C = c.slots_per_seq, L = c.logical_blocks;
   if (req_offsets[0] != 0) return fail(SWA_ERR_INVALID_ARG, "req_offsets[0] must be 0");
@@ -277,10 +343,6 @@ swa_status swa_pager_advance(swa_pager* pg, const int32_t* req_offsets, const in
   }
 
   // Apply: choose slots, update the host state, list the device work.
-  std::vector<int32_t> entries;  // validity updates, in order
-  for (int32_t slot : pg->pending) entries.push_back(slot);
-  std::vector<Load> loads;
-  std::vector<int32_t> new_pending;
   std::vector<std::pair<int64_t, int32_t>> cand;  // (last use, slot) of evictable blocks
   for (int32_t b = 0; b < B; ++b) {
     const size_t bl = static_cast<size_t>(b) * L;
@@ -321,20 +383,42 @@ swa_status swa_pager_advance(swa_pager* pg, const int32_t* req_offsets, const in
         j = cand[next_victim++].second;
         const int32_t old = held[j];
         where[old] = -1;
-        entries.push_back(-1 - static_cast<int32_t>(bc + j));  // clear before the copy lands
+        evicted.push_back(static_cast<int32_t>(bc + j));
       }
       held[j] = k;
       where[k] = j;
-      loads.push_back({static_cast<int32_t>(bl + k), pg->slot_phys[bc + j]});
-      new_pending.push_back(static_cast<int32_t>(bc + j));
+      loads.push_back({static_cast<int32_t>(bl + k), pg->slot_phys[bc + j],
+                       static_cast<int32_t>(bc + j)});
     }
     for (int32_t i = req_offsets[b]; i < req_offsets[b + 1]; ++i) last[req_blocks[i]] = pg->clock;
   }
   pg->clock += 1;
+  return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+swa_status swa_pager_advance(swa_pager* pg, const int32_t* req_offsets, const int32_t* req_blocks,
+                             void* stream, void* copy_stream, int32_t* n_loaded) {
+  if (pg != nullptr && !pg->staged.empty())
+    return fail(SWA_ERR_INVALID_ARG, "swa_pager_advance: the blocks of the last swa_pager_stage "
+                                     "are not copied yet (call swa_pager_decode or "
+                                     "swa_pager_commit first)");
+  std::vector<PagerLoad> loads;
+  std::vector<int32_t> evicted;
+  swa_status st = serve_request(pg, req_offsets, req_blocks, loads, evicted, "swa_pager_advance");
+  if (st != SWA_OK) return st;
 
   // Device work: the previous copies become valid and this call's victims
-  // invalid on the attention stream; the new copies start on the copy stream
-  // after everything enqueued on the attention stream so far.
+  // invalid (cleared before the copies land) on the attention stream; the
+  // new copies start on the copy stream after everything enqueued on the
+  // attention stream so far.
+  std::vector<int32_t> entries(pg->pending);
+  for (int32_t slot : evicted) entries.push_back(-1 - slot);
+  std::vector<int32_t> new_pending;
+  for (const PagerLoad& l : loads) new_pending.push_back(l.slot);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipStream_t cs = static_cast<hipStream_t>(copy_stream);
   // With one stream for both, stream order alone does it: no event is waited
@@ -357,10 +441,97 @@ swa_status swa_pager_advance(swa_pager* pg, const int32_t* req_offsets, const in
   return from_hip(err, "swa_pager_advance");
 }
 
+swa_status swa_pager_stage(swa_pager* pg, const int32_t* req_offsets, const int32_t* req_blocks,
+                           int32_t* n_loaded) {
+  if (pg != nullptr && !pg->staged.empty())
+    return fail(SWA_ERR_INVALID_ARG, "swa_pager_stage: the blocks of the last swa_pager_stage "
+                                     "are not copied yet (call swa_pager_decode or "
+                                     "swa_pager_commit first)");
+  if (pg != nullptr && !pg->pending.empty())
+    return fail(SWA_ERR_INVALID_ARG, "swa_pager_stage: the copies of the last swa_pager_advance "
+                                     "are not visible yet (call swa_pager_commit first)");
+  std::vector<PagerLoad> loads;
+  std::vector<int32_t> evicted;  // overwritten in place after the attention: nothing to clear
+  swa_status st = serve_request(pg, req_offsets, req_blocks, loads, evicted, "swa_pager_stage");
+  if (st != SWA_OK) return st;
+  pg->staged.swap(loads);
+  if (n_loaded != nullptr) *n_loaded = static_cast<int32_t>(pg->staged.size());
+  return ok();
+}
+
+swa_status swa_pager_decode(swa_pager* pg, const void* q, int32_t num_q_heads,
+                            const int32_t* seq_lens, float scale, void* out, swa_dtype out_dtype,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (pg == nullptr) return fail(SWA_ERR_INVALID_ARG, "swa_pager_decode: pager is NULL");
+  if (!pg->pending.empty())
+    return fail(SWA_ERR_INVALID_ARG, "swa_pager_decode: the copies of the last "
+                                     "swa_pager_advance are not visible yet (call "
+                                     "swa_pager_commit first)");
+  const swa_pager_config& c = pg->cfg;
+  size_t need = 0, stage_at = 0;
+  swa_status st = pager_workspace(pg, num_q_heads, &need, &stage_at);
+  if (st != SWA_OK) return st;
+  if (workspace_bytes < need)
+    return fail(SWA_ERR_WORKSPACE, "swa_pager_decode: workspace too small: %zu bytes given, "
+                                   "%zu needed (swa_pager_workspace_bytes)", workspace_bytes, need);
+  swa_paged_desc d{};
+  d.batch = c.batch;
+  d.num_q_heads = num_q_heads;
+  d.num_kv_heads = c.num_kv_heads;
+  d.head_dim = c.head_dim;
+  d.block_size = c.block_size;
+  d.max_blocks_per_seq = c.slots_per_seq;
+  d.num_phys_blocks = c.num_phys_blocks;
+  d.dtype = c.dtype;
+  // The staged copies run in the decode's launches when they fit the staging
+  // area; otherwise as separate launches after the decode (the same order).
+  const bool fused = !pg->staged.empty() &&
+                     pg->staged.size() <= static_cast<size_t>(stage_blocks(pg));
+  swa::PagerFuse f{};
+  if (fused) {
+    char* stage = static_cast<char*>(workspace) + stage_at;
+    f.host_k = pg->host_k;
+    f.host_v = pg->host_v;
+    f.stage_k = stage;
+    f.stage_v = stage + static_cast<size_t>(stage_blocks(pg)) * pg->block_bytes;
+    f.k_pool = pg->k_pool;
+    f.v_pool = pg->v_pool;
+    f.valid = pg->block_valid;
+    f.block_u4 = static_cast<int32_t>(pg->block_bytes / 16);
+    f.n = static_cast<int32_t>(pg->staged.size());
+    for (int32_t i = 0; i < f.n; ++i) {
+      f.src_block[i] = pg->staged[i].src;
+      f.dst_block[i] = pg->staged[i].dst;
+      f.slot[i] = pg->staged[i].slot;
+    }
+  }
+  st = swa::paged_decode_with_copies(
+      &d, q, pg->k_pool, pg->v_pool, pg->block_table, seq_lens, pg->block_valid, scale, out,
+      out_dtype, lse, workspace, workspace_bytes, stream, fused ? &f : nullptr);
+  if (st != SWA_OK) return st;  // an argument error launched nothing: the stage still stands
+  hipError_t err = hipSuccess;
+  if (!fused && !pg->staged.empty()) err = launch_staged(pg, static_cast<hipStream_t>(stream));
+  pg->staged.clear();
+  return from_hip(err, "swa_pager_decode");
+}
+
+swa_status swa_pager_workspace_bytes(const swa_pager* pg, int32_t num_q_heads, size_t* bytes) {
+  if (pg == nullptr || bytes == nullptr)
+    return fail(SWA_ERR_INVALID_ARG, "swa_pager_workspace_bytes: pager or bytes is NULL");
+  size_t stage_at = 0;
+  const swa_status st = pager_workspace(pg, num_q_heads, bytes, &stage_at);
+  return st != SWA_OK ? st : ok();
+}
+
 swa_status swa_pager_commit(swa_pager* pg, void* stream) {
   if (pg == nullptr) return fail(SWA_ERR_INVALID_ARG, "pager is NULL");
-  if (pg->pending.empty()) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!pg->staged.empty()) {  // a stage not yet decoded: its copies now, no attention
+    const hipError_t err = launch_staged(pg, s);
+    pg->staged.clear();
+    if (err != hipSuccess) return from_hip(err, "swa_pager_commit");
+  }
+  if (pg->pending.empty()) return ok();
   hipError_t err = pg->pending_stream != s ? hipStreamWaitEvent(s, pg->copied, 0) : hipSuccess;
   if (err == hipSuccess) err = launch_valid(pg->block_valid, pg->pending, s);
   pg->pending.clear();

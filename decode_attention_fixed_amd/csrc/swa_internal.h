@@ -195,9 +195,13 @@ hipError_t launch_append_i8(const AppendParams& p, hipStream_t stream);
 hipError_t launch_write_paged_i8(const PagedWriteParams& p, hipStream_t stream);
 hipError_t launch_write_paged(const PagedWriteParams& p, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+struct PagerFuse;
+// fuse: a paging step to run after the attention (null: none).
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream,
+                               const PagerFuse* fuse = nullptr);
 hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma_pool(const DecodeParams& p, hipStream_t stream,
+                                   const PagerFuse* fuse = nullptr);
 // The shared-prefix pass (one launch; finds and writes the plan too).
 bool prefix_pass_applies(const DecodeParams& p);
 hipError_t launch_shared_prefix(const DecodeParams& p, hipStream_t stream);
@@ -289,6 +293,7 @@ hipError_t launch_append_paged(const AppendPagedParams& p, hipStream_t stream);
 // memory that a later call could overwrite before the kernel runs.
 constexpr int kPagerMaxCopies = 224;  // blocks per copy launch
 constexpr int kPagerMaxValid = 448;   // validity updates per launch
+constexpr int32_t kPagerCopyPieceU4 = 512;  // 16-byte units per copy workgroup (8 KiB)
 struct PagerCopyParams {
   const void* host_k;   // device view of the pinned host store [B * L blocks]
   const void* host_v;
@@ -305,6 +310,32 @@ struct PagerValidParams {
   uint8_t* valid;       // [B * C]
   int32_t n;
   int32_t entries[kPagerMaxValid];  // e >= 0: valid[e] = 1; e < 0: valid[-1 - e] = 0
+};
+// A paging step folded into the paged decode ([pool] section on copies
+// overlapped with the attention), in two parts.  Fetch: workgroups added to
+// the attention launch copy block src_block[i] (b * L + logical block) of the
+// host store into staging block i while the attention reads the pool (the
+// staging area is not part of the pool, so nothing the attention reads
+// changes).  Place: workgroups added to the merge launch, which starts after
+// the attention kernel has read the pool, move staging block i into pool
+// block dst_block[i] and set the validity byte slot[i] (b * C + slot); so a
+// slot may be overwritten even if this step's attention read its old block.
+constexpr int kPagerFuseMax = 64;  // blocks per fused step (more: separate launches after)
+static_assert(kPagerFuseMax <= kPagerMaxCopies && kPagerFuseMax <= kPagerMaxValid,
+              "a fused step fits one copy and one validity launch");
+struct PagerFuse {
+  const void* host_k;   // device views of the pinned host store
+  const void* host_v;
+  void* stage_k;        // [n blocks] of K, then of V: device memory the attention does not read
+  void* stage_v;
+  void* k_pool;
+  void* v_pool;
+  uint8_t* valid;       // [B * C]
+  int32_t block_u4;     // 16-byte units per block of K (or V)
+  int32_t n;            // blocks (0: nothing to copy)
+  int32_t src_block[kPagerFuseMax];
+  int32_t dst_block[kPagerFuseMax];
+  int32_t slot[kPagerFuseMax];
 };
 hipError_t launch_pager_copy(const PagerCopyParams& p, hipStream_t stream);
 hipError_t launch_pager_valid(const PagerValidParams& p, hipStream_t stream);

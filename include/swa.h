@@ -524,9 +524,60 @@ swa_status swa_pager_reset(swa_pager* pager, void* stream);
 swa_status swa_pager_advance(swa_pager* pager, const int32_t* req_offsets,
                              const int32_t* req_blocks, void* stream, void* copy_stream,
                              int32_t* n_loaded);
+/* (SWA_ERR_INVALID_ARG while a swa_pager_stage is pending.) */
+
+/* The paging step folded into the attention's launches ([pool] "paging", the
+ * copies overlapping the attention kernel so that it only consumes resident
+ * blocks).  swa_pager_stage serves the next step's request on the host
+ * state exactly as swa_pager_advance does (same LRU decisions, same refusal)
+ * but launches nothing; the next swa_pager_decode on the pager runs the
+ * attention over the pool and, in the same launches, the staged copies:
+ * extra workgroups of the attention launch read the staged blocks from the
+ * host store into a staging area of the workspace while the attention reads
+ * the pool, and extra workgroups of the merge launch (which starts after the
+ * attention has read the pool) move them into their slots and set their
+ * validity bytes.  Everything is ordered by `stream` alone: no event, no
+ * second stream.  A step's attention therefore sees the blocks resident when
+ * it starts, including blocks that the staged request evicts (their slots
+ * are overwritten only after the attention has read them), and the staged
+ * blocks are visible to every launch after the decode:
+ *   stage(N_0); commit; stage(N_1); decode(step 0); stage(N_2); decode(step 1); ...
+ *
+ *   req_offsets, req_blocks, n_loaded  as for swa_pager_advance.
+ *
+ * SWA_ERR_INVALID_ARG when a stage is pending (not yet decoded or committed)
+ * or when copies of swa_pager_advance are not yet visible (commit first).
+ * Not thread-safe, as the rest of the pager. */
+swa_status swa_pager_stage(swa_pager* pager, const int32_t* req_offsets, const int32_t* req_blocks,
+                           int32_t* n_loaded);
+
+/* decode_attn_paged over the pager's pool (block_table and block_valid of
+ * the pager, max_blocks_per_seq = slots_per_seq, the config's batch, heads,
+ * head_dim, block_size, pool size and dtype), followed in the same launches
+ * by the copies of the last swa_pager_stage (see above; more staged blocks
+ * than the staging area holds, min(64, 16 MiB / (2 x block bytes)), or a
+ * pool the matrix-core decode does not take, run as separate launches after
+ * the decode, with the same effect).  The arguments are decode_attn_paged's:
+ * q [B, num_q_heads, d] rotated, seq_lens [B] device (C * block_size to
+ * attend every visible slot), scale, out, out_dtype, lse, and a device
+ * workspace of at least swa_pager_workspace_bytes(pager, num_q_heads) bytes,
+ * 256-byte aligned (SWA_ERR_WORKSPACE if smaller).  An argument error
+ * launches nothing and leaves the stage pending; SWA_ERR_INVALID_ARG when
+ * copies of swa_pager_advance are not yet visible (commit first). */
+swa_status swa_pager_decode(swa_pager* pager, const void* q, int32_t num_q_heads,
+                            const int32_t* seq_lens, float scale, void* out, swa_dtype out_dtype,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Library helper (no page defines it): workspace bytes swa_pager_decode needs
+ * with num_q_heads query heads: decode_attn_workspace_bytes(B, num_q_heads,
+ * Hkv, d, slots_per_seq * block_size) rounded up to 256, plus the staging
+ * area of the folded copies.  Also enough for decode_attn_paged over the
+ * pager's pool.  *bytes, host. */
+swa_status swa_pager_workspace_bytes(const swa_pager* pager, int32_t num_q_heads, size_t* bytes);
 
 /* Library helper (no page defines it): makes the copies of the last advance visible to work enqueued on `stream`
- * after this call (it waits for them on the device, not on the host). */
+ * after this call (it waits for them on the device, not on the host); a stage
+ * not yet decoded has its copies launched on `stream` (no attention). */
 swa_status swa_pager_commit(swa_pager* pager, void* stream);
 
 /* Library helper (no page defines it): logical block held by each slot of sequence seq (-1 = empty), as the host

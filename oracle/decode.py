@@ -186,6 +186,30 @@ def pager_schedule(w, b: int):
     return visible, slots
 
 
+def pager_schedule_fused(w, b: int):
+    """(visible, slots) as pager_schedule, for the paging step folded into
+    the decode (swa_pager_stage of step t + 1's request, then the decode of
+    step t, whose merge launch copies the staged blocks).  Reading: a step
+    attends the blocks resident when it starts, i.e. the pool after every
+    earlier copy has landed; the staged request's evictions take effect
+    only after that attention (the slots are overwritten by the copies that
+    follow it), so step t still sees the blocks they evict.  `slots` is the
+    pool after step t + 1's request is served; every block in it is visible
+    once step t's launches are done."""
+    pool = LruPool(w.pool_slots)
+    for r in w.prefill_requests():
+        pool.advance(r)
+    pool.request(w.step_request(b, 0))
+    visible, slots = [], []
+    for step in range(w.decode_steps):
+        pool.commit()
+        visible.append(sorted(pool.visible()))
+        if step + 1 < w.decode_steps:
+            pool.advance(w.step_request(b, step + 1))
+        slots.append(list(pool.slot_block))
+    return visible, slots
+
+
 def pager_expected(w, b: int, step: int, blocks, scale=None, style: str = "interleaved"):
     """(out [Hq, d], lse [Hq]) of decode step `step` over the given blocks."""
     blocks = np.asarray(sorted(blocks), dtype=np.int64)

@@ -93,6 +93,17 @@ hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned) {
 // the launches, done on the host
 // ---------------------------------------------------------------------------
 
+// The decode's workspace size: any value serves the pager's arithmetic here
+// (not a multiple of 256, so the staging area's alignment step is taken).
+extern "C" swa_status decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                                  int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t max_kv_tokens, size_t* bytes) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_kv_tokens < 0)
+    return SWA_ERR_INVALID_ARG;
+  *bytes = 1000 + static_cast<size_t>(batch) * num_q_heads * (head_dim + 1) * 4;
+  return SWA_OK;
+}
+
 namespace swa {
 
 namespace {
@@ -162,6 +173,36 @@ hipError_t launch_pager_copy(const PagerCopyParams& p, hipStream_t) {
 hipError_t launch_fill_u8(uint8_t* dst, size_t n, uint8_t value, hipStream_t) {
   std::memset(dst, value, n);
   return hipSuccess;
+}
+
+// The pager's decode: the attention is not modelled here; the copies of a
+// fused paging step and their validity bytes are (swa_api.cpp is not built).
+swa_status paged_decode_with_copies(const swa_paged_desc* desc, const void* q, const void*,
+                                    const void*, const int32_t* block_table,
+                                    const int32_t* seq_lens, const uint8_t*, float, void* out,
+                                    swa_dtype, float*, void* workspace, size_t, void*,
+                                    const PagerFuse* fuse) {
+  if (desc == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return SWA_ERR_INVALID_ARG;
+  if (fuse == nullptr) return SWA_OK;
+  // the two parts as the kernels run them: host store to staging area (during
+  // the attention), then staging area to pool (in the merge launch)
+  const size_t bytes = static_cast<size_t>(fuse->block_u4) * 16;
+  for (int i = 0; i < fuse->n; ++i) {
+    std::memcpy(static_cast<char*>(fuse->stage_k) + i * bytes,
+                static_cast<const char*>(fuse->host_k) + fuse->src_block[i] * bytes, bytes);
+    std::memcpy(static_cast<char*>(fuse->stage_v) + i * bytes,
+                static_cast<const char*>(fuse->host_v) + fuse->src_block[i] * bytes, bytes);
+  }
+  for (int i = 0; i < fuse->n; ++i) {
+    std::memcpy(static_cast<char*>(fuse->k_pool) + fuse->dst_block[i] * bytes,
+                static_cast<const char*>(fuse->stage_k) + i * bytes, bytes);
+    std::memcpy(static_cast<char*>(fuse->v_pool) + fuse->dst_block[i] * bytes,
+                static_cast<const char*>(fuse->stage_v) + i * bytes, bytes);
+    fuse->valid[fuse->slot[i]] = 1;
+  }
+  return SWA_OK;
 }
 
 }  // namespace swa
@@ -332,6 +373,34 @@ int run() {
       std::printf("rc %d loaded %d\n", rc, loaded);
     } else if (cmd == "commit") {
       std::printf("rc %d\n", swa_pager_commit(pa->pg, fake_stream(0)));
+    } else if (cmd == "stage") {
+      std::vector<int32_t> off{0}, blocks;
+      for (int b = 0; b < pa->cfg.batch; ++b) {
+        int n;
+        in >> n;
+        for (int i = 0; i < n; ++i) {
+          int k;
+          in >> k;
+          blocks.push_back(k);
+        }
+        off.push_back(static_cast<int32_t>(blocks.size()));
+      }
+      int32_t loaded = -1;
+      const int rc = swa_pager_stage(pa->pg, off.data(), blocks.empty() ? nullptr : blocks.data(),
+                                     &loaded);
+      std::printf("rc %d loaded %d\n", rc, loaded);
+    } else if (cmd == "pdecode") {
+      float q = 0.f, o = 0.f;
+      std::vector<int32_t> lens(pa->cfg.batch, pa->cfg.slots_per_seq * pa->cfg.block_size);
+      size_t n = 0;
+      if (swa_pager_workspace_bytes(pa->pg, pa->cfg.num_kv_heads, &n) != SWA_OK) {
+        std::printf("rc -1\n");
+        continue;
+      }
+      std::vector<char> ws(n);  // exactly the size asked for: an overrun is reported
+      std::printf("rc %d\n", swa_pager_decode(pa->pg, &q, pa->cfg.num_kv_heads, lens.data(), 0.f,
+                                               &o, SWA_F32, nullptr, ws.data(), ws.size(),
+                                               fake_stream(0)));
     } else if (cmd == "pstate") {
       const swa_pager_config& c = pa->cfg;
       std::vector<int32_t> sb(c.slots_per_seq);

@@ -239,8 +239,6 @@ class PagerState:
         self.seq_lens = torch.full((B_,), C * w.block_size, dtype=torch.int32, device=device)
         self.desc = B.make_paged_desc(B_, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                       w.block_size, C, self.num_phys, w.dtype)
-        self.workspace = B.new_workspace(B_, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                         C * w.block_size, device)
         self.out = torch.empty((B_, w.num_q_heads, w.head_dim), dtype=out_dtype, device=device)
         self.lse = torch.empty((B_, w.num_q_heads), dtype=torch.float32, device=device)
         self.cfg = B.make_pager_config(B_, w.num_kv_heads, w.head_dim, w.block_size, L, C,
@@ -248,6 +246,9 @@ class PagerState:
         self.handle = B.swa_pager_create(self.cfg, self.host_k, self.host_v, self.k_pool,
                                          self.v_pool, w.slot_phys.tolist(), self.block_table,
                                          self.block_valid)
+        # the decode's workspace plus the staging area of the folded copies
+        self.workspace = torch.empty(B.swa_pager_workspace_bytes(self.handle, w.num_q_heads),
+                                     dtype=torch.uint8, device=device)
 
     def fill_host(self) -> None:
         w = self.w
@@ -277,6 +278,16 @@ class PagerState:
 
     def commit(self) -> None:
         B.swa_pager_commit(self.handle)
+
+    def stage(self, requests) -> int:
+        """The next step's requests, copied by the next fused_decode."""
+        return B.swa_pager_stage(self.handle, requests)
+
+    def fused_decode(self, q: torch.Tensor, scale: float = 0.0, prepare: bool = False):
+        """The decode over the pool, then the staged copies, in its launches."""
+        return B.swa_pager_decode(self.handle, self.desc, q, self.k_pool, self.v_pool,
+                                  self.block_table, self.seq_lens, self.block_valid, self.out,
+                                  self.workspace, self.lse, scale, prepare=prepare)
 
     def warm(self, copy_stream=None) -> int:
         """The history streams in, then step 0's request is met in full."""

@@ -10,13 +10,18 @@ bit for bit (paging moves bytes and changes none).
 
 Pool rows that the pager has not written hold NaN, so a slot read before its
 copy lands, or after its eviction, would show.
+
+The paging step folded into the decode (swa_pager_stage, then
+swa_pager_decode copying the staged blocks in its merge launch) is checked
+the same way against the oracle's fused schedule: a step attends the blocks
+resident when it starts, and after it every resident block is valid.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle.decode import pager_expected, pager_schedule
+from oracle.decode import pager_expected, pager_schedule, pager_schedule_fused
 from oracle.paging import LruPool
 from synth import PagerWorkload, workload
 
@@ -165,5 +170,147 @@ def test_pager_full_size():
     try:
         n = w.decode_steps
         _run(w, st, {0, 1, n // 2, n - 1}, torch.cuda.Stream())
+    finally:
+        st.close()
+
+
+def _run_fused(w, st, steps_to_check, tol=TOL_BF16, calls=None):
+    """stage(N_{t+1}); decode(t) for every step (calls: the decode of each
+    step repeated that many times on its stage, to show a repeat copies
+    nothing more)."""
+    sched = [pager_schedule_fused(w, b) for b in range(w.batch)]
+    st.warm(None)
+    for step in range(w.decode_steps):
+        if step + 1 < w.decode_steps:
+            st.stage(st.step_requests(step + 1))
+        st.fused_decode(st.step_query(step))
+        torch.cuda.synchronize()
+        valid = st.block_valid.cpu().numpy()
+        for b in range(w.batch):
+            visible, slots = sched[b][0][step], sched[b][1][step]
+            assert st.slot_blocks(b) == slots, (step, b)
+            want_valid = np.array([1 if s >= 0 else 0 for s in slots], dtype=np.uint8)
+            assert np.array_equal(valid[b], want_valid), (step, b)
+        if step in steps_to_check:
+            out = st.out.cpu().numpy()
+            lse = st.lse.cpu().numpy()
+            for b in range(w.batch):
+                want, want_lse = pager_expected(w, b, step, sched[b][0][step])
+                err = float(np.abs(out[b] - want).max())
+                assert err <= tol, (step, b, err)
+                assert float(np.abs(lse[b] - want_lse).max()) <= 1e-4
+    torch.cuda.synchronize()
+    _check_pool_bytes(st, w, [st.slot_blocks(b) for b in range(w.batch)])
+
+
+@pytest.mark.parametrize("kw,tol", [
+    (dict(), TOL_BF16),                                              # bf16, g = 4
+    (dict(num_q_heads=24, num_kv_heads=4, pool_slots=15, prefill_blocks=5, seed=62,
+          logical_blocks=80, decode_steps=12), TOL_BF16),            # g = 6
+    (dict(dtype="f32", head_dim=64, num_q_heads=4, num_kv_heads=4, block_size=16),
+     TOL_F32),                                                       # copies after the decode
+])
+def test_pager_fused_step(kw, tol):
+    w = _pager(**kw)
+    st = _state(w)
+    try:
+        _run_fused(w, st, set(range(w.decode_steps)), tol)
+    finally:
+        st.close()
+
+
+def test_pager_fused_step_many_blocks():
+    """More staged blocks than one merge launch takes (64): they are copied
+    by launches after the decode, with the same result."""
+    w = _pager(batch=8, pool_slots=80, logical_blocks=120, focus_blocks=30, focus_drift=30,
+               revisits=4, decode_steps=6, seed=64)
+    st = _state(w)
+    try:
+        st.warm(None)
+        n = st.stage(st.step_requests(1))
+        assert n > 64, n
+        st.fused_decode(st.step_query(0))
+        torch.cuda.synchronize()
+        sched = [pager_schedule_fused(w, b) for b in range(w.batch)]
+        valid = st.block_valid.cpu().numpy()
+        out = st.out.cpu().numpy()
+        for b in range(w.batch):
+            assert st.slot_blocks(b) == sched[b][1][0]
+            assert np.array_equal(valid[b], np.array([1 if s >= 0 else 0 for s in sched[b][1][0]],
+                                                     dtype=np.uint8))
+            want, _ = pager_expected(w, b, 0, sched[b][0][0])
+            assert float(np.abs(out[b] - want).max()) <= TOL_BF16
+        _check_pool_bytes(st, w, [st.slot_blocks(b) for b in range(w.batch)])
+    finally:
+        st.close()
+
+
+def test_pager_stage_order_rules():
+    """A second stage before the decode, an advance while a stage is pending,
+    and a stage while an advance's copies are pending are refused, launching
+    nothing; commit runs a pending stage's copies without an attention."""
+    from decode_attention_fixed_amd.binding import SWA_ERR_INVALID_ARG, SwaError
+    w = _pager(batch=1, decode_steps=4)
+    st = _state(w)
+    try:
+        st.warm(None)
+        assert st.stage(st.step_requests(1)) >= 0
+        with pytest.raises(SwaError) as e:
+            st.stage(st.step_requests(2))
+        assert e.value.code == SWA_ERR_INVALID_ARG
+        with pytest.raises(SwaError) as e:
+            st.advance(st.step_requests(2))
+        assert e.value.code == SWA_ERR_INVALID_ARG
+        st.commit()
+        torch.cuda.synchronize()
+        slots = st.slot_blocks(0)
+        valid = st.block_valid.cpu().numpy()[0]
+        assert list(valid) == [1 if s >= 0 else 0 for s in slots]
+        _check_pool_bytes(st, w, [slots])
+        st.advance(st.step_requests(2))
+        with pytest.raises(SwaError) as e:
+            st.stage(st.step_requests(3))
+        assert e.value.code == SWA_ERR_INVALID_ARG
+        with pytest.raises(SwaError) as e:
+            st.fused_decode(st.step_query(1))
+        assert e.value.code == SWA_ERR_INVALID_ARG
+    finally:
+        st.close()
+
+
+
+def test_pager_decode_workspace_too_small():
+    """swa_pager_decode refuses a workspace below swa_pager_workspace_bytes
+    (the decode's own size is not enough: the staging area follows it),
+    launching nothing and leaving the stage pending."""
+    from decode_attention_fixed_amd import binding as B
+    from decode_attention_fixed_amd.binding import SWA_ERR_WORKSPACE, SwaError
+    w = _pager(batch=2, decode_steps=4)
+    st = _state(w)
+    try:
+        st.warm(None)
+        need = B.swa_pager_workspace_bytes(st.handle, w.num_q_heads)
+        dec = B.decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                            w.pool_slots * w.block_size)
+        assert need > dec
+        n = st.stage(st.step_requests(1))
+        assert n > 0
+        small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+        pool_k = st.k_pool.clone()
+        valid = st.block_valid.clone()
+        with pytest.raises(SwaError) as e:
+            B.swa_pager_decode(st.handle, st.desc, st.step_query(0), st.k_pool, st.v_pool,
+                               st.block_table, st.seq_lens, st.block_valid, st.out, small,
+                               st.lse)
+        assert e.value.code == SWA_ERR_WORKSPACE
+        torch.cuda.synchronize()
+        assert torch.equal(pool_k, st.k_pool) and torch.equal(valid, st.block_valid)
+        # the stage still stands: the decode with the right workspace copies it
+        st.fused_decode(st.step_query(0))
+        torch.cuda.synchronize()
+        sched = [pager_schedule_fused(w, b) for b in range(w.batch)]
+        for b in range(w.batch):
+            assert st.slot_blocks(b) == sched[b][1][0]
+        _check_pool_bytes(st, w, [st.slot_blocks(b) for b in range(w.batch)])
     finally:
         st.close()

@@ -12,9 +12,10 @@ traces then drive the C ABI and every state is compared with the oracles:
           and the free count bit for bit, and every sequence read back
           through the device table (its own history, per head, K and V).
   pager   LRU requests (some refused, copies on the attention stream or a
-          second one), against oracle/paging.py: the block in every slot,
-          the device validity bytes (= the oracle's visible set), and every
-          valid slot's pool block equal to the host store's block.
+          second one, or staged and run by the pager's decode), against
+          oracle/paging.py: the block in every slot, the device validity
+          bytes (= the oracle's visible set), and every valid slot's pool
+          block equal to the host store's block.
 
 Any heap misuse, leak (events included), or undefined behaviour aborts the
 binary, which fails the test.
@@ -164,36 +165,82 @@ def test_block_manager_sanitized(binary, seed, nb, bs, seqs, maxb):
 # ---------------------------------------------------------------------------
 
 def _pager_trace(seed, batch, L, C, n_ops):
+    """Advances (copies on the attention stream or a second one), stages
+    with their fused decodes, and commits, in random order: the library's
+    refusals follow its rules (no stage while an advance's copies or another
+    stage are pending; no advance while a stage is pending; no decode while
+    an advance's copies are pending).  The state is checked whenever no
+    stage is pending (a pending stage's slots still hold their old blocks)."""
     rng = np.random.default_rng(seed)
     pools = [LruPool(C) for _ in range(batch)]
     nphys = batch * C
     cmds, exp = [f"pager {batch} 2 64 16 {L} {C} {nphys}"], [("rc", 0, None)]
+    staged = pending = False
+
+    def draw():
+        reqs = []
+        for _b in range(batch):
+            n = int(rng.integers(0, C // 2 + 1)) if rng.random() < 0.85 else \
+                int(rng.integers(0, min(L, C + 3)))
+            reqs.append([int(x) for x in rng.integers(0, L, size=n)])
+        return reqs
+
+    def serve(reqs):
+        nonlocal pools
+        trial = copy.deepcopy(pools)
+        loaded = 0
+        try:
+            for p, r in zip(trial, reqs):
+                loaded += len(p.advance(r))
+        except PoolRefused:
+            return -1, None
+        pools = trial
+        return 0, loaded
+
+    def packed(reqs):
+        return " ".join(f"{len(r)} " + " ".join(map(str, r)) for r in reqs)
+
     for _ in range(n_ops):
-        if rng.random() < 0.15:
+        x = rng.random()
+        if x < 0.12:
             for p in pools:
                 p.commit()
+            staged = pending = False
             cmds.append("commit")
             exp.append(("rc", 0, None))
-        else:
-            reqs = []
-            for _b in range(batch):
-                n = int(rng.integers(0, C // 2 + 1)) if rng.random() < 0.85 else \
-                    int(rng.integers(0, min(L, C + 3)))
-                reqs.append([int(x) for x in rng.integers(0, L, size=n)])
-            trial = copy.deepcopy(pools)
-            loaded = 0
-            try:
-                for p, r in zip(trial, reqs):
-                    loaded += len(p.advance(r))
-                pools, rc = trial, 0
-            except PoolRefused:
+        elif x < 0.45:
+            reqs = draw()
+            if staged:
                 rc, loaded = -1, None
-            split = int(rng.integers(2))
-            cmds.append(f"advance {split} " + " ".join(f"{len(r)} " + " ".join(map(str, r))
-                                                        for r in reqs))
+            else:
+                rc, loaded = serve(reqs)
+                if rc == 0:
+                    pending = loaded > 0
+            cmds.append(f"advance {int(rng.integers(2))} " + packed(reqs))
             exp.append(("advance", rc, loaded))
-        cmds.append("pstate")
-        exp.append(("pstate", copy.deepcopy(pools), None))
+        elif x < 0.75:
+            reqs = draw()
+            if staged or pending:
+                rc, loaded = -1, None
+            else:
+                rc, loaded = serve(reqs)
+                if rc == 0:
+                    staged = loaded > 0
+            cmds.append("stage " + packed(reqs))
+            exp.append(("advance", rc, loaded))
+        else:
+            if pending:
+                rc = -1
+            else:
+                rc = 0
+                for p in pools:
+                    p.commit()
+                staged = False
+            cmds.append("pdecode")
+            exp.append(("rc", rc, None))
+        if not staged:
+            cmds.append("pstate")
+            exp.append(("pstate", copy.deepcopy(pools), None))
     return cmds, exp
 
 

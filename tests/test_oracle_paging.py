@@ -138,3 +138,34 @@ def test_random_trace_invariants():
                     (last_use[b] for b in kept), default=1 << 30)
             assert pool.visible() == (pool.resident() - missing)
             prev = reqset
+
+
+@pytest.mark.parametrize("seed,slots", [(61, 12), (62, 15), (63, 10)])
+def test_fused_schedule_against_the_advance_schedule(seed, slots):
+    """oracle/decode.py's two pager schedules, pinned against each other and
+    the LRU pool: with the paging step folded into the decode, step t sees
+    every block its request names, exactly what the advance-then-decode
+    order shows it plus the blocks that step t + 1's request evicts, and the
+    pool after serving step t + 1's request is the same in both orders."""
+    from oracle.decode import pager_schedule, pager_schedule_fused
+    from synth import PagerWorkload
+    w = PagerWorkload(name="pg", seed=seed, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      dtype="bf16", block_size=64, logical_blocks=48, pool_slots=slots,
+                      rope_base=10000.0, scale=0.5, decode_steps=12, prefill_blocks=4,
+                      window_blocks=2, focus_blocks=3, focus_drift=2, revisits=2)
+    for b in range(w.batch):
+        vis_a, slots_a = pager_schedule(w, b)
+        vis_f, slots_f = pager_schedule_fused(w, b)
+        assert slots_a == slots_f
+        evicted_total = 0
+        for t in range(w.decode_steps):
+            named = set(int(x) for x in w.step_request(b, t))
+            assert named <= set(vis_f[t]), (b, t)
+            assert set(vis_a[t]) <= set(vis_f[t]), (b, t)
+            before = set(slots_f[t - 1]) - {-1} if t > 0 else set(vis_f[0])
+            assert set(vis_f[t]) == before, (b, t)  # everything resident at its start
+            if t + 1 < w.decode_steps:  # (the last step serves no next request)
+                evicted = before - (set(slots_f[t]) - {-1})
+                assert set(vis_f[t]) - set(vis_a[t]) == evicted, (b, t)
+                evicted_total += len(evicted)
+        assert evicted_total > 0  # the case evicts blocks
