@@ -174,10 +174,9 @@ def test_pager_full_size():
         st.close()
 
 
-def _run_fused(w, st, steps_to_check, tol=TOL_BF16, calls=None):
-    """stage(N_{t+1}); decode(t) for every step (calls: the decode of each
-    step repeated that many times on its stage, to show a repeat copies
-    nothing more)."""
+def _run_fused(w, st, steps_to_check, tol=TOL_BF16, seqs=None):
+    """stage(N_{t+1}); decode(t) for every step; outputs checked on the
+    sequences `seqs` (all: None)."""
     sched = [pager_schedule_fused(w, b) for b in range(w.batch)]
     st.warm(None)
     for step in range(w.decode_steps):
@@ -194,7 +193,7 @@ def _run_fused(w, st, steps_to_check, tol=TOL_BF16, calls=None):
         if step in steps_to_check:
             out = st.out.cpu().numpy()
             lse = st.lse.cpu().numpy()
-            for b in range(w.batch):
+            for b in (range(w.batch) if seqs is None else seqs):
                 want, want_lse = pager_expected(w, b, step, sched[b][0][step])
                 err = float(np.abs(out[b] - want).max())
                 assert err <= tol, (step, b, err)
@@ -215,6 +214,24 @@ def test_pager_fused_step(kw, tol):
     st = _state(w)
     try:
         _run_fused(w, st, set(range(w.decode_steps)), tol)
+    finally:
+        st.close()
+
+
+def test_pager_fused_step_wide_grid():
+    """A pool of 1M rows of capacity takes the 512 x 4-wave grid; a fused step
+    gives the workgroups of 8 CUs to the fetch, so the attention runs on 496
+    workgroups (shares by division, not by shift) and the merge finds the
+    owners of 496 shares."""
+    w = _pager(batch=8, num_q_heads=4, num_kv_heads=1, pool_slots=2048, logical_blocks=3000,
+               prefill_blocks=128, window_blocks=16, focus_blocks=16, focus_drift=8, revisits=16,
+               decode_steps=3, seed=66)
+    assert w.batch * w.num_kv_heads * w.pool_slots * w.block_size >= 512 * 2048
+    st = _state(w)
+    try:
+        # step 0 stages 53 blocks (folded), step 1 stages 75 (more than a
+        # folded step takes: launches of their own after the decode)
+        _run_fused(w, st, {0, 1}, seqs=[0, 5])
     finally:
         st.close()
 
