@@ -25,8 +25,9 @@ Pages are cited by address and section:
   [kvc]    http://www.pwwt.cn/news/5010196/         (KV cache fundamentals)
   [pool]   https://www.cloudlnk.cn/blog/kv-cache-paging (fixed KV pool, slot mask)
 
-Parity status of each function is stated in its module.  Unpinned by the
-pages: the RoPE pairing convention and frequencies beyond the first pair
-(rope.py), and the exact ring slot chosen for a position (ring.slot_of; the
-set of positions held is pinned, the slot index is a reading).
+Parity status of each function is stated in its module.  Not fixed by the
+pages: the RoPE pairing convention and frequencies (rope.py pins both
+against two library implementations of the rotary embedding instead), and
+the exact ring slot chosen for a position (ring.slot_of; the set of
+positions held is pinned, the slot index is a reading).
 """

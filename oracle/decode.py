@@ -189,13 +189,15 @@ def pager_schedule(w, b: int):
 def pager_schedule_fused(w, b: int):
     """(visible, slots) as pager_schedule, for the paging step folded into
     the decode (swa_pager_stage of step t + 1's request, then the decode of
-    step t, whose merge launch copies the staged blocks).  Reading: a step
-    attends the blocks resident when it starts, i.e. the pool after every
-    earlier copy has landed; the staged request's evictions take effect
-    only after that attention (the slots are overwritten by the copies that
-    follow it), so step t still sees the blocks they evict.  `slots` is the
+    step t, whose launches copy the staged blocks into their slots after the
+    attention has read the pool).  Reading: a step attends the blocks
+    resident when it starts, i.e. the pool after every earlier copy has
+    landed; the staged request's evictions take effect only after that
+    attention, so step t still sees the blocks they evict.  `slots` is the
     pool after step t + 1's request is served; every block in it is visible
-    once step t's launches are done."""
+    once step t's launches are done.  Pinned (tests/test_oracle_paging.py):
+    its slot decisions are those of the advance schedule, request for
+    request, and a step sees every block the advance schedule shows it."""
     pool = LruPool(w.pool_slots)
     for r in w.prefill_requests():
         pool.advance(r)
