@@ -674,6 +674,48 @@ def copy_calibration(nbytes: int = 1 << 30) -> None:
                       "gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def copy_engine_probe(block_bytes: int = 64 << 10, blocks: int = 256, reps: int = 4) -> dict:
+    """What one host-to-device copy through the copy engine costs: `blocks`
+    scattered blocks of `block_bytes` from pinned host memory, one
+    hipMemcpyAsync each (torch's non-blocking copy_), against one copy of the
+    same bytes contiguous.  The pager moves its blocks with a kernel instead
+    (one launch for all of a step's blocks)."""
+    import numpy as np
+    import torch
+    torch.cuda.set_device(0)
+    n = block_bytes // 2
+    src = torch.empty((blocks, n), dtype=torch.int16, pin_memory=True).fill_(1)
+    dst = torch.empty((blocks, n), dtype=torch.int16, device="cuda")
+    order = np.random.default_rng(0).permutation(blocks)
+    stream = torch.cuda.Stream()
+    out = {}
+    with torch.cuda.stream(stream):
+        for kind in ("per_block", "contiguous"):
+            def run():
+                if kind == "per_block":
+                    for i in order:
+                        dst[int(i)].copy_(src[int(i)], non_blocking=True)
+                else:
+                    dst.copy_(src, non_blocking=True)
+            run()
+            stream.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record(stream)
+            for _ in range(reps):
+                run()
+            b.record(stream)
+            b.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3 / reps
+            ms = a.elapsed_time(b) / reps
+            calls = blocks if kind == "per_block" else 1
+            out[kind] = {"copies": calls, "bytes_each": block_bytes * blocks // calls,
+                         "gpu_us_per_copy": round(ms * 1e3 / calls, 2),
+                         "host_us_per_copy": round(wall * 1e3 / calls, 2),
+                         "gbs": round(block_bytes * blocks / ms / 1e6, 2)}
+    return {"copy_engine_probe": out}
+
+
 def read_ceiling(nbytes: int = 4 << 30, reps: int = 20) -> dict:
     """The HBM read rate the chip achieves: swa_stream_read (nontemporal
     16-byte loads, 2048 workgroups, nothing written but one word per wave)
@@ -768,6 +810,9 @@ def main() -> int:
     ap.add_argument("--no-per-config", action="store_true",
                     help="measure the named workload only (the profiling runs use this)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-engine-probe", action="store_true",
+                    help="print only the cost of host-to-device block copies through the copy "
+                         "engine (one hipMemcpyAsync per 64 KiB block, and one contiguous copy)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="print only the streaming HBM read rate (swa_stream_read)")
     ap.add_argument("--no-read-ceiling", action="store_true")
@@ -795,6 +840,9 @@ def main() -> int:
 
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.copy_engine_probe:
+        print(json.dumps(copy_engine_probe()), flush=True)
         return 0
     if args.read_ceiling:
         print(json.dumps(read_ceiling()), flush=True)
