@@ -576,7 +576,8 @@ static swa_status paged_decode(const swa_paged_desc* desc, const void* q, const 
                                const int32_t* seq_lens, const uint8_t* block_valid, float scale,
                                void* out, swa_dtype out_dtype, float* lse, void* workspace,
                                size_t workspace_bytes, void* stream, const char* name,
-                               const swa::PagerFuse* fuse = nullptr) {
+                               const swa::PagerFuse* fuse = nullptr,
+                               bool private_blocks = false) {
   swa_status st = check_paged_desc(desc);
   if (st != SWA_OK) return st;
   st = check_group(desc->num_q_heads, desc->num_kv_heads);
@@ -627,6 +628,9 @@ static swa_status paged_decode(const swa_paged_desc* desc, const void* q, const 
     p.v_scale = i8_scales(const_cast<void*>(v_pool), rows, desc->head_dim);
   }
   fill_workspace_ptrs(p, workspace, lay);
+  // no two sequences name the same block: the shared-prefix pass would find
+  // nothing, so it is not launched
+  if (private_blocks) p.plan = nullptr;
   return from_hip(swa::launch_decode_paged(p, static_cast<hipStream_t>(stream), fuse), name);
 }
 
@@ -634,7 +638,8 @@ static swa_status paged_decode(const swa_paged_desc* desc, const void* q, const 
 
 namespace swa {
 // The pager's decode (swa_pager_decode): decode_attn_paged, with the paging
-// step `fuse` run after the attention in the same stream order.
+// step `fuse` run after the attention in the same stream order.  The pager's
+// slots are distinct pool blocks, so no two sequences share one.
 swa_status paged_decode_with_copies(const swa_paged_desc* desc, const void* q, const void* k_pool,
                                     const void* v_pool, const int32_t* block_table,
                                     const int32_t* seq_lens, const uint8_t* block_valid,
@@ -642,7 +647,8 @@ swa_status paged_decode_with_copies(const swa_paged_desc* desc, const void* q, c
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     const PagerFuse* fuse) {
   return paged_decode(desc, q, k_pool, v_pool, block_table, seq_lens, block_valid, scale, out,
-                      out_dtype, lse, workspace, workspace_bytes, stream, "swa_pager_decode", fuse);
+                      out_dtype, lse, workspace, workspace_bytes, stream, "swa_pager_decode", fuse,
+                      true);
 }
 }  // namespace swa
 

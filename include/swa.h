@@ -553,7 +553,8 @@ swa_status swa_pager_stage(swa_pager* pager, const int32_t* req_offsets, const i
 
 /* decode_attn_paged over the pager's pool (block_table and block_valid of
  * the pager, max_blocks_per_seq = slots_per_seq, the config's batch, heads,
- * head_dim, block_size, pool size and dtype), followed in the same launches
+ * head_dim, block_size, pool size and dtype; no shared-prefix pass, since no
+ * two of the pager's sequences share a block), followed in the same launches
  * by the copies of the last swa_pager_stage (see above; more staged blocks
  * than the staging area holds, min(64, 16 MiB / (2 x block bytes)), or a
  * pool the matrix-core decode does not take, run as separate launches after
