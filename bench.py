@@ -37,7 +37,10 @@ Prints one JSON line:
                    same run: steps/s, step GB/s, the decode call's duration,
                    GB/s and fraction of the peak, and the rocprofv3 average of
                    the call's kernels from the committed profile when it was
-                   taken on the current kernel sources.
+                   taken on the current kernel sources; then the host-pool
+                   paging step (long-pool-swap, with the same decode on the
+                   same pool without paging) and the chunked prefill
+                   (gqa-prefill: TFLOP/s against the MFMA peak).
 
 Prefill workloads (mha-prefill, gqa-prefill): a step is one prefill_attn_ring
 call over a chunk of new tokens per sequence (rotation of the chunk, the
@@ -91,7 +94,8 @@ DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "decode_share
 PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill.hip", "append_rope.hip",
                                                  "device_common.h")]
 DEFAULT_WORKLOAD = "paged"
-PER_CONFIG = ("gqa-ring", "long-pool-b1", "long-pool-b16", "mha-ring")
+PER_CONFIG = ("gqa-ring", "long-pool-b1", "long-pool-b16", "mha-ring", "long-pool-swap",
+              "gqa-prefill")
 MIN_CALLS = 64   # decode calls timed back to back for the roofline region
 
 
@@ -786,9 +790,24 @@ def per_config_entry(name: str, args, ceiling_gbs: float | None = None) -> dict:
     from synth import WORKLOADS
     w = WORKLOADS[name]
     res = measure(w, args.steps, args.warmup)
+    if w.kind == "ring" and w.chunk:  # chunked prefill: flops against the MFMA peak
+        line = prefill_line(w, args, res)
+        r = line["roofline"]
+        prof = profile_call_us(name, "prefill")
+        return {"workload": line["config"]["workload"], "tokens_per_s": line["tokens_per_s"],
+                "ms_per_step": line["ms_per_step"], "tflops": line["value"],
+                "call_us": r["call_us"], "call_tflops": r["achieved"], "bound": "mfma",
+                "frac": r["frac"], "profile_call_us": prof,
+                "algorithmic_flops": r["algorithmic_flops"]}
     n = decode_numbers(w, args.steps, res)
     prof = profile_call_us(name)
-    return {"workload": describe(w)["workload"], "steps_per_s": round(1e3 / n["ms_per_step"], 1),
+    extra = {}
+    if w.kind == "pager":
+        extra["swap"] = {"mode": "fused",
+                         "blocks_per_step": round(res["blocks_loaded_region1"] / args.steps, 3),
+                         "no_swap_ms_per_step": round(res["no_swap_ms"], 5)}
+    return {"workload": describe(w)["workload"],
+            "steps_per_s": round(1e3 / n["ms_per_step"], 1),
             "ms_per_step": round(n["ms_per_step"], 5), "gbs": round(n["value"], 1),
             "call_us": round(n["call_us"], 2), "call_gbs": round(n["achieved"], 1),
             "frac": round(n["achieved"] / HBM_PEAK_GBS, 4),
@@ -797,7 +816,7 @@ def per_config_entry(name: str, args, ceiling_gbs: float | None = None) -> dict:
             "profile_call_us": prof,
             "profile_frac": (round(res["kv_bytes_call"] / (prof * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                              if prof else None),
-            "algorithmic_bytes": res["kv_bytes_call"]}
+            "algorithmic_bytes": res["kv_bytes_call"], **extra}
 
 
 def main() -> int:
@@ -916,7 +935,9 @@ def main() -> int:
         for name in PER_CONFIG:
             out["per_config"].append(per_config_entry(name, args,
                                                       ceiling["read_gbs"] if ceiling else None))
-            log(f"per-config {name}: {out['per_config'][-1]['call_gbs']} GB/s per call")
+            e = out["per_config"][-1]
+            log(f"per-config {name}: " + (f"{e['call_gbs']} GB/s per call" if "call_gbs" in e
+                                          else f"{e['call_tflops']} TFLOP/s per call"))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
