@@ -1406,8 +1406,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
   }
   if (count == 1 && shared == 0) return;  // written directly by the attention kernel
   const int slots = count + shared;
+  // with T >= W every share holds at least one granule: all of them present
+  const bool dense = !pool || total >= nwg;
   auto present = [&](int k) {  // pool: the k-th workgroup of the run owns rows
-    if (!pool || k >= count) return true;
+    if (dense || k >= count) return true;
     const int64_t wk = w0 + k;
     const int64_t a = share_start(wk, total, nwg);
     const int64_t e = wk + 1 == nwg ? total : share_start(wk + 1, total, nwg);

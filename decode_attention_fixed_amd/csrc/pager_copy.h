@@ -9,21 +9,24 @@ namespace swa {
 constexpr int kCopyUnroll = 4;  // independent 16-byte loads in flight per thread
 
 // Units [begin, end) of a block (16-byte units) from src to dst, by the whole
-// workgroup of `threads` threads.
+// workgroup of `threads` threads.  Four named registers, not an array (an
+// array indexed in a loop is placed in memory before the loop is unrolled),
+// and the four loads are issued unconditionally, the addresses past the end
+// clamped to the last unit, so none waits on its own; only the stores are
+// conditional.
 __device__ __forceinline__ void copy_block_piece(const uint4* src, uint4* dst, int begin, int end,
                                                  int threads) {
+  static_assert(kCopyUnroll == 4, "four loads per thread and pass");
   for (int i = begin + static_cast<int>(threadIdx.x); i < end; i += threads * kCopyUnroll) {
-    uint4 v[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int j = i + u * threads;
-      if (j < end) v[u] = src[j];
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int j = i + u * threads;
-      if (j < end) dst[j] = v[u];
-    }
+    const int j1 = i + threads, j2 = i + 2 * threads, j3 = i + 3 * threads;
+    const uint4 a0 = src[i];
+    const uint4 a1 = src[min(j1, end - 1)];
+    const uint4 a2 = src[min(j2, end - 1)];
+    const uint4 a3 = src[min(j3, end - 1)];
+    dst[i] = a0;
+    if (j1 < end) dst[j1] = a1;
+    if (j2 < end) dst[j2] = a2;
+    if (j3 < end) dst[j3] = a3;
   }
 }
 
