@@ -208,7 +208,7 @@ swa_status paged_decode_with_copies(const swa_paged_desc* desc, const void* q, c
 }  // namespace swa
 
 // ---------------------------------------------------------------------------
-// the driver
+// the command-line front end of this test program
 // ---------------------------------------------------------------------------
 
 namespace {
