@@ -290,6 +290,10 @@ int run() {
       int s;
       in >> s;
       std::printf("rc %d\n", swa_blocks_free(bl->m, s, bl->lens.data(), fake_stream(0)));
+    } else if (cmd == "reset") {
+      std::printf("rc %d\n", swa_blocks_reset(bl->m));
+    } else if (cmd == "bsync") {
+      std::printf("rc %d\n", swa_blocks_sync(bl->m, bl->table.data(), bl->lens.data(), nullptr));
     } else if (cmd == "bstate") {
       const swa_paged_desc& d = bl->desc;
       std::vector<int32_t> table(bl->table.size()), lens(d.batch), refs(d.num_phys_blocks);

@@ -387,6 +387,13 @@ def test_pager_null_handle():
     L.swa_pager_destroy(None)
 
 
+def test_blocks_null_handle():
+    L = B.LIB
+    assert L.swa_blocks_reset(None) == B.SWA_ERR_INVALID_ARG
+    assert L.swa_blocks_free(None, 0, FAKE, None) == B.SWA_ERR_INVALID_ARG
+    L.swa_blocks_destroy(None)
+
+
 def test_int8_is_not_an_output_dtype():
     """SWA_I8 names a cache element type, never an output type: every entry
     point that writes `out` refuses it before anything is launched (an int8

@@ -8,7 +8,7 @@ traces then drive the C ABI and every state is compared with the oracles:
 
   blocks  allocate-on-append / share_prefix / append (several sequences per
           call, copy-on-write of shared partial blocks, refused calls) /
-          free, against oracle/blocks.py: tables, lengths, reference counts
+          free / reset, against oracle/blocks.py: tables, lengths, reference counts
           and the free count bit for bit, and every sequence read back
           through the device table (its own history, per head, K and V).
   pager   LRU requests (some refused, copies on the attention stream or a
@@ -81,7 +81,7 @@ def _blocks_trace(seed, nb, bs, seqs, maxb, n_ops):
     cmds, exp = [f"blocks {nb} {bs} {seqs} {maxb} 2 64"], [("rc", 0)]
     lens = lambda s: om.lens.get(s, 0)  # noqa: E731
     for _ in range(n_ops):
-        op = rng.choice(["append", "share", "free"], p=[0.5, 0.3, 0.2])
+        op = rng.choice(["append", "share", "free", "reset"], p=[0.49, 0.3, 0.18, 0.03])
         if op == "append":
             k = int(rng.integers(1, seqs + 1))
             chosen = [int(s) for s in rng.choice(seqs, size=k, replace=False)]
@@ -113,11 +113,15 @@ def _blocks_trace(seed, nb, bs, seqs, maxb, n_ops):
             om.share_prefix(src, dst, n)
             cmds.append(f"share {src} {dst} {n}")
             exp.append(("rc", 0))
-        else:
+        elif op == "free":
             s = int(rng.integers(seqs))
             om.free(s)
             cmds.append(f"free {s}")
             exp.append(("rc", 0))
+        else:  # everything empty again, the device mirrors rewritten
+            om = BlockManager(nb, bs)
+            cmds += ["reset", "bsync"]
+            exp += [("rc", 0), ("rc", 0)]
         cmds.append("bstate")
         exp.append(("bstate", copy.deepcopy(om)))
     return cmds, exp
