@@ -16,12 +16,12 @@
 // streams contiguous memory.
 //   ring cache  all sequences have S + W slots: a grid of (b, kv head, split)
 //               with equal splits, one piece per workgroup.
-//   paged pool  lengths differ: a fixed grid of workgroups, each taking an
-//               equal share of all resident rows (every sequence's rows padded
-//               to a 64-row multiple, kv heads laid end to end); its share
-//               may span several pieces.  Equal shares keep the last round of
-//               workgroups from running half empty when long and short
-//               sequences mix.
+//   paged pool  lengths differ: a fixed grid of workgroups, each taking a
+//               share of all resident rows (every sequence's rows padded to a
+//               64-row multiple, kv heads laid end to end); its share may span
+//               several pieces.  Shares balanced over the whole pool keep the
+//               last round of workgroups from running half empty when long
+//               and short sequences mix.
 //
 // Per tile of NS 16-row subtiles and wave (lane l, row group lq = l / 16,
 // column lc = l % 16):
@@ -1053,7 +1053,11 @@ struct PoolPlace {
 // contributes Hkv ranges of n_b = ceil(len_b / 64) granules (one per kv head,
 // heads laid end to end), sequences in order; the total is
 // T = Hkv * sum_b n_b.  Workgroup w of W (see share_start) owns granules
-// [s(w), s(w+1)) with s(w) = floor(w T / W).  The piece of unit
+// [s(w), s(w+1)) with s(w) = floor((16 w + w mod 2) T / (16 W)): workgroups
+// of even index take 17/16 of an equal share, those of odd index 15/16.
+// Workgroup w runs on XCD w mod 8, and the even XCDs stream faster: on two
+// MI355X machines these weights brought paged and long-pool-b16 calls ~2%
+// below equal shares (1/8 instead of 1/16 overshot).  The piece of unit
 // u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
 // granule order move u or w forward by one each, so the slots are distinct
 // and fewer than units + W).
@@ -1071,10 +1075,11 @@ __device__ __forceinline__ int granules(const DecodeParams& p, int b) {
 // that less the workgroups of kFetchCus CUs in a call with a folded paging
 // step.
 __device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg) {
+  const int64_t c = 16 * w + (w & 1);  // cumulative weight, in sixteenths
   if ((nwg & (nwg - 1)) != 0)
-    return static_cast<int64_t>(static_cast<uint64_t>(w * total) / static_cast<uint64_t>(nwg));
-  const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg));
-  return (w * total) >> shift;
+    return static_cast<int64_t>(static_cast<uint64_t>(c * total) / static_cast<uint64_t>(16 * nwg));
+  const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg)) + 4;
+  return (c * total) >> shift;
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
@@ -1406,8 +1411,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
   }
   if (count == 1 && shared == 0) return;  // written directly by the attention kernel
   const int slots = count + shared;
-  // with T >= W every share holds at least one granule: all of them present
-  const bool dense = !pool || total >= nwg;
+  // with T >= 2 W every share holds at least one granule (each is at least
+  // 15/16 of T / W): all of them present
+  const bool dense = !pool || total >= 2 * nwg;
   auto present = [&](int k) {  // pool: the k-th workgroup of the run owns rows
     if (dense || k >= count) return true;
     const int64_t wk = w0 + k;
