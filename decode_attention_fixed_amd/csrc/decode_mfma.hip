@@ -1053,11 +1053,14 @@ struct PoolPlace {
 // contributes Hkv ranges of n_b = ceil(len_b / 64) granules (one per kv head,
 // heads laid end to end), sequences in order; the total is
 // T = Hkv * sum_b n_b.  Workgroup w of W (see share_start) owns granules
-// [s(w), s(w+1)) with s(w) = floor((16 w + w mod 2) T / (16 W)): workgroups
-// of even index take 17/16 of an equal share, those of odd index 15/16.
-// Workgroup w runs on XCD w mod 8, and the even XCDs stream faster: on two
-// MI355X machines these weights brought paged and long-pool-b16 calls ~2%
-// below equal shares (1/8 instead of 1/16 overshot).  The piece of unit
+// [s(w), s(w+1)).  On bf16 pools s(w) = floor((16 w + w mod 2) T / (16 W)):
+// workgroups of even index take 17/16 of an equal share, those of odd index
+// 15/16.  Workgroup w runs on XCD w mod 8, and the even XCDs stream faster:
+// on two MI355X machines these weights brought paged and long-pool-b16 calls
+// 2-3% below equal shares (1/8 instead of 1/16 overshot).  The int8 kernels
+// are bound by their VALU work, not by the stream, and the same weights made
+// them 1.5-3.5% slower: int8 pools keep equal shares, s(w) = floor(w T / W).
+// The piece of unit
 // u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
 // granule order move u or w forward by one each, so the slots are distinct
 // and fewer than units + W).
@@ -1074,8 +1077,9 @@ __device__ __forceinline__ int granules(const DecodeParams& p, int b) {
 // W is kPoolGrid or kPoolGrid / 2, a power of two (no 64-bit division), or
 // that less the workgroups of kFetchCus CUs in a call with a folded paging
 // step.
-__device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg) {
-  const int64_t c = 16 * w + (w & 1);  // cumulative weight, in sixteenths
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg,
+                                               bool i8) {
+  const int64_t c = 16 * w + (i8 ? 0 : (w & 1));  // cumulative weight, in sixteenths
   if ((nwg & (nwg - 1)) != 0)
     return static_cast<int64_t>(static_cast<uint64_t>(c * total) / static_cast<uint64_t>(16 * nwg));
   const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg)) + 4;
@@ -1283,8 +1287,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
   for (int b = NT + threadIdx.x; b < p.batch; b += NT) rest += granules(p, b);
   if (p.batch > NT) rest = block_sum<NT>(rest, sc.red);
   const int64_t total = (csum + rest) * hkv;
-  const int64_t g0 = share_start(w, total, nwg);
-  const int64_t g1 = w + 1 == nwg ? total : share_start(w + 1, total, nwg);
+  const int64_t g0 = share_start(w, total, nwg, p.i8);
+  const int64_t g1 = w + 1 == nwg ? total : share_start(w + 1, total, nwg, p.i8);
   if (g0 >= g1) return;
 
   // Chunk holding the first sequence that ends past g0, and that sequence.
@@ -1399,8 +1403,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
         int64_t wq = static_cast<int64_t>(static_cast<double>(x) * static_cast<double>(nwg) /
                                           static_cast<double>(total));
         wq = wq < 0 ? 0 : (wq >= nwg ? nwg - 1 : wq);
-        while (wq > 0 && share_start(wq, total, nwg) > x) --wq;
-        while (wq + 1 < nwg && share_start(wq + 1, total, nwg) <= x) ++wq;
+        while (wq > 0 && share_start(wq, total, nwg, p.i8) > x) --wq;
+        while (wq + 1 < nwg && share_start(wq + 1, total, nwg, p.i8) <= x) ++wq;
         return wq;
       };
       w0 = owner(u0);
@@ -1417,8 +1421,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
   auto present = [&](int k) {  // pool: the k-th workgroup of the run owns rows
     if (dense || k >= count) return true;
     const int64_t wk = w0 + k;
-    const int64_t a = share_start(wk, total, nwg);
-    const int64_t e = wk + 1 == nwg ? total : share_start(wk + 1, total, nwg);
+    const int64_t a = share_start(wk, total, nwg, p.i8);
+    const int64_t e = wk + 1 == nwg ? total : share_start(wk + 1, total, nwg, p.i8);
     return a < e;
   };
   auto slot_of = [&](int k) -> size_t {  // partial slot of the k-th partial
