@@ -1053,13 +1053,16 @@ struct PoolPlace {
 // contributes Hkv ranges of n_b = ceil(len_b / 64) granules (one per kv head,
 // heads laid end to end), sequences in order; the total is
 // T = Hkv * sum_b n_b.  Workgroup w of W (see share_start) owns granules
-// [s(w), s(w+1)).  On bf16 pools s(w) = floor((16 w + w mod 2) T / (16 W)):
-// workgroups of even index take 17/16 of an equal share, those of odd index
-// 15/16.  Workgroup w runs on XCD w mod 8, and the even XCDs stream faster:
-// on two MI355X machines these weights brought paged and long-pool-b16 calls
-// 2-3% below equal shares (1/8 instead of 1/16 overshot).  The int8 kernels
-// are bound by their VALU work, not by the stream, and the same weights made
-// them 1.5-3.5% slower: int8 pools keep equal shares, s(w) = floor(w T / W).
+// [s(w), s(w+1)).  On bf16 pools with the grid of 4-wave workgroups
+// s(w) = floor((16 w + w mod 2) T / (16 W)): workgroups of even index take
+// 17/16 of an equal share, those of odd index 15/16.  Workgroup w runs on XCD
+// w mod 8, and the even XCDs stream faster: on two MI355X machines these
+// weights brought paged and long-pool-b16 calls 2-3% below equal shares (1/8
+// instead of 1/16 overshot).  Elsewhere the shares stay equal,
+// s(w) = floor(w T / W): the int8 kernels are bound by their VALU work, not
+// by the stream (the weights made them 1.5-3.5% slower), and on the small
+// pools' grid of 8-wave workgroups the weights measured no better or slower
+// (long-pool-b1 within noise, its folded paging step 3% slower).
 // The piece of unit
 // u = b * Hkv + h inside workgroup w uses partial slot u + w (pieces in
 // granule order move u or w forward by one each, so the slots are distinct
@@ -1079,7 +1082,8 @@ __device__ __forceinline__ int granules(const DecodeParams& p, int b) {
 // step.
 __device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t nwg,
                                                bool i8) {
-  const int64_t c = 16 * w + (i8 ? 0 : (w & 1));  // cumulative weight, in sixteenths
+  const bool weighted = !i8 && nwg > kPoolGrid / 2;
+  const int64_t c = 16 * w + (weighted ? (w & 1) : 0);  // cumulative weight, in sixteenths
   if ((nwg & (nwg - 1)) != 0)
     return static_cast<int64_t>(static_cast<uint64_t>(c * total) / static_cast<uint64_t>(16 * nwg));
   const int shift = __builtin_ctzll(static_cast<unsigned long long>(nwg)) + 4;
