@@ -1056,9 +1056,9 @@ struct PoolPlace {
 // [s(w), s(w+1)).  On bf16 pools with the grid of 4-wave workgroups
 // s(w) = floor((16 w + w mod 2) T / (16 W)): workgroups of even index take
 // 17/16 of an equal share, those of odd index 15/16.  Workgroup w runs on XCD
-// w mod 8, and the even XCDs stream faster: on two MI355X machines these
-// weights brought paged and long-pool-b16 calls 2-3% below equal shares (1/8
-// instead of 1/16 overshot).  Elsewhere the shares stay equal,
+// w mod 8, and the even XCDs stream faster: measured against equal shares in
+// the same run, these weights brought paged and long-pool-b16 calls 1.5-3.4%
+// lower (1/8 instead of 1/16 overshot).  Elsewhere the shares stay equal,
 // s(w) = floor(w T / W): the int8 kernels are bound by their VALU work, not
 // by the stream (the weights made them 1.5-3.5% slower), and on the small
 // pools' grid of 8-wave workgroups the weights measured no better or slower
