@@ -5,6 +5,10 @@
 // Workgroup w streams its own contiguous share of 16-byte units with
 // nontemporal loads, kUnroll loads in flight per thread; the XOR of what a
 // wave read goes to sink[w * kWaves + wave] so that no load can be dropped.
+// Workgroup w runs on XCD w mod 8, and the even XCDs stream faster: shares
+// of 17/16 of an equal one on even w and 15/16 on odd w read 4 GiB ~1.3%
+// faster than equal shares (7.12 against 7.03 TB/s, in one run), the same
+// weights as the paged decode's balanced grid.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -23,9 +27,12 @@ static_assert(kStreamReadGrid * kWaves * sizeof(uint32_t) == kStreamReadSinkByte
               "one sink word per wave");
 
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4_t* src, size_t units,
-                                                               size_t per, uint32_t* sink) {
-  const size_t u0 = static_cast<size_t>(blockIdx.x) * per;
-  const size_t u1 = u0 + per < units ? u0 + per : units;
+                                                               uint32_t* sink) {
+  auto start = [&](size_t w) {  // first unit of workgroup w's share
+    return (16 * w + (w & 1)) * units / (16 * static_cast<size_t>(gridDim.x));
+  };
+  const size_t u0 = start(blockIdx.x);
+  const size_t u1 = blockIdx.x + 1 == gridDim.x ? units : start(blockIdx.x + 1);
   uint32_t acc = 0;
   size_t u = u0 + threadIdx.x;
   for (; u + static_cast<size_t>(kUnroll - 1) * kThreads < u1; u += kUnroll * kThreads) {
@@ -48,9 +55,8 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4_t* sr
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const size_t units = bytes / 16;
-  const size_t per = (units + kStreamReadGrid - 1) / kStreamReadGrid;
   stream_read_kernel<<<kStreamReadGrid, kThreads, 0, stream>>>(static_cast<const u32x4_t*>(src),
-                                                              units, per, sink);
+                                                              units, sink);
   return hipGetLastError();
 }
 
