@@ -86,25 +86,24 @@ __device__ __forceinline__ f16x8_t as_f16x8(const Vec16& v) {
   return __builtin_bit_cast(f16x8_t, v);
 }
 
-// Eight int8 codes (two 32-bit words) as fp16, exactly: a code c, its sign
-// bit flipped, is the byte c + 128; placed under the fp16 exponent of 1024
-// (0x64, unit spacing) it reads 1152 + c, and one packed subtraction of 1152
-// leaves c (all exact: |c| <= 127).  Two byte permutes and one packed add per
-// four codes.
-__device__ __forceinline__ Vec16 codes8_to_f16(uint32_t w0, uint32_t w1) {
+// Eight int8 codes (two 32-bit words) as the fp16 values 1152 + c, exactly:
+// a code c, its sign bit flipped, is the byte c + 128; placed under the fp16
+// exponent of 1024 (0x64, unit spacing) it reads 1152 + c (exact: |c| <= 127,
+// and 1025 .. 1279 have unit spacing).  One XOR per four codes, one byte
+// permute per two.  The matrix products take these biased values and the
+// bias is taken off their results (1152 times a sum over the other operand,
+// formed by products of its own), which saves the packed subtraction per two
+// codes that would make each value c.
+constexpr uint32_t kF16x2Bias = 0x64806480u;  // (1152, 1152) in fp16
+__device__ __forceinline__ Vec16 codes8_to_f16_biased(uint32_t w0, uint32_t w1) {
   const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-  const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
   // v_perm_b32 byte selectors: 0..3 pick bytes of the second operand (the
   // codes), 4 picks the first operand's 0x64
-  auto pair = [&](uint32_t x, uint32_t sel) {
-    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, x, sel);
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, b) + off);
-  };
   Vec16 r;
-  r.w[0] = pair(x0, 0x04010400u);
-  r.w[1] = pair(x0, 0x04030402u);
-  r.w[2] = pair(x1, 0x04010400u);
-  r.w[3] = pair(x1, 0x04030402u);
+  r.w[0] = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);
+  r.w[1] = __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u);
+  r.w[2] = __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u);
+  r.w[3] = __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u);
   return r;
 }
 
@@ -518,6 +517,21 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
         }
     }
   }
+  // int8 rows: the score products take the codes as 1152 + c; every score of
+  // head lc then carries 1152 times the sum of the head's query, which the
+  // same products with every code at 1152 form once per piece, and the score
+  // accumulators start at its negation.
+  f32x4_t score_init = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (I8) {
+    Vec16 bias;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias.w[i] = kF16x2Bias;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s)
+      score_init =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(bias), as_f16x8(qop[s]), score_init, 0, 0, 0);
+    score_init = -score_init;
+  }
 
   const float c = p.score_scale_log2 * qinv;
   float m = kNegInf;  // running max of head lc (log2 units)
@@ -683,12 +697,12 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
     float tmax = kNegInf;
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t d = score_init;
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s) {
-        if constexpr (I8) {  // 8 codes of row lc -> exact fp16 operand
+        if constexpr (I8) {  // 8 codes of row lc -> fp16 operand 1152 + c
           const Vec16& w = ka[u][s >> 1];
-          const Vec16 a = codes8_to_f16(w.w[2 * (s & 1)], w.w[2 * (s & 1) + 1]);
+          const Vec16 a = codes8_to_f16_biased(w.w[2 * (s & 1)], w.w[2 * (s & 1) + 1]);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(qop[s]), d, 0, 0, 0);
         } else {
           d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[u][s]), as_bf16x8(qop[s]), d, 0,
@@ -764,9 +778,12 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
         // 16 rows and 16 dims: A = P (lane (lc, lq): head lc, rows 4lq + i,
         // exactly pr[u][i]); B = V (lane (lc, lq): rows 4lq + i, dim 8lc + nb
         // in block nb, byte nb of the lane's own codes of those rows, made
-        // fp16 as for K).  P carries the V scale; the tile's weights are scaled
-        // by 2^k, k from the largest V scale of its present rows, into fp16's
-        // range, and the tile's product by 2^-k on the way into accm.
+        // fp16 as 1152 + c, as for K).  P carries the V scale; the tile's
+        // weights are scaled by 2^k, k from the largest V scale of its present
+        // rows, into fp16's range, and the tile's product by 2^-k on the way
+        // into accm.  The bias, 1152 times each head's weight sum, is the
+        // product of the same P with B = 1152 everywhere (tc), taken off once
+        // per tile.
         float vmax = 0.f;
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
@@ -784,12 +801,14 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
           k = k < -126 ? -126 : (k > 126 ? 126 : k);
         }
         const float up = ldexpf(1.f, k), down = ldexpf(1.f, -k);
-        const f16x2_t off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
+        const f16x4_t bias = __builtin_bit_cast(f16x4_t, make_uint2(kF16x2Bias, kF16x2Bias));
+        f32x4_t tc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
           const f16x2_t a01 = __builtin_convertvector(f32x2_t{pr[u][0] * up, pr[u][1] * up}, f16x2_t);
           const f16x2_t a23 = __builtin_convertvector(f32x2_t{pr[u][2] * up, pr[u][3] * up}, f16x2_t);
           const f16x4_t a = {a01[0], a01[1], a23[0], a23[1]};
+          tc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bias, tc, 0, 0, 0);
           uint32_t x[4][2];  // codes of rows 4lq + i, sign bits flipped
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -804,16 +823,15 @@ __device__ void attend_piece(const DecodeParams& p, Smem<G, NW, NS_, I8 ? 8 : 16
                                  static_cast<uint32_t>(bsel);
             const uint32_t b01 = __builtin_amdgcn_perm(x[1][w], x[0][w], sel) | 0x64006400u;
             const uint32_t b23 = __builtin_amdgcn_perm(x[3][w], x[2][w], sel) | 0x64006400u;
-            const f16x2_t v01 = __builtin_bit_cast(f16x2_t, b01) + off;
-            const f16x2_t v23 = __builtin_bit_cast(f16x2_t, b23) + off;
-            const f16x4_t bv = {v01[0], v01[1], v23[0], v23[1]};
+            const f16x4_t bv = __builtin_bit_cast(f16x4_t, make_uint2(b01, b23));
             t[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bv, t[nb], 0, 0, 0);
           }
         }
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) accm[nb][j] = fmaf(t[nb][j], down, accm[nb][j] * aj[j]);
+          for (int j = 0; j < 4; ++j)
+            accm[nb][j] = fmaf(t[nb][j] - tc[j], down, accm[nb][j] * aj[j]);
       } else {
         // O[head][dim] += P[head][row] V[row][dim] as above, with
         // v_mfma_f32_16x16x16_bf16: B = the bf16 V rows as stored (absent
