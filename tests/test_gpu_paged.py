@@ -185,6 +185,33 @@ def test_probe_position_digits_paged(bs, lens):
         assert np.allclose(lse[b], math.log(lens[b]), rtol=1e-5)
 
 
+@pytest.mark.parametrize("lens", [[1, 17, 9000, 16000], [1, 17, 250, 1000]])
+def test_probe_position_digits_wide_grid_sparse(lens):
+    """A block table of 8192 entries per sequence gives the pool 1M rows of
+    capacity, so the call takes the 512 x 4-wave grid, whose shares are
+    weighted by workgroup (17/16, 15/16); the sequences are short, so the
+    resident granules number between 512 and 1024 (every share holds some,
+    uneven ones) or far fewer (most shares empty): the merge then checks
+    each share for rows instead of taking them all as present."""
+    rng = np.random.default_rng(11)
+    batch, hkv, hq, d, bs = len(lens), 2, 8, 128, 16
+    maxb = 8192
+    assert batch * hkv * maxb * bs >= 512 * 2048  # the 4-wave grid
+    nblocks = [-(-n // bs) for n in lens]
+    nphys = sum(nblocks) + 5
+    perm = rng.permutation(nphys)
+    tables, o = [], 0
+    for nb in nblocks:
+        tables.append(perm[o:o + nb].astype(np.int32))
+        o += nb
+    k, v, bt = _probe_pool(batch, hkv, d, bs, tables, None, nphys, maxb)
+    out, lse = _run_paged(batch, hq, hkv, d, bs, maxb, nphys, k, v, bt, lens)
+    for b in range(batch):
+        want = _mean_digits(np.arange(lens[b]), b, d)
+        assert np.allclose(out[b][:, :5], want[:5], rtol=1e-5, atol=1e-5), b
+        assert np.allclose(lse[b], math.log(lens[b]), rtol=1e-5)
+
+
 def test_probe_position_digits_validity_mask():
     """Pool slots flagged absent (and slots whose id is out of range) drop out
     of the set exactly."""
