@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.decode import pool_expected, paged_expected, ring_expected, ring_slot_table
+from oracle.attention import attend_heads
+from oracle.decode import pool_expected, pool_rows, paged_expected, ring_expected, ring_slot_table
 from oracle.quant import quantize_rows
 from oracle.rope import rope
 from synth import TENSOR_K, TENSOR_V, PagedWorkload, PoolWorkload, RingWorkload, workload
@@ -236,3 +237,28 @@ def test_pool_i8_value_scales(scale, heads):
         want, _ = pool_expected(w, b, 0)
         bar = TOL * float(np.abs(want).max())
         assert float(np.abs(out[b] - want).max()) <= bar, (b, scale, heads)
+
+
+@pytest.mark.parametrize("heads", [(8, 2), (4, 4)])
+def test_pool_i8_same_sign_queries(heads):
+    """The int8 score products take the codes as 1152 + c and start from
+    minus 1152 times the query's sum: queries whose dims all share a sign
+    make that sum, and so the cancellation, as large as it gets.  Every head
+    positive (|N(0, 1)| times 3), then every dim 1 in one head, through the
+    matrix-core (g = 4) and the VALU (g = 1) P*V forms."""
+    hq, hkv = heads
+    w = PoolWorkload(name="p8q", seed=89, batch=2, num_q_heads=hq, num_kv_heads=hkv,
+                     head_dim=128, dtype="bf16", block_size=64, logical_blocks=48, pool_slots=20,
+                     rope_base=10000.0, scale=0.5, decode_steps=1, cache="i8")
+    st = _pool_state(w)
+    gen = torch.Generator().manual_seed(90)
+    q = (torch.randn(w.batch, hq, w.head_dim, generator=gen).abs() * 3).to(torch.bfloat16)
+    q[1, 0] = 1.0
+    st.step(q.cuda())
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy()
+    for b in range(w.batch):
+        _, k, v = pool_rows(w, b)
+        want, _ = attend_heads(q[b].double().numpy(), k, v, None)
+        assert float(np.abs(out[b] - want).max()) <= TOL, b
+
