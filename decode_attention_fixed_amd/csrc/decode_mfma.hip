@@ -1281,26 +1281,13 @@ __device__ bool next_piece(const DecodeParams& p, SeqChunk<NT>& sc, Piece& pc) {
 // the attention workgroups read the pool.  They take CUs of their own: a CU
 // holding an attention workgroup has no room for another.
 template <int G, int NW, bool I8>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p,
-                                                                        PoolFetch f) {
+__device__ __forceinline__ void pool_attend(const DecodeParams& p) {
   constexpr int NT = NW * 64;
   __shared__ Smem<G, NW, subtiles<G, true, I8>(), I8 ? 8 : 16> sm;
   __shared__ SeqChunk<NT> sc;
   const int64_t hkv = p.num_kv_heads;
   const int64_t nwg = p.num_splits;
   const int64_t w = blockIdx.x;
-  if (w >= nwg) {  // fetch workgroup w - nwg of gridDim.x - nwg takes every such piece
-    const int pieces = f.n * 2 * copy_pieces(f.block_u4, NT);
-    for (int j = static_cast<int>(w - nwg); j < pieces; j += static_cast<int>(gridDim.x - nwg)) {
-      const CopyPiece c = copy_piece(j, f.block_u4, NT);
-      const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.host_k : f.host_v) +
-                         static_cast<size_t>(f.src_block[c.item]) * f.block_u4;
-      uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
-                   static_cast<size_t>(c.item) * f.block_u4;
-      copy_block_piece(src, dst, c.begin, c.end, NT);
-    }
-    return;
-  }
 
   // Total granules: the first chunk's sum, plus a strided sum over the
   // sequences past it when the batch is larger than the workgroup.
@@ -1340,6 +1327,35 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
     attend_piece<G, PoolRows, NW, false, I8>(p, sm, pc.b, pc.h, pc.t0, pc.t1, pc.direct, pc.slot);
 }
 
+template <int G, int NW, bool I8>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodeParams p) {
+  pool_attend<G, NW, I8>(p);
+}
+
+// The same with a folded paging step: the workgroups past the balanced grid
+// fetch.  A kernel of its own, so that the calls without paging pass no fetch
+// descriptor (its block list doubles the kernel arguments).
+template <int G, int NW, bool I8>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_fetch_kernel(DecodeParams p,
+                                                                              PoolFetch f) {
+  constexpr int NT = NW * 64;
+  const int64_t nwg = p.num_splits;
+  const int64_t w = blockIdx.x;
+  if (w >= nwg) {  // fetch workgroup w - nwg of gridDim.x - nwg takes every such piece
+    const int pieces = f.n * 2 * copy_pieces(f.block_u4, NT);
+    for (int j = static_cast<int>(w - nwg); j < pieces; j += static_cast<int>(gridDim.x - nwg)) {
+      const CopyPiece c = copy_piece(j, f.block_u4, NT);
+      const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.host_k : f.host_v) +
+                         static_cast<size_t>(f.src_block[c.item]) * f.block_u4;
+      uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
+                   static_cast<size_t>(c.item) * f.block_u4;
+      copy_block_piece(src, dst, c.begin, c.end, NT);
+    }
+    return;
+  }
+  pool_attend<G, NW, I8>(p);
+}
+
 // Combines the partials of one (sequence, query head) spread over several
 // workgroups (a separate launch, so the partials written by the attention
 // kernels are visible without any cross-workgroup fence):
@@ -1355,15 +1371,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_kernel(DecodePara
 // out = 0, lse = -inf here.  256 threads = 8 slot groups x 32 float4 columns;
 // the partial rows are read by independent loads in flight together, and
 // slots with lse = -inf are dropped with selects.
-// The place part of a paging step folded into the call (f.n > 0) runs here
-// too: f.n * 2 * copy_pieces(block_u4, 256) workgroups after the B * Hq merge
-// workgroups move its blocks from the staging area into the pool and set
-// their validity bytes.
+// The place part of a paging step folded into the call (f.n > 0) runs in
+// the same launch (merge_place_kernel): f.n * 2 * copy_pieces(block_u4, 256)
+// workgroups after the B * Hq merge workgroups move its blocks from the
+// staging area into the pool and set their validity bytes.
 // The attention kernel that read the pool has finished when this launch
 // starts, and nothing in this launch reads the pool or the validity bytes,
 // so the moves overlap the merge and are visible to the launches after it.
 template <int PER>  // partial rows per thread held in registers
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, PoolPlace f) {
+__device__ __forceinline__ void merge_head(const DecodeParams& p, int pool) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
   constexpr int kSlots = 1024;  // pool pieces (at most the grid) plus the shared chunks
@@ -1372,17 +1388,6 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
   __shared__ float s_lse[kSlots];
   __shared__ float s_red_f[8];
   __shared__ float4 s_part[GROUPS][COLS];
-  const size_t heads = static_cast<size_t>(p.batch) * p.num_q_heads;
-  if (blockIdx.x >= heads) {
-    const CopyPiece c = copy_piece(static_cast<int>(blockIdx.x - heads), f.block_u4, 256);
-    const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
-                       static_cast<size_t>(c.item) * f.block_u4;
-    uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.k_pool : f.v_pool) +
-                 static_cast<size_t>(f.dst_block[c.item]) * f.block_u4;
-    copy_block_piece(src, dst, c.begin, c.end, 256);
-    if (c.tensor == 0 && c.begin == 0 && threadIdx.x == 0) f.valid[f.slot[c.item]] = 1;
-    return;
-  }
   const size_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / p.num_q_heads);
   const int hq = static_cast<int>(bh - static_cast<size_t>(b) * p.num_q_heads);
@@ -1537,6 +1542,30 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool, Po
     if (p.lse != nullptr && col == 0) p.lse[bh] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
   }
 }
+// Workgroup (sequence, query head) of the merge launch.
+template <int PER>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
+  merge_head<PER>(p, pool);
+}
+
+// The merge launch of a call with a folded paging step: the B * Hq merge
+// workgroups, then the place workgroups.  A kernel of its own, so that the
+// calls without paging pass no place descriptor (its block lists make the
+// kernel arguments three times larger).
+__global__ __launch_bounds__(256) void merge_place_kernel(DecodeParams p, PoolPlace f) {
+  const size_t heads = static_cast<size_t>(p.batch) * p.num_q_heads;
+  if (blockIdx.x >= heads) {
+    const CopyPiece c = copy_piece(static_cast<int>(blockIdx.x - heads), f.block_u4, 256);
+    const uint4* src = static_cast<const uint4*>(c.tensor == 0 ? f.stage_k : f.stage_v) +
+                       static_cast<size_t>(c.item) * f.block_u4;
+    uint4* dst = static_cast<uint4*>(c.tensor == 0 ? f.k_pool : f.v_pool) +
+                 static_cast<size_t>(f.dst_block[c.item]) * f.block_u4;
+    copy_block_piece(src, dst, c.begin, c.end, 256);
+    if (c.tensor == 0 && c.begin == 0 && threadIdx.x == 0) f.valid[f.slot[c.item]] = 1;
+    return;
+  }
+  merge_head<8>(p, 1);
+}
 
 template <int NW, bool I8>
 hipError_t decode_pool_kernel_launch(const DecodeParams& p, const PoolFetch& f,
@@ -1544,13 +1573,19 @@ hipError_t decode_pool_kernel_launch(const DecodeParams& p, const PoolFetch& f,
   // the balanced grid, then the fetch workgroups of a folded paging step:
   // those of one CU per XCD
   const unsigned grid = static_cast<unsigned>(p.num_splits) + (f.n > 0 ? kFetchCus * (8 / NW) : 0u);
+  auto go = [&](auto plain, auto fetch) {
+    if (f.n > 0)
+      fetch<<<grid, NW * 64, 0, stream>>>(p, f);
+    else
+      plain<<<grid, NW * 64, 0, stream>>>(p);
+  };
   switch (p.num_q_heads / p.num_kv_heads) {
-    case 1: decode_pool_kernel<1, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
-    case 2: decode_pool_kernel<2, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
-    case 3: decode_pool_kernel<3, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
-    case 4: decode_pool_kernel<4, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
-    case 6: decode_pool_kernel<6, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
-    case 8: decode_pool_kernel<8, NW, I8><<<grid, NW * 64, 0, stream>>>(p, f); break;
+    case 1: go(decode_pool_kernel<1, NW, I8>, decode_pool_fetch_kernel<1, NW, I8>); break;
+    case 2: go(decode_pool_kernel<2, NW, I8>, decode_pool_fetch_kernel<2, NW, I8>); break;
+    case 3: go(decode_pool_kernel<3, NW, I8>, decode_pool_fetch_kernel<3, NW, I8>); break;
+    case 4: go(decode_pool_kernel<4, NW, I8>, decode_pool_fetch_kernel<4, NW, I8>); break;
+    case 6: go(decode_pool_kernel<6, NW, I8>, decode_pool_fetch_kernel<6, NW, I8>); break;
+    case 8: go(decode_pool_kernel<8, NW, I8>, decode_pool_fetch_kernel<8, NW, I8>); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1586,7 +1621,7 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
                 : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream);
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0, PoolPlace{});
+  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);
   return hipGetLastError();
 }
 
@@ -1634,8 +1669,13 @@ hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream,
                : decode_pool_kernel_launch<8, false>(p, fetch, stream);
   if (err != hipSuccess) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  const unsigned copy_wgs = static_cast<unsigned>(place.n * 2 * copy_pieces(place.block_u4, 256));
-  merge_kernel<8><<<copy_wgs + heads, 256, 0, stream>>>(p, 1, place);
+  if (place.n > 0) {
+    const unsigned copy_wgs =
+        static_cast<unsigned>(place.n * 2 * copy_pieces(place.block_u4, 256));
+    merge_place_kernel<<<copy_wgs + heads, 256, 0, stream>>>(p, place);
+  } else {
+    merge_kernel<8><<<heads, 256, 0, stream>>>(p, 1);
+  }
   return hipGetLastError();
 }
 
