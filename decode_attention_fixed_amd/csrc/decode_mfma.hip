@@ -1378,13 +1378,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void decode_pool_fetch_kernel(Deco
 // The attention kernel that read the pool has finished when this launch
 // starts, and nothing in this launch reads the pool or the validity bytes,
 // so the moves overlap the merge and are visible to the launches after it.
-template <int PER>  // partial rows per thread held in registers
+template <int PER, bool SHARED>  // partial rows per thread held in registers;
+                                 // SHARED: the call may have shared-prefix chunks
 __device__ __forceinline__ void merge_head(const DecodeParams& p, int pool) {
   constexpr int COLS = kD / 4;
   constexpr int GROUPS = 256 / COLS;
-  constexpr int kSlots = 1024;  // pool pieces (at most the grid) plus the shared chunks
-  static_assert(kMaxSplits + kPrefixChunks <= kSlots && kPoolGrid + kPrefixChunks <= kSlots,
-                "four slots per thread");
+  // pool pieces (at most the grid), plus the shared chunks
+  constexpr int kSlots = SHARED ? 1024 : 512;
+  static_assert(kMaxSplits + (SHARED ? kPrefixChunks : 0) <= kSlots &&
+                    kPoolGrid + (SHARED ? kPrefixChunks : 0) <= kSlots,
+                "kSlots / 256 slots per thread");
   __shared__ float s_lse[kSlots];
   __shared__ float s_red_f[8];
   __shared__ float4 s_part[GROUPS][COLS];
@@ -1412,7 +1415,7 @@ __device__ __forceinline__ void merge_head(const DecodeParams& p, int pool) {
     const int64_t hkv = p.num_kv_heads;
     nwg = p.num_splits;
     const int64_t n = granules(p, b);
-    shared = shared_rows(p, b) > 0 ? p.prefix_chunks : 0;
+    if constexpr (SHARED) shared = shared_rows(p, b) > 0 ? p.prefix_chunks : 0;
     int64_t all = 0, pb = 0;
     for (int bb = threadIdx.x; bb < p.batch; bb += 256) {
       const int x = granules(p, bb);
@@ -1453,7 +1456,7 @@ __device__ __forceinline__ void merge_head(const DecodeParams& p, int pool) {
     return a < e;
   };
   auto slot_of = [&](int k) -> size_t {  // partial slot of the k-th partial
-    if (k < count) return static_cast<size_t>(first + k);
+    if (!SHARED || k < count) return static_cast<size_t>(first + k);
     return static_cast<size_t>(p.shared_base) +
            static_cast<size_t>(k - count) * p.batch * p.num_kv_heads + static_cast<size_t>(unit);
   };
@@ -1543,9 +1546,9 @@ __device__ __forceinline__ void merge_head(const DecodeParams& p, int pool) {
   }
 }
 // Workgroup (sequence, query head) of the merge launch.
-template <int PER>
+template <int PER, bool SHARED>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int pool) {
-  merge_head<PER>(p, pool);
+  merge_head<PER, SHARED>(p, pool);
 }
 
 // The merge launch of a call with a folded paging step: the B * Hq merge
@@ -1564,7 +1567,7 @@ __global__ __launch_bounds__(256) void merge_place_kernel(DecodeParams p, PoolPl
     if (c.tensor == 0 && c.begin == 0 && threadIdx.x == 0) f.valid[f.slot[c.item]] = 1;
     return;
   }
-  merge_head<8>(p, 1);
+  merge_head<8, true>(p, 1);
 }
 
 template <int NW, bool I8>
@@ -1621,7 +1624,7 @@ hipError_t launch_decode_mfma_ring(const DecodeParams& p, hipStream_t stream) {
                 : decode_ring_kernel_launch<kRingWaves, false, false>(p, grid, stream);
   if (err != hipSuccess || p.num_splits == 1) return err;
   const unsigned heads = static_cast<unsigned>(p.batch) * static_cast<unsigned>(p.num_q_heads);
-  merge_kernel<8><<<heads, 256, 0, stream>>>(p, 0);
+  merge_kernel<8, false><<<heads, 256, 0, stream>>>(p, 0);
   return hipGetLastError();
 }
 
@@ -1673,8 +1676,10 @@ hipError_t launch_decode_mfma_pool(const DecodeParams& p_in, hipStream_t stream,
     const unsigned copy_wgs =
         static_cast<unsigned>(place.n * 2 * copy_pieces(place.block_u4, 256));
     merge_place_kernel<<<copy_wgs + heads, 256, 0, stream>>>(p, place);
+  } else if (p.plan != nullptr) {  // the shared-prefix pass ran: chunk partials
+    merge_kernel<8, true><<<heads, 256, 0, stream>>>(p, 1);
   } else {
-    merge_kernel<8><<<heads, 256, 0, stream>>>(p, 1);
+    merge_kernel<8, false><<<heads, 256, 0, stream>>>(p, 1);
   }
   return hipGetLastError();
 }
